@@ -1,0 +1,90 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds none of the attention arithmetic: it only draws Q, K, V,
+rounds them to bf16 when asked, and scales a few columns to mimic activation
+outliers.  Both the HIP library and the fp64 oracle are fed from it.
+
+Workloads (latent token grids of the pages' video shapes; DCAE-V compresses
+32x in space and 4x in time, a 60 s clip at 16 FPS has 240 latent frames):
+
+  tiny    B1 H2  N256    d32  fp32, no RoPE
+  480p    B1 H16 N8190   d64  bf16, grid 21x15x26, 1% of (head, channel) columns x8
+  720p5s  B2 H32 N19320  d64  bf16, grid 21x23x40
+  720p60s B1 H32 N220800 d64  bf16, grid 240x23x40, 10 blocks of 22080 tokens
+  sweep   B1 H32 d in {32,64,128}, N in {4096,16384,65536,220800}, grid ceil(N/920)x23x40
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+SWEEP_D = (32, 64, 128)
+SWEEP_N = (4096, 16384, 65536, 220800)
+
+
+def _workload(name, B, H, N, d, dtype, grid, seed, block=None, outliers=False, eps=1e-6):
+    return dict(name=name, B=B, H=H, N=N, d=d, dtype=dtype, grid=grid, seed=seed,
+                block=block, outliers=outliers, eps=eps)
+
+
+def sweep_grid(N: int) -> tuple[int, int, int]:
+    """Frames of a 23x40 latent plane needed to hold N tokens (last frame partial)."""
+    return (math.ceil(N / 920), 23, 40)
+
+
+WORKLOADS = {
+    "tiny": _workload("tiny", 1, 2, 256, 32, "fp32", None, 1001),
+    "480p": _workload("480p", 1, 16, 8190, 64, "bf16", (21, 15, 26), 1002, outliers=True),
+    "720p5s": _workload("720p5s", 2, 32, 19320, 64, "bf16", (21, 23, 40), 1003),
+    "720p60s": _workload("720p60s", 1, 32, 220800, 64, "bf16", (240, 23, 40), 1004,
+                         block=22080),
+}
+for _d in SWEEP_D:
+    for _n in SWEEP_N:
+        WORKLOADS[f"sweep_d{_d}_n{_n}"] = _workload(
+            f"sweep_d{_d}_n{_n}", 1, 32, _n, _d, "bf16", sweep_grid(_n), 1005)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 (ties to even); returns float32.
+
+    Operates on the bit pattern: add 0x7FFF plus the lowest kept bit, then clear
+    the 16 low bits.  Inputs here are finite normal draws, so no NaN handling.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+def make_qkv(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
+             outliers: bool = False):
+    """Draw Q, K, V ~ N(0, 1) of shape [B, H, N, d] as float32 arrays.
+
+    Draw order is Q, K, V from numpy's PCG64 stream of `seed`.  For bf16 the
+    values are rounded to bf16 (so they are exactly representable).  With
+    `outliers`, for each of Q, K, V in turn, round(0.01 * H * d) distinct
+    (head, channel) columns are multiplied by 8 (a power of two, so the bf16
+    rounding is unaffected).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(3):
+        a = rng.standard_normal((B, H, N, d), dtype=np.float32)
+        if dtype == "bf16":
+            a = round_to_bf16(a)
+        out.append(a)
+    if outliers:
+        ncols = int(round(0.01 * H * d))
+        for a in out:
+            cols = rng.choice(H * d, size=ncols, replace=False)
+            for c in cols:
+                a[:, c // d, :, c % d] *= np.float32(8.0)
+    return tuple(out)
+
+
+def make_workload(name: str):
+    """Inputs of a named workload: (q, k, v, spec)."""
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"], w["outliers"])
+    return q, k, v, w

@@ -1,0 +1,11 @@
+"""fp64 CPU oracle of the ReLU linear-attention token mixer (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg use this
+package.  It imports nothing from the HIP library and the library imports
+nothing from it.
+"""
+from .linattn_oracle import (  # noqa: F401
+    ROPE_BASE, phi, rope_axis_pairs, grid_positions, rope_angles, rope,
+    state, apply, bidirectional_head, block_causal_head, weights_form_head,
+    bidirectional, states, block_causal, rel_row_error,
+)
