@@ -1,0 +1,125 @@
+/*
+ * la.h -- C ABI of the MI355X (gfx950) ReLU linear-attention token mixer.
+ *
+ * The operation is the one defined on the SANA-Video analysis page
+ * (arXiv 2509.24695, section 3.4 "Detailed, Sentence-Based Technical
+ * Breakdown"):
+ *
+ *   "ReLU Linear Attention Mechanism" (unnumbered equation) with RoPE as in
+ *   "Integration of 3D Rotary Position Embeddings", Eq. 2:
+ *
+ *     S = sum_j RoPE(relu(K_j))^T V_j          (d x d per (batch, head))
+ *     z = sum_j relu(K_j)                       (d, NOT rotated)
+ *     O_i = RoPE(relu(Q_i)) S / (relu(Q_i) . z + eps)
+ *
+ *   and "Block Linear Attention with Constant-Memory KV Cache" (Eq. 3, the
+ *   running-sum update, Table 1, Algorithm 1): S and z are carried from block
+ *   to block; block b is applied with the sums over blocks 0..b.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Q, K, V, O are contiguous [B, H, n, d] arrays in device memory, element
+ *    type `dtype` (LA_BF16 = bfloat16, LA_FP32 = float).  n is N for the
+ *    bidirectional calls and the block's length for la_block_causal_step.
+ *  - S is a contiguous [B, H, d, d] float array, row index = key channel,
+ *    column index = value channel.  z is a contiguous [B, H, d] float array.
+ *    Both are always fp32 and always caller-owned device memory.
+ *  - d must be 32, 64 or 128.  eps >= 0 is added to the denominator only.
+ *    A row whose relu(Q_i) is all zero gets an all-zero output row.
+ *  - (gt, gh, gw) is the latent grid.  Token n sits at
+ *    t = n / (gh*gw), h = (n / gw) % gh, w = n % gw (0-based, t-major).
+ *    gt = gh = gw = 0 switches RoPE off; otherwise all three must be >= 1 and
+ *    gt*gh*gw >= N.  The d/2 interleaved channel pairs (2p, 2p+1) are split
+ *    into t, h, w ranges of d/2 - 2*floor(d/6), floor(d/6), floor(d/6) pairs;
+ *    pair k of an axis with P_a pairs turns by pos_a * 10000^(-k/P_a).
+ *  - ws is a device workspace of at least la_workspace_bytes(B, H, N, d)
+ *    bytes.  It MUST be zero-filled once before its first use; every call
+ *    leaves its first words zero again, so it can be reused call after call.
+ *    One workspace must not be used by two calls that may overlap in time
+ *    (two streams): they would race on it.
+ *  - All pointers must be 16-byte aligned.  O must not overlap Q, K, V, S or z.
+ *  - stream is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues kernels: it never allocates, never synchronises, and returns as
+ *    soon as the launches are queued.
+ *  - Return value: LA_OK or a negative LA_E_* code.  Argument checks run
+ *    before any launch; when one fails nothing is launched and no buffer is
+ *    touched.  LA_E_HIP means a launch was rejected by the HIP runtime.
+ *    Non-finite inputs are not checked: they propagate.
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define LA_API __attribute__((visibility("default")))
+#else
+#define LA_API
+#endif
+
+enum { LA_FP32 = 0, LA_BF16 = 1 };
+
+enum {
+    LA_OK = 0,
+    LA_E_NULLPTR = -1,     /* a required pointer is NULL */
+    LA_E_SHAPE = -2,       /* bad B/H/N/grid/block arguments */
+    LA_E_UNSUPPORTED = -3, /* d not in {32,64,128}, bad dtype, grid too large */
+    LA_E_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    LA_E_WORKSPACE = -5,   /* ws_bytes < la_workspace_bytes(...) */
+    LA_E_HIP = -6,         /* the HIP runtime rejected a launch */
+    LA_E_ALIAS = -7        /* O overlaps an input */
+};
+
+/* Upper bound on the workspace any call below needs for these sizes
+ * (N = tokens of the whole sequence).  Returns 0 for invalid sizes. */
+LA_API size_t la_workspace_bytes(int B, int H, int N, int d);
+
+/* State pass (the two sums of the linear-attention equation, Eq. 2 form):
+ *   S[b,h] = sum_{n<N} RoPE(relu(K[b,h,n]))^T V[b,h,n],  z[b,h] = sum_n relu(K[b,h,n]).
+ * Reads K and V; writes S and z.  Q and O are not used and may be NULL;
+ * block_tokens is ignored.  N = 0 gives S = 0, z = 0 (K, V may then be NULL).  The sum is split over many workgroups and
+ * combined in a fixed order, so repeated calls give bitwise equal results. */
+LA_API int la_state_reduce(const void* Q, const void* K, const void* V, void* O,
+                    float* S, float* z, void* ws, size_t ws_bytes,
+                    int B, int H, int N, int d, int gt, int gh, int gw,
+                    int block_tokens, float eps, int dtype, void* stream);
+
+/* Apply pass (numerator / denominator of Eq. 2):
+ *   O[b,h,n] = RoPE(relu(Q[b,h,n])) S[b,h] / (relu(Q[b,h,n]) . z[b,h] + eps).
+ * Reads Q, S, z; writes O (bf16 outputs are rounded to nearest even).
+ * K and V are not used and may be NULL; block_tokens is ignored.  ws is not
+ * used by this call and may be NULL (ws_bytes is then ignored).  N = 0 is a
+ * no-op that returns LA_OK after the argument checks on sizes. */
+LA_API int la_apply(const void* Q, const void* K, const void* V, void* O,
+             const float* S, const float* z, void* ws, size_t ws_bytes,
+             int B, int H, int N, int d, int gt, int gh, int gw,
+             int block_tokens, float eps, int dtype, void* stream);
+
+/* One block of block-causal mode (Eq. 3 taken a block at a time, Algorithm 1).
+ * The sequence has N tokens in blocks of L = block_tokens; block b =
+ * block_idx covers global tokens [b*L, min((b+1)*L, N)) and Q, K, V, O hold
+ * only that block: [B, H, L_b, d] with L_b = min(L, N - b*L).
+ * On entry S_carry/z_carry hold the sums over blocks < b (zero-filled before
+ * block 0: the empty cache).  The call forms S_b = S_carry + (block b's sum),
+ * z_b likewise, applies them to block b's rows with RoPE at the global
+ * positions, and writes O.  commit = 1 stores S_b, z_b back into
+ * S_carry/z_carry (the cache update after the clean block); commit = 0 leaves
+ * the carry untouched (a denoising step that only reads the cache). */
+LA_API int la_block_causal_step(const void* Q, const void* K, const void* V, void* O,
+                         float* S_carry, float* z_carry, void* ws, size_t ws_bytes,
+                         int B, int H, int N, int d, int gt, int gh, int gw,
+                         int block_tokens, float eps, int dtype,
+                         int block_idx, int commit, void* stream);
+
+/* Static text for a status code (never NULL). */
+LA_API const char* la_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

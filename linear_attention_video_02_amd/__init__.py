@@ -1,0 +1,221 @@
+"""MI355X (gfx950) ReLU linear-attention token mixer.
+
+Python binding of the C-ABI library liblinattn.so (declared in include/la.h).
+This module only marshals arguments: every step of the computation runs in the
+library's HIP kernels.  PyTorch supplies device memory and the stream.  There
+is no fallback: if the library is not built, every call raises.
+
+The method is the ReLU linear attention of the SANA-Video analysis page
+(section 3.4: the linear-attention equation, Eq. 2 for RoPE, Eq. 3 and
+Algorithm 1 for the block-causal cache).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
+
+LA_FP32 = 0
+LA_BF16 = 1
+
+STATUS = {
+    0: "LA_OK", -1: "LA_E_NULLPTR", -2: "LA_E_SHAPE", -3: "LA_E_UNSUPPORTED",
+    -4: "LA_E_ALIGN", -5: "LA_E_WORKSPACE", -6: "LA_E_HIP", -7: "LA_E_ALIAS",
+}
+
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({strerror(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblinattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, ci, cf, cs = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        common = [ci] * 8 + [cf, ci]  # B H N d gt gh gw block_tokens, eps, dtype
+        L.la_workspace_bytes.argtypes = [ci, ci, ci, ci]
+        L.la_workspace_bytes.restype = cs
+        L.la_state_reduce.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [vp]
+        L.la_state_reduce.restype = ci
+        L.la_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [vp]
+        L.la_apply.restype = ci
+        L.la_block_causal_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [ci, ci, vp]
+        L.la_block_causal_step.restype = ci
+        L.la_strerror.argtypes = [ci]
+        L.la_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().la_strerror(int(status)).decode()
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().la_workspace_bytes(B, H, N, d))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _grid(grid):
+    if grid is None:
+        return 0, 0, 0
+    gt, gh, gw = (int(x) for x in grid)
+    return gt, gh, gw
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_qkv(*ts):
+    ref = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+        if t.dim() != 4:
+            raise ValueError("tensors must be 4-D [B, H, N, d]")
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("Q/K/V/O must share dtype and device")
+
+
+_ws_cache: dict = {}
+
+
+def workspace(B: int, H: int, N: int, d: int, device):
+    """A zero-filled workspace, cached per (device, size); reusable on one stream."""
+    torch = _torch()
+    nbytes = workspace_bytes(B, H, N, d)
+    if nbytes == 0:
+        raise ValueError("invalid sizes for a workspace")
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device(), nbytes)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _state_tensors(B, H, d, device):
+    torch = _torch()
+    return (torch.empty((B, H, d, d), dtype=torch.float32, device=device),
+            torch.empty((B, H, d), dtype=torch.float32, device=device))
+
+
+def state_reduce(k, v, grid=None, S=None, z=None, ws=None):
+    """S = sum_j RoPE(relu K_j)^T V_j and z = sum_j relu K_j per (batch, head)."""
+    _check_qkv(k, v)
+    B, H, N, d = k.shape
+    if S is None or z is None:
+        S, z = _state_tensors(B, H, d, k.device)
+    if ws is None:
+        ws = workspace(B, H, N, d, k.device)
+    gt, gh, gw = _grid(grid)
+    rc = lib().la_state_reduce(None, _ptr(k), _ptr(v), None, _ptr(S), _ptr(z), _ptr(ws),
+                               ws.numel(), B, H, N, d, gt, gh, gw, 0, 0.0,
+                               _dtype_code(k), _stream(k))
+    if rc:
+        raise LinAttnError(rc, "la_state_reduce")
+    return S, z
+
+
+def apply(q, S, z, grid=None, eps=1e-6, out=None):
+    """O_i = RoPE(relu Q_i) S / (relu Q_i . z + eps)."""
+    torch = _torch()
+    _check_qkv(q)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    gt, gh, gw = _grid(grid)
+    rc = lib().la_apply(_ptr(q), None, None, _ptr(out), _ptr(S), _ptr(z), None, 0,
+                        B, H, N, d, gt, gh, gw, 0, float(eps), _dtype_code(q), _stream(q))
+    if rc:
+        raise LinAttnError(rc, "la_apply")
+    return out
+
+
+def bidirectional(q, k, v, grid=None, eps=1e-6, out=None, ws=None):
+    """Bidirectional ReLU linear attention with (optional) 3D RoPE."""
+    S, z = state_reduce(k, v, grid, ws=ws)
+    return apply(q, S, z, grid, eps, out)
+
+
+def block_causal_step(q, k, v, S_carry, z_carry, N, grid, block_tokens, block_idx,
+                      commit=True, eps=1e-6, out=None, ws=None):
+    """One block of block-causal mode; q/k/v/out hold only this block."""
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, Lb, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    if ws is None:
+        ws = workspace(B, H, N, d, q.device)
+    gt, gh, gw = _grid(grid)
+    rc = lib().la_block_causal_step(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_carry),
+                                    _ptr(z_carry), _ptr(ws), ws.numel(), B, H, N, d,
+                                    gt, gh, gw, int(block_tokens), float(eps), _dtype_code(q),
+                                    int(block_idx), int(bool(commit)), _stream(q))
+    if rc:
+        raise LinAttnError(rc, "la_block_causal_step")
+    return out
+
+
+def split_blocks(x, block_tokens):
+    """Per-block contiguous copies [B, H, L_b, d] of a [B, H, N, d] tensor."""
+    N = x.shape[2]
+    return [x[:, :, b0:b0 + block_tokens].contiguous() for b0 in range(0, N, block_tokens)]
+
+
+def block_causal(q_blocks, k_blocks, v_blocks, N, grid, block_tokens, eps=1e-6,
+                 S_carry=None, z_carry=None, first_block=0):
+    """Run blocks first_block, first_block+1, ... in order, committing each.
+
+    q_blocks etc. are lists of per-block [B, H, L_b, d] tensors.  Returns the
+    list of outputs and the carry (S, z) after the last block.
+    """
+    torch = _torch()
+    q0 = q_blocks[0]
+    B, H, _, d = q0.shape
+    if S_carry is None:
+        S_carry = torch.zeros((B, H, d, d), dtype=torch.float32, device=q0.device)
+        z_carry = torch.zeros((B, H, d), dtype=torch.float32, device=q0.device)
+    outs = []
+    for i, (qb, kb, vb) in enumerate(zip(q_blocks, k_blocks, v_blocks)):
+        outs.append(block_causal_step(qb, kb, vb, S_carry, z_carry, N, grid, block_tokens,
+                                      first_block + i, True, eps))
+    return outs, S_carry, z_carry

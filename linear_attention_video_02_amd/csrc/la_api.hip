@@ -1,0 +1,383 @@
+// C ABI of the ReLU linear-attention library: argument checks, launch
+// configuration and dispatch.  Declarations and the full contract are in
+// include/la.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "la.h"
+#include "la_apply.h"
+#include "la_common.h"
+#include "la_state.h"
+
+namespace {
+
+constexpr int kMaxPartials = 64;         // state workgroups per (batch, head), upper bound
+constexpr size_t kLdsLimit = 160 * 1024; // gfx950 LDS per workgroup
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int env_int(const char* name, int dflt) {
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    int v = atoi(s);
+    return v > 0 ? v : dflt;
+}
+
+struct WsLayout {
+    size_t ticket, partial, state, total;
+};
+
+WsLayout ws_layout(int BH, int d) {
+    WsLayout L;
+    L.ticket = 0;
+    L.partial = align_up((size_t)BH * 4, 256);
+    L.state = L.partial + align_up((size_t)BH * kMaxPartials * (d * d + d) * 4, 256);
+    L.total = L.state + align_up((size_t)BH * (d * d + d) * 4, 256);
+    return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || !na || !nb) return false;
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Checks shared by every entry point.  N is the whole sequence length.
+int check_common(int B, int H, int N, int d, int gt, int gh, int gw, float eps, int dtype) {
+    if (dtype != LA_FP32 && dtype != LA_BF16) return LA_E_UNSUPPORTED;
+    if (d != 32 && d != 64 && d != 128) return LA_E_UNSUPPORTED;
+    if (B < 1 || H < 1 || N < 0) return LA_E_SHAPE;
+    if (!(eps >= 0.0f) || eps != eps) return LA_E_SHAPE;
+    const long long BH = (long long)B * H;
+    if (BH > 65535) return LA_E_SHAPE;                       // grid.y limit
+    if (BH * (long long)N * d >= (1ll << 40)) return LA_E_SHAPE;
+    if (N >= (1 << 30)) return LA_E_SHAPE;
+    const bool none = gt == 0 && gh == 0 && gw == 0;
+    if (!none) {
+        if (gt < 1 || gh < 1 || gw < 1) return LA_E_SHAPE;
+        if ((long long)gt * gh * gw < N) return LA_E_SHAPE;
+        if ((long long)gt * gh * gw >= (1ll << 31)) return LA_E_SHAPE;
+    }
+    return LA_OK;
+}
+
+LaGeom make_geom(int B, int H, int ntok, int n_offset, int d, int gt, int gh, int gw) {
+    LaGeom g;
+    memset(&g, 0, sizeof(g));
+    g.BH = B * H;
+    g.ntok = ntok;
+    g.n_offset = n_offset;
+    g.rope = !(gt == 0 && gh == 0 && gw == 0);
+    if (g.rope) {
+        const int P = d / 2;
+        g.ph = g.pw = P / 3;
+        g.pt = P - 2 * (P / 3);
+        g.gh = gh;
+        g.gw = gw;
+        g.div_hw = make_fastdiv((uint32_t)gh * (uint32_t)gw);
+        g.div_w = make_fastdiv((uint32_t)gw);
+    } else {
+        g.gh = g.gw = 1;
+        g.div_hw = make_fastdiv(1);
+        g.div_w = make_fastdiv(1);
+    }
+    return g;
+}
+
+// Entries of the per-workgroup RoPE table for a chunk of `chunk` tokens.
+size_t table_entries(const LaGeom& g, int chunk) {
+    if (!g.rope) return 0;
+    const long long hw = (long long)g.gh * g.gw;
+    const long long nt = (chunk + hw - 1) / hw + 1;   // frames one chunk can touch
+    return (size_t)(nt * g.pt + (long long)g.gh * g.ph + (long long)g.gw * g.pw);
+}
+
+int state_fixed_lds(int d, int dtype) {
+    if (dtype == LA_BF16) {
+        switch (d) {
+            case 32: return StateBf16Cfg<32>::SMEM_FIXED;
+            case 64: return StateBf16Cfg<64>::SMEM_FIXED;
+            default: return StateBf16Cfg<128>::SMEM_FIXED;
+        }
+    }
+    switch (d) {
+        case 32: return StateF32Cfg<32>::SMEM_FIXED;
+        case 64: return StateF32Cfg<64>::SMEM_FIXED;
+        default: return StateF32Cfg<128>::SMEM_FIXED;
+    }
+}
+
+int apply_fixed_lds(int d, int dtype) {
+    if (dtype == LA_BF16) return 0;
+    switch (d) {
+        case 32: return ApplyF32Cfg<32>::SMEM_FIXED;
+        case 64: return ApplyF32Cfg<64>::SMEM_FIXED;
+        default: return ApplyF32Cfg<128>::SMEM_FIXED;
+    }
+}
+
+struct Plan {
+    int P, chunk;
+    size_t lds;
+};
+
+// State pass: about LA_STATE_WGS workgroups in all (default 1024, four per CU),
+// chunks a multiple of the 64-token tile, at most kMaxPartials per head.
+int plan_state(const LaGeom& g, int d, int dtype, Plan* out) {
+    const int target = env_int("LA_STATE_WGS", 1024);
+    const int tile = 64;
+    const int ntok = g.ntok;
+    int P = (target + g.BH - 1) / g.BH;
+    P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
+    const int max_p = ntok > 0 ? (ntok + tile - 1) / tile : 1;
+    if (P > max_p) P = max_p;
+    for (;;) {
+        int chunk = ntok > 0 ? (ntok + P - 1) / P : tile;
+        chunk = (int)align_up((size_t)chunk, tile);
+        const int Peff = ntok > 0 ? (ntok + chunk - 1) / chunk : 1;
+        const size_t lds = (size_t)state_fixed_lds(d, dtype) + table_entries(g, chunk) * 8;
+        if (lds <= kLdsLimit) {
+            out->P = Peff;
+            out->chunk = chunk;
+            out->lds = lds;
+            return LA_OK;
+        }
+        if (P >= kMaxPartials || P >= max_p) return LA_E_UNSUPPORTED;   // grid plane too large
+        ++P;
+    }
+}
+
+// Apply pass: about LA_APPLY_WGS workgroups in all (default 2048).
+int plan_apply(const LaGeom& g, int d, int dtype, Plan* out) {
+    const int target = env_int("LA_APPLY_WGS", 2048);
+    const int tile = 128;
+    const int ntok = g.ntok;
+    int P = (target + g.BH - 1) / g.BH;
+    if (P < 1) P = 1;
+    const int max_p = ntok > 0 ? (ntok + tile - 1) / tile : 1;
+    if (P > max_p) P = max_p;
+    for (;;) {
+        int chunk = ntok > 0 ? (ntok + P - 1) / P : tile;
+        chunk = (int)align_up((size_t)chunk, tile);
+        const int Peff = ntok > 0 ? (ntok + chunk - 1) / chunk : 1;
+        const size_t lds = (size_t)apply_fixed_lds(d, dtype) + table_entries(g, chunk) * 8;
+        if (lds <= kLdsLimit) {
+            out->P = Peff;
+            out->chunk = chunk;
+            out->lds = lds;
+            return LA_OK;
+        }
+        if (P >= max_p) return LA_E_UNSUPPORTED;
+        ++P;
+    }
+}
+
+template <typename Args>
+using KernelFn = void (*)(Args);
+
+template <typename Args>
+int launch_kernel(KernelFn<Args> fn, dim3 grid, size_t lds, hipStream_t st, const Args& args) {
+    if (lds > 64 * 1024) {
+        if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess)
+            return LA_E_HIP;
+    }
+    hipLaunchKernelGGL(fn, grid, dim3(256), lds, st, args);
+    return hipGetLastError() == hipSuccess ? LA_OK : LA_E_HIP;
+}
+
+KernelFn<StateArgs> state_kernel(int d, int dtype, bool rope) {
+#define LA_PICK(D)                                                                              \
+    if (d == D) {                                                                               \
+        if (dtype == LA_BF16) return rope ? la_state_bf16_kernel<D, true> : la_state_bf16_kernel<D, false>; \
+        return rope ? la_state_f32_kernel<D, true> : la_state_f32_kernel<D, false>;             \
+    }
+    LA_PICK(32)
+    LA_PICK(64)
+    LA_PICK(128)
+#undef LA_PICK
+    return nullptr;
+}
+
+KernelFn<ApplyArgs> apply_kernel(int d, int dtype, bool rope) {
+#define LA_PICK(D)                                                                              \
+    if (d == D) {                                                                               \
+        if (dtype == LA_BF16) return rope ? la_apply_bf16_kernel<D, true> : la_apply_bf16_kernel<D, false>; \
+        return rope ? la_apply_f32_kernel<D, true> : la_apply_f32_kernel<D, false>;             \
+    }
+    LA_PICK(32)
+    LA_PICK(64)
+    LA_PICK(128)
+#undef LA_PICK
+    return nullptr;
+}
+
+// Enqueue the state pass over `ntok` tokens starting at global index n_offset.
+int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S_out2, float* z_out2,
+              const float* S_carry, const float* z_carry, void* ws, int B, int H, int ntok, int n_offset,
+              int d, int gt, int gh, int gw, int dtype, hipStream_t st) {
+    const LaGeom g = make_geom(B, H, ntok, n_offset, d, gt, gh, gw);
+    Plan pl;
+    int rc = plan_state(g, d, dtype, &pl);
+    if (rc != LA_OK) return rc;
+    const WsLayout L = ws_layout(g.BH, d);
+    StateArgs a;
+    a.K = K;
+    a.V = V;
+    a.partial = (float*)((char*)ws + L.partial);
+    a.ticket = (unsigned*)((char*)ws + L.ticket);
+    a.S_out = S_out;
+    a.z_out = z_out;
+    a.S_out2 = S_out2;
+    a.z_out2 = z_out2;
+    a.S_carry = S_carry;
+    a.z_carry = z_carry;
+    a.chunk = pl.chunk;
+    a.P = pl.P;
+    a.g = g;
+    return launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P, g.BH), pl.lds, st, a);
+}
+
+int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int H, int ntok, int n_offset,
+              int d, int gt, int gh, int gw, float eps, int dtype, hipStream_t st) {
+    if (ntok == 0) return LA_OK;
+    const LaGeom g = make_geom(B, H, ntok, n_offset, d, gt, gh, gw);
+    Plan pl;
+    int rc = plan_apply(g, d, dtype, &pl);
+    if (rc != LA_OK) return rc;
+    ApplyArgs a;
+    a.Q = Q;
+    a.O = O;
+    a.S = S;
+    a.z = z;
+    a.eps = eps;
+    a.chunk = pl.chunk;
+    a.P = pl.P;
+    a.g = g;
+    return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.P, g.BH), pl.lds, st, a);
+}
+
+size_t elem_bytes(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
+
+// Plans depend only on sizes, so a plan failure is reported before any launch.
+int precheck_plans(int B, int H, int ntok, int n_offset, int d, int gt, int gh, int gw, int dtype,
+                   bool state, bool apply) {
+    const LaGeom g = make_geom(B, H, ntok, n_offset, d, gt, gh, gw);
+    Plan pl;
+    if (state) {
+        int rc = plan_state(g, d, dtype, &pl);
+        if (rc != LA_OK) return rc;
+    }
+    if (apply && ntok > 0) {
+        int rc = plan_apply(g, d, dtype, &pl);
+        if (rc != LA_OK) return rc;
+    }
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t la_workspace_bytes(int B, int H, int N, int d) {
+    if (check_common(B, H, N, d, 0, 0, 0, 0.0f, LA_BF16) != LA_OK) return 0;
+    return ws_layout(B * H, d).total;
+}
+
+int la_state_reduce(const void* Q, const void* K, const void* V, void* O, float* S, float* z, void* ws,
+                    size_t ws_bytes, int B, int H, int N, int d, int gt, int gh, int gw, int block_tokens,
+                    float eps, int dtype, void* stream) {
+    (void)Q;
+    (void)O;
+    (void)block_tokens;
+    int rc = check_common(B, H, N, d, gt, gh, gw, eps, dtype);
+    if (rc != LA_OK) return rc;
+    if (!S || !z || !ws || (N > 0 && (!K || !V))) return LA_E_NULLPTR;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(S) || !aligned16(z) || !aligned16(ws)) return LA_E_ALIGN;
+    if (ws_bytes < ws_layout(B * H, d).total) return LA_E_WORKSPACE;
+    const size_t nS = (size_t)B * H * d * d * 4, nz = (size_t)B * H * d * 4;
+    const size_t nkv = (size_t)B * H * N * d * elem_bytes(dtype);
+    if (overlaps(S, nS, K, nkv) || overlaps(S, nS, V, nkv) || overlaps(z, nz, K, nkv) ||
+        overlaps(z, nz, V, nkv) || overlaps(S, nS, z, nz))
+        return LA_E_ALIAS;
+    rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, true, false);
+    if (rc != LA_OK) return rc;
+    return run_state(K, V, S, z, nullptr, nullptr, nullptr, nullptr, ws, B, H, N, 0, d, gt, gh, gw, dtype,
+                     (hipStream_t)stream);
+}
+
+int la_apply(const void* Q, const void* K, const void* V, void* O, const float* S, const float* z, void* ws,
+             size_t ws_bytes, int B, int H, int N, int d, int gt, int gh, int gw, int block_tokens, float eps,
+             int dtype, void* stream) {
+    (void)K;
+    (void)V;
+    (void)ws;
+    (void)ws_bytes;
+    (void)block_tokens;
+    int rc = check_common(B, H, N, d, gt, gh, gw, eps, dtype);
+    if (rc != LA_OK) return rc;
+    if (N == 0) return LA_OK;  // nothing to write
+    if (!Q || !O || !S || !z) return LA_E_NULLPTR;
+    if (!aligned16(Q) || !aligned16(O) || !aligned16(S) || !aligned16(z)) return LA_E_ALIGN;
+    const size_t nqo = (size_t)B * H * N * d * elem_bytes(dtype);
+    if (overlaps(O, nqo, Q, nqo) || overlaps(O, nqo, S, (size_t)B * H * d * d * 4) ||
+        overlaps(O, nqo, z, (size_t)B * H * d * 4))
+        return LA_E_ALIAS;
+    rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, false, true);
+    if (rc != LA_OK) return rc;
+    return run_apply(Q, O, S, z, B, H, N, 0, d, gt, gh, gw, eps, dtype, (hipStream_t)stream);
+}
+
+int la_block_causal_step(const void* Q, const void* K, const void* V, void* O, float* S_carry, float* z_carry,
+                         void* ws, size_t ws_bytes, int B, int H, int N, int d, int gt, int gh, int gw,
+                         int block_tokens, float eps, int dtype, int block_idx, int commit, void* stream) {
+    int rc = check_common(B, H, N, d, gt, gh, gw, eps, dtype);
+    if (rc != LA_OK) return rc;
+    if (block_tokens < 1 || block_idx < 0 || (commit != 0 && commit != 1)) return LA_E_SHAPE;
+    const long long start = (long long)block_idx * block_tokens;
+    if (start >= N) return LA_E_SHAPE;
+    const int Lb = (int)((N - start) < block_tokens ? (N - start) : block_tokens);
+    if (!Q || !K || !V || !O || !S_carry || !z_carry || !ws) return LA_E_NULLPTR;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_carry) ||
+        !aligned16(z_carry) || !aligned16(ws))
+        return LA_E_ALIGN;
+    const WsLayout L = ws_layout(B * H, d);
+    if (ws_bytes < L.total) return LA_E_WORKSPACE;
+    const size_t nb = (size_t)B * H * Lb * d * elem_bytes(dtype);
+    const size_t nS = (size_t)B * H * d * d * 4, nz = (size_t)B * H * d * 4;
+    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, K, nb) || overlaps(O, nb, V, nb) ||
+        overlaps(O, nb, S_carry, nS) || overlaps(O, nb, z_carry, nz) || overlaps(S_carry, nS, z_carry, nz) ||
+        overlaps(S_carry, nS, K, nb) || overlaps(S_carry, nS, V, nb) || overlaps(z_carry, nz, K, nb) ||
+        overlaps(z_carry, nz, V, nb) || overlaps(ws, ws_bytes, S_carry, nS) || overlaps(ws, ws_bytes, z_carry, nz))
+        return LA_E_ALIAS;
+    rc = precheck_plans(B, H, Lb, (int)start, d, gt, gh, gw, dtype, true, true);
+    if (rc != LA_OK) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    float* Sb = (float*)((char*)ws + L.state);
+    float* zb = Sb + (size_t)B * H * d * d;
+    rc = run_state(K, V, Sb, zb, commit ? S_carry : nullptr, commit ? z_carry : nullptr, S_carry, z_carry, ws, B,
+                   H, Lb, (int)start, d, gt, gh, gw, dtype, st);
+    if (rc != LA_OK) return rc;
+    return run_apply(Q, O, Sb, zb, B, H, Lb, (int)start, d, gt, gh, gw, eps, dtype, st);
+}
+
+const char* la_strerror(int status) {
+    switch (status) {
+        case LA_OK: return "ok";
+        case LA_E_NULLPTR: return "a required pointer is NULL";
+        case LA_E_SHAPE: return "invalid shape, grid or block arguments";
+        case LA_E_UNSUPPORTED: return "unsupported head dim, dtype or grid size";
+        case LA_E_ALIGN: return "pointer not 16-byte aligned";
+        case LA_E_WORKSPACE: return "workspace too small";
+        case LA_E_HIP: return "HIP runtime rejected a launch";
+        case LA_E_ALIAS: return "output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -88,3 +88,38 @@ def make_workload(name: str):
     w = WORKLOADS[name]
     q, k, v = make_qkv(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"], w["outliers"])
     return q, k, v, w
+
+
+def make_qkv_device(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0,
+                    device="cuda:0"):
+    """Draw Q, K, V ~ N(0, 1) of shape [B, H, N, d] directly on a GPU.
+
+    Uses torch's device generator seeded with `seed` (draw order Q, K, V) and
+    rounds to bf16 with torch's round-to-nearest-even cast.  Used for the large
+    workloads, where drawing gigabytes on the host would dominate run time;
+    callers copy the heads they check back to the host for the oracle.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = []
+    for _ in range(3):
+        a = torch.randn((B, H, N, d), generator=gen, dtype=torch.float32, device=device)
+        out.append(a.to(torch.bfloat16) if dtype == "bf16" else a)
+        del a
+    return tuple(out)
+
+
+def make_workload_device(name: str, device="cuda:0"):
+    """Device tensors of a named workload: (q, k, v, spec).
+
+    The two small workloads come from the numpy stream (make_qkv) and are
+    uploaded; the large ones are drawn on the device (make_qkv_device).
+    """
+    import torch
+    w = WORKLOADS[name]
+    if w["name"] in ("tiny", "480p"):
+        q, k, v = make_qkv(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"], w["outliers"])
+        tdt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+        return tuple(torch.from_numpy(a).to(device=device, dtype=tdt) for a in (q, k, v)) + (w,)
+    return make_qkv_device(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"], device) + (w,)

@@ -1,0 +1,163 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function include/la.h declares, and
+reject bad arguments with the documented status code before it launches
+anything.  Every call below fails an argument check, so the (fake) device
+addresses never reach a kernel.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+import linear_attention_video_02_amd as la  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(la.LIB_PATH):
+        from linear_attention_video_02_amd.build import build
+        build()
+    return la.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "la.h")).read()
+    return re.findall(r"LA_API\s+[\w\s\*]+?\b(la_\w+)\s*\(", text)
+
+
+def header_enum(name):
+    text = open(os.path.join(ROOT, "include", "la.h")).read()
+    m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+    return int(m.group(1))
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
+                          "la_block_causal_step", "la_strerror"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_codes_match_header():
+    for code, name in la.STATUS.items():
+        assert header_enum(name) == code
+    assert header_enum("LA_FP32") == la.LA_FP32 and header_enum("LA_BF16") == la.LA_BF16
+
+
+def test_strerror(L):
+    for code in list(la.STATUS) + [-99, 5]:
+        s = la.strerror(code)
+        assert isinstance(s, str) and s
+    assert la.strerror(-99) == "unknown status"
+
+
+def test_workspace_bytes(L):
+    a = la.workspace_bytes(2, 32, 19320, 64)
+    b = la.workspace_bytes(2, 32, 19320, 128)
+    assert a > 64 * 4160 * 4 and b > a
+    # independent of N (the state is O(d^2) per head)
+    assert la.workspace_bytes(1, 32, 220800, 64) == la.workspace_bytes(1, 32, 22080, 64)
+    assert la.workspace_bytes(1, 1, 10, 48) == 0
+    assert la.workspace_bytes(0, 1, 10, 64) == 0
+    assert la.workspace_bytes(1, 1, -1, 64) == 0
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def p(off=0):
+    return ctypes.c_void_p(FAKE + off)
+
+
+def state_call(L, **kw):
+    a = dict(Q=None, K=p(0), V=p(1 << 30), O=None, S=p(2 << 30), z=p(3 << 30), ws=p(4 << 30),
+             ws_bytes=1 << 40, B=1, H=2, N=256, d=64, gt=0, gh=0, gw=0, L=0, eps=1e-6,
+             dtype=la.LA_BF16)
+    a.update(kw)
+    return L.la_state_reduce(a["Q"], a["K"], a["V"], a["O"], a["S"], a["z"], a["ws"], a["ws_bytes"],
+                             a["B"], a["H"], a["N"], a["d"], a["gt"], a["gh"], a["gw"], a["L"],
+                             a["eps"], a["dtype"], None)
+
+
+def apply_call(L, **kw):
+    a = dict(Q=p(0), O=p(1 << 30), S=p(2 << 30), z=p(3 << 30), B=1, H=2, N=256, d=64,
+             gt=0, gh=0, gw=0, eps=1e-6, dtype=la.LA_BF16)
+    a.update(kw)
+    return L.la_apply(a["Q"], None, None, a["O"], a["S"], a["z"], None, 0, a["B"], a["H"], a["N"],
+                      a["d"], a["gt"], a["gh"], a["gw"], 0, a["eps"], a["dtype"], None)
+
+
+def step_call(L, **kw):
+    a = dict(Q=p(0), K=p(1 << 30), V=p(2 << 30), O=p(3 << 30), S=p(4 << 30), z=p(5 << 30),
+             ws=p(6 << 30), ws_bytes=1 << 40, B=1, H=2, N=1000, d=64, gt=10, gh=10, gw=10, blkL=300,
+             eps=1e-6, dtype=la.LA_BF16, blk=0, commit=1)
+    a.update(kw)
+    return L.la_block_causal_step(a["Q"], a["K"], a["V"], a["O"], a["S"], a["z"], a["ws"], a["ws_bytes"],
+                                  a["B"], a["H"], a["N"], a["d"], a["gt"], a["gh"], a["gw"], a["blkL"],
+                                  a["eps"], a["dtype"], a["blk"], a["commit"], None)
+
+
+E = {v: k for k, v in la.STATUS.items()}
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=48), "LA_E_UNSUPPORTED"),
+    (dict(d=256), "LA_E_UNSUPPORTED"),
+    (dict(dtype=7), "LA_E_UNSUPPORTED"),
+    (dict(B=0), "LA_E_SHAPE"),
+    (dict(H=-1), "LA_E_SHAPE"),
+    (dict(N=-5), "LA_E_SHAPE"),
+    (dict(eps=-1.0), "LA_E_SHAPE"),
+    (dict(eps=float("nan")), "LA_E_SHAPE"),
+    (dict(gt=1, gh=10, gw=10), "LA_E_SHAPE"),      # grid smaller than N
+    (dict(gt=3, gh=0, gw=10), "LA_E_SHAPE"),       # partly zero grid
+    (dict(K=None), "LA_E_NULLPTR"),
+    (dict(S=None), "LA_E_NULLPTR"),
+    (dict(ws=None), "LA_E_NULLPTR"),
+    (dict(V=p(8)), "LA_E_ALIGN"),
+    (dict(ws_bytes=1000), "LA_E_WORKSPACE"),
+    (dict(S=p(64)), "LA_E_ALIAS"),                 # S inside K
+    (dict(gt=1, gh=3000, gw=3000), "LA_E_UNSUPPORTED"),  # RoPE table cannot fit LDS
+])
+def test_state_reduce_rejects(L, kw, want):
+    assert state_call(L, **kw) == E[want]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=16), "LA_E_UNSUPPORTED"),
+    (dict(Q=None), "LA_E_NULLPTR"),
+    (dict(z=None), "LA_E_NULLPTR"),
+    (dict(O=p(4)), "LA_E_ALIGN"),
+    (dict(O=p(16)), "LA_E_ALIAS"),                 # O overlaps Q
+    (dict(gt=2, gh=2, gw=2), "LA_E_SHAPE"),
+])
+def test_apply_rejects(L, kw, want):
+    assert apply_call(L, **kw) == E[want]
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(blk=4), "LA_E_SHAPE"),                   # block starts past N
+    (dict(blk=-1), "LA_E_SHAPE"),
+    (dict(blkL=0), "LA_E_SHAPE"),
+    (dict(commit=2), "LA_E_SHAPE"),
+    (dict(S=None), "LA_E_NULLPTR"),
+    (dict(ws_bytes=10), "LA_E_WORKSPACE"),
+    (dict(O=p(1 << 30)), "LA_E_ALIAS"),           # O == K
+    (dict(z=p(4 << 30)), "LA_E_ALIAS"),           # z == S
+    (dict(d=100), "LA_E_UNSUPPORTED"),
+    (dict(Q=p(2)), "LA_E_ALIGN"),
+])
+def test_block_step_rejects(L, kw, want):
+    assert step_call(L, **kw) == E[want]
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(la, "_lib", None)
+    monkeypatch.setattr(la, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        la.lib()

@@ -1,0 +1,169 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerance (max over rows of ||got_i - ref_i||_inf / ||ref_i||_inf): 2e-2 for
+bf16 inputs, 1e-5 for fp32 inputs; an all-zero reference row needs an exact
+zero row.  Workloads: the five latent shapes (tiny, 480p, 720p-5s, 720p-60s
+block-causal, the d/N sweep) at full size -- every head for the small ones,
+sampled heads (all rows) for the large ones -- plus ragged/odd fuzz shapes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from _gpu import TOL, assert_close, host, say, state_err, upload
+from linear_attention_video_02_amd.inputs import (SWEEP_D, SWEEP_N, WORKLOADS, make_qkv,
+                                                  make_workload_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def la():
+    import linear_attention_video_02_amd as m
+    m.lib()
+    return m
+
+
+def _oracle_heads(q, k, v, heads, grid, eps):
+    out, S, z = [], [], []
+    for (b, h) in heads:
+        Sh, zh = oracle.state(k[b, h], v[b, h], grid)
+        out.append(oracle.apply(q[b, h], Sh, zh, grid, eps))
+        S.append(Sh)
+        z.append(zh)
+    return out, S, z
+
+
+def _check_bidirectional(la, name, heads=None):
+    import torch
+    tq, tk, tv, w = make_workload_device(name)
+    B, H, N, d, grid, eps, dt = w["B"], w["H"], w["N"], w["d"], w["grid"], w["eps"], w["dtype"]
+    say(f"[{name}] B={B} H={H} N={N} d={d} grid={grid} {dt}")
+    S, z = la.state_reduce(tk, tv, grid)
+    out = la.apply(tq, S, z, grid, eps)
+    torch.cuda.synchronize()
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    sel = lambda t: np.stack([host(t[b, h]) for (b, h) in heads])  # noqa: E731
+    q, k, v = sel(tq)[:, None], sel(tk)[:, None], sel(tv)[:, None]
+    ref_o, ref_S, ref_z = _oracle_heads(q, k, v, [(i, 0) for i in range(len(heads))], grid, eps)
+    got_o = sel(out)
+    got_S = np.stack([host(S[b, h]) for (b, h) in heads])
+    got_z = np.stack([host(z[b, h]) for (b, h) in heads])
+    assert_close(got_o, np.stack(ref_o), dt, f"{name} O ({len(heads)} heads)")
+    es = state_err(got_S, np.stack(ref_S))
+    say(f"  {name} S: {es:.3e}")
+    assert es <= TOL[dt]
+    np.testing.assert_allclose(got_z, np.stack(ref_z), rtol=1e-4, atol=1e-4)
+
+
+def test_tiny_fp32(la):
+    _check_bidirectional(la, "tiny")
+
+
+def test_tiny_fp32_against_weights_form(la):
+    """The tiny workload also against the O(N^2) explicit-weights form."""
+    import torch
+    tq, tk, tv, w = make_workload_device("tiny")
+    out = la.bidirectional(tq, tk, tv, None, w["eps"])
+    torch.cuda.synchronize()
+    got = host(out)
+    for h in range(w["H"]):
+        ref = oracle.weights_form_head(host(tq[0, h]), host(tk[0, h]), host(tv[0, h]), None, w["eps"])
+        assert_close(got[0, h], ref, "fp32", f"tiny head {h} vs O(N^2)")
+
+
+def test_480p(la):
+    _check_bidirectional(la, "480p")
+
+
+def test_720p5s(la):
+    _check_bidirectional(la, "720p5s")
+
+
+@pytest.mark.parametrize("d", SWEEP_D)
+@pytest.mark.parametrize("N", SWEEP_N)
+def test_sweep(la, d, N):
+    _check_bidirectional(la, f"sweep_d{d}_n{N}", heads=[(0, 0), (0, 19), (0, 31)])
+
+
+def test_720p60s_block_causal(la):
+    import torch
+    tq, tk, tv, w = make_workload_device("720p60s")
+    B, H, N, d, grid, L, eps = w["B"], w["H"], w["N"], w["d"], w["grid"], w["block"], w["eps"]
+    say(f"[720p60s] B={B} H={H} N={N} d={d} grid={grid} L={L}")
+    qb, kb, vb = (la.split_blocks(t, L) for t in (tq, tk, tv))
+    del tk, tv
+    outs, S, z = la.block_causal(qb, kb, vb, N, grid, L, eps)
+    torch.cuda.synchronize()
+    out = torch.cat(outs, dim=2)
+    for h in (0, 11, 31):
+        qh = np.concatenate([host(x[0, h]) for x in qb])
+        kh = np.concatenate([host(x[0, h]) for x in kb])
+        vh = np.concatenate([host(x[0, h]) for x in vb])
+        ref, Sr, zr = oracle.block_causal_head(qh, kh, vh, grid, L, eps)
+        assert_close(host(out[0, h]), ref, "bf16", f"720p60s head {h} O")
+        es = state_err(host(S[0, h]), Sr)
+        say(f"  carry S head {h}: {es:.3e}")
+        assert es <= 2e-2
+        np.testing.assert_allclose(host(z[0, h]), zr, rtol=1e-4)
+
+
+FUZZ = [
+    # B, H, N, d, dtype, grid, eps
+    (1, 1, 1, 64, "bf16", (1, 1, 1), 1e-6),
+    (1, 1, 7, 32, "fp32", (2, 2, 2), 1e-6),
+    (2, 3, 255, 64, "bf16", (3, 9, 10), 0.0),
+    (1, 2, 4097, 128, "bf16", (5, 23, 40), 1e-6),
+    (3, 1, 1000, 32, "bf16", None, 1e-6),
+    (1, 2, 1000, 64, "fp32", (4, 17, 19), 1e-6),
+    (1, 2, 777, 128, "fp32", (2, 20, 20), 1e-3),
+    (2, 2, 513, 32, "fp32", None, 0.0),
+    (1, 3, 130, 128, "bf16", (130, 1, 1), 1e-6),
+    (1, 1, 5000, 64, "bf16", (3, 41, 41), 1e-6),
+]
+
+
+@pytest.mark.parametrize("case", FUZZ, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{c[4]}" for c in FUZZ])
+def test_fuzz_shapes(la, case):
+    import torch
+    B, H, N, d, dt, grid, eps = case
+    say(f"[fuzz] {case}")
+    q, k, v = make_qkv(B, H, N, d, dt, seed=2000 + N + d)
+    out = la.bidirectional(upload(q, dt), upload(k, dt), upload(v, dt), grid, eps)
+    torch.cuda.synchronize()
+    ref = oracle.bidirectional(q, k, v, grid, eps)
+    assert_close(host(out), ref, dt, f"fuzz {case}")
+
+
+BC_FUZZ = [
+    # B, H, N, d, dtype, grid, L, eps
+    (1, 2, 1000, 64, "bf16", (10, 10, 10), 300, 1e-6),
+    (2, 1, 257, 32, "fp32", (3, 9, 10), 64, 1e-6),
+    (1, 1, 500, 128, "bf16", (5, 10, 10), 100, 0.0),
+    (1, 2, 100, 64, "fp32", (4, 5, 5), 1, 1e-6),
+    (1, 1, 640, 64, "bf16", None, 128, 1e-6),
+]
+
+
+@pytest.mark.parametrize("case", BC_FUZZ, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{c[4]}L{c[6]}" for c in BC_FUZZ])
+def test_fuzz_block_causal(la, case):
+    import torch
+    B, H, N, d, dt, grid, L, eps = case
+    say(f"[bc fuzz] {case}")
+    q, k, v = make_qkv(B, H, N, d, dt, seed=3000 + N + d)
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+    qb, kb, vb = (la.split_blocks(t, L) for t in (tq, tk, tv))
+    outs, S, z = la.block_causal(qb, kb, vb, N, grid, L, eps)
+    torch.cuda.synchronize()
+    ref, Sr, zr = oracle.block_causal(q, k, v, grid, L, eps)
+    assert_close(host(torch.cat(outs, dim=2)), ref, dt, f"bc fuzz {case}")
+    assert state_err(host(S).reshape(-1, d), Sr.reshape(-1, d)) <= TOL[dt]
+
+
+def test_state_reduce_empty_sequence(la):
+    import torch
+    k = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda:0")
+    S, z = la.state_reduce(k, k.clone(), None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S).item() == 0 and torch.count_nonzero(z).item() == 0
