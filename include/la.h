@@ -33,10 +33,9 @@
  *    into t, h, w ranges of d/2 - 2*floor(d/6), floor(d/6), floor(d/6) pairs;
  *    pair k of an axis with P_a pairs turns by pos_a * 10000^(-k/P_a).
  *  - ws is a device workspace of at least la_workspace_bytes(B, H, N, d)
- *    bytes.  It MUST be zero-filled once before its first use; every call
- *    leaves its first words zero again, so it can be reused call after call.
- *    One workspace must not be used by two calls that may overlap in time
- *    (two streams): they would race on it.
+ *    bytes (scratch for per-workgroup partial states; no initialisation
+ *    needed).  One workspace must not be used by two calls that may overlap
+ *    in time (two streams): they would race on it.
  *  - All pointers must be 16-byte aligned.  O must not overlap Q, K, V, S or z.
  *  - stream is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues kernels: it never allocates, never synchronises, and returns as
@@ -117,6 +116,11 @@ LA_API int la_block_causal_step(const void* Q, const void* K, const void* V, voi
 
 /* Static text for a status code (never NULL). */
 LA_API const char* la_strerror(int status);
+
+/* After LA_E_HIP: the failing HIP call, error name, code and description, as
+ * seen by the calling thread ("" if no HIP call has failed on this thread).
+ * The text stays valid until the thread's next failing call. */
+LA_API const char* la_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,10 @@ _lib = None
 class LinAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {STATUS.get(status, status)} ({strerror(status)})")
+        msg = f"{where}: {STATUS.get(status, status)} ({strerror(status)})"
+        if status == -6:
+            msg += ": " + lib().la_last_hip_error().decode()
+        super().__init__(msg)
 
 
 def lib() -> ctypes.CDLL:
@@ -39,6 +42,10 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        # PyTorch ships its own HIP/HSA runtime.  It must be the one in the
+        # process before the library is loaded, or the library would bring in
+        # the system runtime as a second, device-less instance.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, ci, cf, cs = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         common = [ci] * 8 + [cf, ci]  # B H N d gt gh gw block_tokens, eps, dtype
@@ -52,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.la_block_causal_step.restype = ci
         L.la_strerror.argtypes = [ci]
         L.la_strerror.restype = ctypes.c_char_p
+        L.la_last_hip_error.argtypes = []
+        L.la_last_hip_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -115,7 +124,7 @@ _ws_cache: dict = {}
 
 
 def workspace(B: int, H: int, N: int, d: int, device):
-    """A zero-filled workspace, cached per (device, size); reusable on one stream."""
+    """A workspace buffer, cached per (device, size); reusable on one stream."""
     torch = _torch()
     nbytes = workspace_bytes(B, H, N, d)
     if nbytes == 0:
@@ -124,7 +133,7 @@ def workspace(B: int, H: int, N: int, d: int, device):
     key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device(), nbytes)
     ws = _ws_cache.get(key)
     if ws is None:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -27,13 +28,12 @@ int env_int(const char* name, int dflt) {
 }
 
 struct WsLayout {
-    size_t ticket, partial, state, total;
+    size_t partial, state, total;
 };
 
 WsLayout ws_layout(int BH, int d) {
     WsLayout L;
-    L.ticket = 0;
-    L.partial = align_up((size_t)BH * 4, 256);
+    L.partial = 0;
     L.state = L.partial + align_up((size_t)BH * kMaxPartials * (d * d + d) * 4, 256);
     L.total = L.state + align_up((size_t)BH * (d * d + d) * 4, 256);
     return L;
@@ -126,10 +126,10 @@ struct Plan {
     size_t lds;
 };
 
-// State pass: about LA_STATE_WGS workgroups in all (default 1024, four per CU),
+// State pass: about LA_STATE_WGS workgroups in all (default 512, two per CU),
 // chunks a multiple of the 64-token tile, at most kMaxPartials per head.
 int plan_state(const LaGeom& g, int d, int dtype, Plan* out) {
-    const int target = env_int("LA_STATE_WGS", 1024);
+    const int target = env_int("LA_STATE_WGS", 512);
     const int tile = 64;
     const int ntok = g.ntok;
     int P = (target + g.BH - 1) / g.BH;
@@ -152,9 +152,9 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out) {
     }
 }
 
-// Apply pass: about LA_APPLY_WGS workgroups in all (default 2048).
+// Apply pass: about LA_APPLY_WGS workgroups in all (default 512).
 int plan_apply(const LaGeom& g, int d, int dtype, Plan* out) {
-    const int target = env_int("LA_APPLY_WGS", 2048);
+    const int target = env_int("LA_APPLY_WGS", 512);
     const int tile = 128;
     const int ntok = g.ntok;
     int P = (target + g.BH - 1) / g.BH;
@@ -180,15 +180,34 @@ int plan_apply(const LaGeom& g, int d, int dtype, Plan* out) {
 template <typename Args>
 using KernelFn = void (*)(Args);
 
+// Last HIP failure seen by this thread, for la_last_hip_error().
+thread_local char g_hip_msg[256];
+
+int hip_fail(hipError_t e, const char* what) {
+    snprintf(g_hip_msg, sizeof(g_hip_msg), "%s: %s (%d): %s", what, hipGetErrorName(e), (int)e,
+             hipGetErrorString(e));
+    return LA_E_HIP;
+}
+
 template <typename Args>
 int launch_kernel(KernelFn<Args> fn, dim3 grid, size_t lds, hipStream_t st, const Args& args) {
+    hipError_t e = hipGetLastError();  // clear a stale error so it is not reported as ours
+    (void)e;
     if (lds > 64 * 1024) {
-        if (hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-            hipSuccess)
-            return LA_E_HIP;
+        e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute");
     }
-    hipLaunchKernelGGL(fn, grid, dim3(256), lds, st, args);
-    return hipGetLastError() == hipSuccess ? LA_OK : LA_E_HIP;
+    Args copy = args;
+    void* params[] = {&copy};
+    e = hipLaunchKernel((const void*)fn, grid, dim3(256), params, lds, st);
+    if (e != hipSuccess) return hip_fail(e, "hipLaunchKernel");
+    return LA_OK;
+}
+
+KernelFn<CombineArgs> combine_kernel(int d) {
+    if (d == 32) return la_state_combine_kernel<32>;
+    if (d == 64) return la_state_combine_kernel<64>;
+    return la_state_combine_kernel<128>;
 }
 
 KernelFn<StateArgs> state_kernel(int d, int dtype, bool rope) {
@@ -230,17 +249,23 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     a.K = K;
     a.V = V;
     a.partial = (float*)((char*)ws + L.partial);
-    a.ticket = (unsigned*)((char*)ws + L.ticket);
-    a.S_out = S_out;
-    a.z_out = z_out;
-    a.S_out2 = S_out2;
-    a.z_out2 = z_out2;
-    a.S_carry = S_carry;
-    a.z_carry = z_carry;
     a.chunk = pl.chunk;
     a.P = pl.P;
     a.g = g;
-    return launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P, g.BH), pl.lds, st, a);
+    rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P, g.BH), pl.lds, st, a);
+    if (rc != LA_OK) return rc;
+    CombineArgs c;
+    c.partial = a.partial;
+    c.S_out = S_out;
+    c.z_out = z_out;
+    c.S_out2 = S_out2;
+    c.z_out2 = z_out2;
+    c.S_carry = S_carry;
+    c.z_carry = z_carry;
+    c.P = pl.P;
+    c.BH = g.BH;
+    const int e4 = (d * d + d) / 4;
+    return launch_kernel<CombineArgs>(combine_kernel(d), dim3((e4 + 255) / 256, g.BH), 0, st, c);
 }
 
 int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int H, int ntok, int n_offset,
@@ -365,6 +390,8 @@ int la_block_causal_step(const void* Q, const void* K, const void* V, void* O, f
     if (rc != LA_OK) return rc;
     return run_apply(Q, O, Sb, zb, B, H, Lb, (int)start, d, gt, gh, gw, eps, dtype, st);
 }
+
+const char* la_last_hip_error(void) { return g_hip_msg; }
 
 const char* la_strerror(int status) {
     switch (status) {

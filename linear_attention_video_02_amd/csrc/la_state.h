@@ -4,12 +4,14 @@
 //   S = sum_j RoPE(relu(K_j))^T V_j   (d x d, fp32)      z = sum_j relu(K_j)   (d, fp32)
 //
 // Work split: grid (P, B*H).  Workgroup p of head bh reduces the token chunk
-// [p*chunk, (p+1)*chunk) to a partial (S_p, z_p) in the workspace.  The last
-// workgroup of a head to finish (atomic ticket; the ticket orders no
-// arithmetic) sums the P partials in the fixed order p = 0..P-1, adds the
-// carried state when there is one (block-causal mode, Eq. 3 / Algorithm 1),
-// writes S and z, and resets the ticket to zero.  Results are therefore
-// bitwise reproducible for a given shape.
+// [p*chunk, (p+1)*chunk) to a partial (S_p, z_p) in the workspace.  A second,
+// small kernel (la_state_combine_kernel) sums the P partials of each head in
+// the fixed order p = 0..P-1, adds the carried state when there is one
+// (block-causal mode, Eq. 3 / Algorithm 1) and writes S and z.  No atomics
+// and no in-kernel cross-workgroup signalling: the kernel boundary makes the
+// partials visible (an in-kernel device-scope fence per workgroup would write
+// back and invalidate a whole XCD L2 each time).  Results are bitwise
+// reproducible for a given shape.
 #pragma once
 
 #include "la_common.h"
@@ -18,48 +20,74 @@ struct StateArgs {
     const void* K;
     const void* V;
     float* partial;        // [BH][P][D*D + D]
-    unsigned* ticket;      // [BH], zero on entry, zero again on exit
+    int chunk;             // tokens per workgroup
+    int P;                 // workgroups per (batch, head)
+    LaGeom g;
+};
+
+struct CombineArgs {
+    const float* partial;  // [BH][P][D*D + D]
     float* S_out;          // [BH][D*D]
     float* z_out;          // [BH][D]
     float* S_out2;         // optional second destination (block commit)
     float* z_out2;
     const float* S_carry;  // optional addend (block mode)
     const float* z_carry;
-    int chunk;             // tokens per workgroup
-    int P;                 // workgroups per (batch, head)
-    LaGeom g;
+    int P;
+    int BH;
 };
 
-// Called by every thread of a workgroup once its partial is in global memory.
+// Stage 2: grid (ceil(E4 / 256), B*H), one float4 of (S, z) per thread.  Sums
+// the P partials in the fixed order p = 0..P-1 (eight partials' loads in
+// flight before they are added), then adds the carry: S_b = carry + sum_p S_p.
 template <int D>
-__device__ void state_finish(const StateArgs& a, int bh, int* flag) {
-    __threadfence();  // release: this workgroup's partial is visible device-wide
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned prev = atomicAdd(&a.ticket[bh], 1u);
-        *flag = (prev == (unsigned)(a.P - 1));
-    }
-    __syncthreads();
-    if (!*flag) return;
-    __threadfence();  // acquire: every other workgroup's partial is visible
+__global__ __launch_bounds__(256) void la_state_combine_kernel(CombineArgs a) {
     constexpr int E = D * D + D;
-    const float* part = a.partial + (size_t)bh * a.P * E;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        float s = 0.0f;
-        for (int p = 0; p < a.P; ++p) s += part[(size_t)p * E + e];
-        if (e < D * D) {
-            size_t o = (size_t)bh * D * D + e;
-            if (a.S_carry) s = a.S_carry[o] + s;
-            a.S_out[o] = s;
-            if (a.S_out2) a.S_out2[o] = s;
-        } else {
-            size_t o = (size_t)bh * D + (e - D * D);
-            if (a.z_carry) s = a.z_carry[o] + s;
-            a.z_out[o] = s;
-            if (a.z_out2) a.z_out2[o] = s;
+    constexpr int E4 = E / 4;  // S and z regions both hold whole float4s (D % 4 == 0)
+    const int f = blockIdx.x * 256 + threadIdx.x;
+    const int bh = blockIdx.y;
+    if (f >= E4) return;
+    const float4* part = (const float4*)(a.partial + (size_t)bh * a.P * E);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int p = 0;
+    for (; p + 8 <= a.P; p += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(p + u) * E4 + f];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
         }
     }
-    if (threadIdx.x == 0) atomicExch(&a.ticket[bh], 0u);
+    {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (p + u < a.P) v[u] = part[(size_t)(p + u) * E4 + f];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (p + u < a.P) {
+                s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+            }
+    }
+    const int e = 4 * f;
+    if (e < D * D) {
+        const size_t o = (size_t)bh * D * D + e;
+        if (a.S_carry) {
+            const float4 c = *(const float4*)(a.S_carry + o);
+            s.x = c.x + s.x; s.y = c.y + s.y; s.z = c.z + s.z; s.w = c.w + s.w;
+        }
+        *(float4*)(a.S_out + o) = s;
+        if (a.S_out2) *(float4*)(a.S_out2 + o) = s;
+    } else {
+        const size_t o = (size_t)bh * D + (e - D * D);
+        if (a.z_carry) {
+            const float4 c = *(const float4*)(a.z_carry + o);
+            s.x = c.x + s.x; s.y = c.y + s.y; s.z = c.z + s.z; s.w = c.w + s.w;
+        }
+        *(float4*)(a.z_out + o) = s;
+        if (a.z_out2) *(float4*)(a.z_out2 + o) = s;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -107,8 +135,6 @@ __global__ __launch_bounds__(256) void la_state_bf16_kernel(StateArgs a) {
     uint16_t* ks = (uint16_t*)smem;
     uint16_t* vs = ks + D * C::PITCH;
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
-    __shared__ int flag;
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = blockIdx.x, bh = blockIdx.y;
     const int ntok = a.g.ntok;
@@ -276,7 +302,6 @@ __global__ __launch_bounds__(256) void la_state_bf16_kernel(StateArgs a) {
         for (int r = 0; r < C::ROWS; ++r) s += zr[((tid >> 3) + C::CH * r) * 8 + (tid & 7)];
         part[D * D + tid] = s;
     }
-    state_finish<D>(a, bh, &flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -298,8 +323,6 @@ __global__ __launch_bounds__(256) void la_state_f32_kernel(StateArgs a) {
     float* kq = kp + C::TT * D;    // RoPE(relu(K))
     float* vv = kq + C::TT * D;    // V
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
-    __shared__ int flag;
-
     const int tid = threadIdx.x;
     const int p = blockIdx.x, bh = blockIdx.y;
     const int ntok = a.g.ntok;
@@ -358,5 +381,4 @@ __global__ __launch_bounds__(256) void la_state_f32_kernel(StateArgs a) {
 #pragma unroll
     for (int j = 0; j < C::NE; ++j) part[tid + 256 * j] = acc[j];
     if (tid < D) part[D * D + tid] = zacc;
-    state_finish<D>(a, bh, &flag);
 }

@@ -38,7 +38,7 @@ def header_enum(name):
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
-                          "la_block_causal_step", "la_strerror"}
+                          "la_block_causal_step", "la_strerror", "la_last_hip_error"}
     for n in names:
         assert hasattr(L, n), n
 
