@@ -126,11 +126,16 @@ struct Plan {
     size_t lds;
 };
 
-// State pass: about LA_STATE_WGS workgroups in all (default 512, two per CU),
+// State pass: about LA_STATE_WGS workgroups in all (default: one 512-thread
+// workgroup per CU for bf16),
 // chunks a multiple of the 64-token tile, at most kMaxPartials per head.
 int plan_state(const LaGeom& g, int d, int dtype, Plan* out) {
-    const int target = env_int("LA_STATE_WGS", 512);
-    const int tile = 64;
+    const int target = env_int("LA_STATE_WGS", dtype == LA_BF16 ? 256 : 1024);
+    // chunks are whole tiles (the kernel's ring then runs on to a whole round
+    // with zero tiles: a little compute, no memory traffic)
+    const int tile = dtype == LA_BF16 ? (d == 32 ? StateBf16Cfg<32>::TT : d == 64 ? StateBf16Cfg<64>::TT
+                                                                              : StateBf16Cfg<128>::TT)
+                                      : 64;
     const int ntok = g.ntok;
     int P = (target + g.BH - 1) / g.BH;
     P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
@@ -152,9 +157,10 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out) {
     }
 }
 
-// Apply pass: about LA_APPLY_WGS workgroups in all (default 512).
+// Apply pass: about LA_APPLY_WGS workgroups in all (default: one 512-thread
+// workgroup per CU for bf16).
 int plan_apply(const LaGeom& g, int d, int dtype, Plan* out) {
-    const int target = env_int("LA_APPLY_WGS", 512);
+    const int target = env_int("LA_APPLY_WGS", dtype == LA_BF16 ? 256 : 1024);
     const int tile = 128;
     const int ntok = g.ntok;
     int P = (target + g.BH - 1) / g.BH;
@@ -190,7 +196,8 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 template <typename Args>
-int launch_kernel(KernelFn<Args> fn, dim3 grid, size_t lds, hipStream_t st, const Args& args) {
+int launch_kernel(KernelFn<Args> fn, dim3 grid, size_t lds, hipStream_t st, const Args& args,
+                  int threads = 256) {
     hipError_t e = hipGetLastError();  // clear a stale error so it is not reported as ours
     (void)e;
     if (lds > 64 * 1024) {
@@ -199,7 +206,7 @@ int launch_kernel(KernelFn<Args> fn, dim3 grid, size_t lds, hipStream_t st, cons
     }
     Args copy = args;
     void* params[] = {&copy};
-    e = hipLaunchKernel((const void*)fn, grid, dim3(256), params, lds, st);
+    e = hipLaunchKernel((const void*)fn, grid, dim3(threads), params, lds, st);
     if (e != hipSuccess) return hip_fail(e, "hipLaunchKernel");
     return LA_OK;
 }
@@ -252,7 +259,8 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     a.chunk = pl.chunk;
     a.P = pl.P;
     a.g = g;
-    rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P, g.BH), pl.lds, st, a);
+    rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a,
+                                  dtype == LA_BF16 ? kStateThreads : 256);
     if (rc != LA_OK) return rc;
     CombineArgs c;
     c.partial = a.partial;
@@ -284,7 +292,11 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
     a.chunk = pl.chunk;
     a.P = pl.P;
     a.g = g;
-    return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.P, g.BH), pl.lds, st, a);
+    const int threads = dtype != LA_BF16 ? 256
+                        : d == 32        ? ApplyBf16Cfg<32>::THREADS
+                        : d == 64        ? ApplyBf16Cfg<64>::THREADS
+                                         : ApplyBf16Cfg<128>::THREADS;
+    return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
 }
 
 size_t elem_bytes(int dtype) { return dtype == LA_BF16 ? 2 : 4; }

@@ -25,8 +25,10 @@ struct ApplyArgs {
 // every accumulator a lane holds belongs to one token (column n = lane % 16)
 // and the B operand -- 8 consecutive channels of one token -- is a plain
 // 16-byte load of Q.  S^T is held in registers for the whole workgroup as
-// bf16 hi + lo parts (S = hi + lo to ~2^-17), so the product carries only the
-// bf16 rounding of RoPE(relu Q).
+// bf16 hi + lo parts (S = hi + lo to ~2^-17; hi only at d = 128), and
+// RoPE(relu Q) is split the same way (hi truncated, lo rounded), so the
+// product S q is formed to ~2^-16 (a single bf16 rounding of RoPE(relu Q) costs up to ~1% in rows
+// whose sum over channels cancels).
 //
 // Lane (n = lane % 16, g = lane / 16) handles token n of a 16-token group and
 // the key channels 32*ks + 8*g .. +7, ks = 0 .. d/32 - 1.  Output tile T (16
@@ -34,53 +36,88 @@ struct ApplyArgs {
 // so a lane ends with 8 consecutive output channels per pair of tiles: one
 // 16-byte store each.  The denominator is summed over the 4 lanes of a token
 // with two cross-lane xors.
-// Each wave takes GR consecutive 16-token groups per iteration and prefetches
-// the next iteration's Q while computing.
+// One 512-thread workgroup (8 waves; 4 at d = 128) per CU over a chunk of one head; each
+// wave takes UNIT-token units of the chunk from an LDS queue and keeps DEPTH
+// units of Q in flight.
 // ---------------------------------------------------------------------------
 template <int D>
 struct ApplyBf16Cfg {
+    // 8 waves per CU; at d = 128 a lane needs ~350 registers, which only fits
+    // with 4 waves per workgroup (one per SIMD)
+    static constexpr int THREADS = D <= 64 ? 512 : 256;
+    static constexpr int NW = THREADS / 64;
     static constexpr int KS = D / 32;   // 32-channel k-steps
     static constexpr int NT = D / 16;   // 16-channel output tiles
-    static constexpr int GR = D <= 64 ? 2 : 1;   // 16-token groups per wave iteration
-    static constexpr int TOK_ITER = 4 * 16 * GR; // tokens per workgroup iteration
+    static constexpr int GR = D <= 64 ? 2 : 1;   // 16-token groups per unit of work
+    static constexpr int UNIT = 16 * GR;         // tokens a wave takes from the queue at a time
+    static constexpr int DEPTH = D <= 64 ? 3 : 2;  // units of Q in flight per wave
+    // S as bf16 hi + lo (to ~2^-17) needs d*d/32 registers per lane: 128 at
+    // d = 64, 512 at d = 128.  At d = 128 only the hi part is held (S rounded to
+    // bf16, relative error 2^-9 per entry).
+    static constexpr bool SLO = D <= 64;
 };
 
+// Work item mapping shared with the state pass (whole heads per XCD).
+__device__ __forceinline__ void apply_item_of_block(int P, int BH, int& bh, int& p) {
+    const int T = P * BH;
+    const int i = blockIdx.x;
+    const int k = (T % 8 == 0) ? (i % 8) * (T / 8) + i / 8 : i;
+    bh = k / P;
+    p = k % P;
+}
+
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
+__global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel(ApplyArgs a) {
     using C = ApplyBf16Cfg<D>;
     extern __shared__ __align__(16) unsigned char smem[];
     float2* tab = (float2*)smem;
+    __shared__ int q_next;  // next unit of this workgroup's chunk, in tokens
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
-    const int p = blockIdx.x, bh = blockIdx.y;
+    int bh, p;
+    apply_item_of_block(a.P, a.g.BH, bh, p);
     const int ntok = a.g.ntok;
     const int c0 = p * a.chunk;
     const int c1 = min(c0 + a.chunk, ntok);
-    const size_t head = (size_t)bh * ntok * D;
-    const uint16_t* Qh = (const uint16_t*)a.Q + head;
-    uint16_t* Oh = (uint16_t*)a.O + head;
+    const int len = c1 > c0 ? c1 - c0 : 0;
+    // Q and O of this chunk through descriptors bounded to [c0, c1): rows
+    // past c1 read as zeros and their stores are dropped.
+    const size_t chunk_off = ((size_t)bh * ntok + c0) * D;
+    const uint32_t chunk_bytes = (uint32_t)len * D * 2;
+    const BufRsrc Qr = make_rsrc((const uint16_t*)a.Q + chunk_off, chunk_bytes);
+    const BufRsrc Or = make_rsrc((uint16_t*)a.O + chunk_off, chunk_bytes);
 
-    // first iteration's loads go out before the prologue work
-    u32x4 qn[C::GR][C::KS];
-    auto load_iter = [&](int t0) {
+    if (threadIdx.x == 0) q_next = C::NW * C::DEPTH * C::UNIT;  // the first units are pre-assigned
+    // Units of UNIT tokens are taken from the workgroup's queue, so waves that
+    // run faster (the sequencer favours older waves) take more of the chunk.
+    auto grab = [&]() -> int {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&q_next, C::UNIT);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    u32x4 qr[C::DEPTH][C::GR][C::KS];
+    auto load_unit = [&](u32x4 (&q)[C::GR][C::KS], int u0) {
 #pragma unroll
         for (int r = 0; r < C::GR; ++r) {
-            const int tok = t0 + 16 * r + n;
+            const int tl = u0 + 16 * r + n;
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                if (tok < c1)
-                    qn[r][ks] = *(const u32x4*)(Qh + (size_t)tok * D + 32 * ks + 8 * g);
-                else
-                    qn[r][ks] = u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int ks = 0; ks < C::KS; ++ks)
+                q[r][ks] = buf_load16(Qr, (uint32_t)(tl * D + 32 * ks + 8 * g) * 2u);
         }
     };
-    const int tw0 = c0 + wave * 16 * C::GR;
-    load_iter(tw0);
+    // first DEPTH units of each wave: fixed, so their loads go out before the
+    // prologue work
+    const int wave = threadIdx.x >> 6;
+    int us[C::DEPTH];
+#pragma unroll
+    for (int s = 0; s < C::DEPTH; ++s) {
+        us[s] = (s * C::NW + wave) * C::UNIT;
+        load_unit(qr[s], us[s]);
+    }
 
     // S^T fragments (hi/lo bf16) and this lane's z entries
-    bf16x8 Ahi[C::NT][C::KS], Alo[C::NT][C::KS];
+    bf16x8 Ahi[C::NT][C::KS], Alo[C::SLO ? C::NT : 1][C::KS];
     const float* Sh = a.S + (size_t)bh * D * D;
 #pragma unroll
     for (int T = 0; T < C::NT; ++T) {
@@ -89,10 +126,10 @@ __global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
         for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float s = Sh[(32 * ks + 8 * g + e) * D + co];
-                const __bf16 hi = (__bf16)s;
+                const float sv = Sh[(32 * ks + 8 * g + e) * D + co];
+                const __bf16 hi = (__bf16)sv;
                 Ahi[T][ks][e] = hi;
-                Alo[T][ks][e] = (__bf16)(s - (float)hi);
+                if (C::SLO) Alo[C::SLO ? T : 0][ks][e] = (__bf16)(sv - (float)hi);
             }
         }
     }
@@ -103,72 +140,95 @@ __global__ __launch_bounds__(256) void la_apply_bf16_kernel(ApplyArgs a) {
         for (int e = 0; e < 8; ++e) zr[ks][e] = a.z[(size_t)bh * D + 32 * ks + 8 * g + e];
 
     int t_lo = 0, nt = 1;
+    PairRef pr[C::KS][4];
     if (ROPE) {
         const int cl = c1 > c0 ? c1 - 1 : c0;
         t_lo = (int)fdiv((uint32_t)(a.g.n_offset + c0), a.g.div_hw);
         nt = (int)fdiv((uint32_t)(a.g.n_offset + cl), a.g.div_hw) - t_lo + 1;
         build_rope_table(tab, t_lo, nt, a.g);
-        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[ks][i] = pair_ref(16 * ks + 4 * g + i, nt, a.g);
     }
+    lds_barrier();  // RoPE table and queue head visible
 
-    for (int t0 = tw0; t0 < c1; t0 += C::TOK_ITER) {
-        u32x4 qc[C::GR][C::KS];
+    bool more = true;
+    while (more) {
 #pragma unroll
-        for (int r = 0; r < C::GR; ++r)
+        for (int s = 0; s < C::DEPTH; ++s) {
+            const int u0 = us[s];
+            if (u0 >= len) {  // units are taken in increasing order: nothing left
+                more = false;
+                break;
+            }
+            u32x4 qc[C::GR][C::KS];
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) qc[r][ks] = qn[r][ks];
-        if (t0 + C::TOK_ITER < c1) load_iter(t0 + C::TOK_ITER);
+            for (int r = 0; r < C::GR; ++r)
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) qc[r][ks] = qr[s][r][ks];
+            us[s] = grab();
+            load_unit(qr[s], us[s]);
 
 #pragma unroll
-        for (int r = 0; r < C::GR; ++r) {
-            const int tok = t0 + 16 * r + n;
-            Pos3 ps;
-            if (ROPE) ps = token_pos((uint32_t)(a.g.n_offset + min(tok, c1 - 1)), t_lo, a.g);
-            float den = 0.0f;
-            bf16x8 Bq[C::KS];
+            for (int r = 0; r < C::GR; ++r) {
+                const int tl = u0 + 16 * r + n;  // token within the chunk
+                Pos3 ps;
+                if (ROPE) ps = token_pos((uint32_t)(a.g.n_offset + c0 + min(tl, len - 1)), t_lo, a.g);
+                float den = 0.0f;
+                bf16x8 Bq[C::KS], Bl[C::KS];
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[2 * i] = fmaxf(bf_lo(qc[r][ks][i]), 0.0f);
-                    x[2 * i + 1] = fmaxf(bf_hi(qc[r][ks][i]), 0.0f);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) den = fmaf(x[e], zr[ks][e], den);
-                if (ROPE) {
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    float x[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const PairRef pr = pair_ref(16 * ks + 4 * g + i, nt, a.g);
-                        rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr, ps)]);
+                        const uint32_t w = relu_bf16x2(qc[r][ks][i]);
+                        x[2 * i] = bf_lo(w);
+                        x[2 * i + 1] = bf_hi(w);
                     }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) den = fmaf(x[e], zr[ks][e], den);
+                    if (ROPE) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[ks][i], ps)]);
+                    }
+                    u32x4 hw, lw;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t h, l;
+                        split_bf16x2(x[2 * i], x[2 * i + 1], h, l);
+                        hw[i] = h;
+                        lw[i] = l;
+                    }
+                    Bq[ks] = __builtin_bit_cast(bf16x8, hw);
+                    Bl[ks] = __builtin_bit_cast(bf16x8, lw);
                 }
+                f32x4 acc[C::NT];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) Bq[ks][e] = (__bf16)x[e];
-            }
-            f32x4 acc[C::NT];
+                for (int T = 0; T < C::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int T = 0; T < C::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
+                    for (int T = 0; T < C::NT; ++T) {
+                        // S q = S_hi q_hi + S_lo q_hi + S_hi q_lo  (S_lo q_lo ~ 2^-18 dropped)
+                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi[T][ks], Bq[ks], acc[T], 0, 0, 0);
+                        if (C::SLO)
+                            acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo[C::SLO ? T : 0][ks], Bq[ks],
+                                                                             acc[T], 0, 0, 0);
+                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi[T][ks], Bl[ks], acc[T], 0, 0, 0);
+                    }
+                den += __shfl_xor(den, 16);
+                den += __shfl_xor(den, 32);
+                den += a.eps;
+                const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll
-                for (int T = 0; T < C::NT; ++T) {
-                    acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi[T][ks], Bq[ks], acc[T], 0, 0, 0);
-                    acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo[T][ks], Bq[ks], acc[T], 0, 0, 0);
-                }
-            den += __shfl_xor(den, 16);
-            den += __shfl_xor(den, 32);
-            den += a.eps;
-            const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-            if (tok < c1) {
-#pragma unroll
-                for (int s = 0; s < C::NT / 2; ++s) {
+                for (int sp = 0; sp < C::NT / 2; ++sp) {
                     u32x4 o;
-                    o[0] = pack_bf16(acc[2 * s][0] * inv, acc[2 * s][1] * inv);
-                    o[1] = pack_bf16(acc[2 * s][2] * inv, acc[2 * s][3] * inv);
-                    o[2] = pack_bf16(acc[2 * s + 1][0] * inv, acc[2 * s + 1][1] * inv);
-                    o[3] = pack_bf16(acc[2 * s + 1][2] * inv, acc[2 * s + 1][3] * inv);
-                    *(u32x4*)(Oh + (size_t)tok * D + 32 * s + 8 * g) = o;
+                    o[0] = pack_bf16(acc[2 * sp][0] * inv, acc[2 * sp][1] * inv);
+                    o[1] = pack_bf16(acc[2 * sp][2] * inv, acc[2 * sp][3] * inv);
+                    o[2] = pack_bf16(acc[2 * sp + 1][0] * inv, acc[2 * sp + 1][1] * inv);
+                    o[3] = pack_bf16(acc[2 * sp + 1][2] * inv, acc[2 * sp + 1][3] * inv);
+                    buf_store16(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
                 }
             }
         }
@@ -196,7 +256,8 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
 
     const int tid = threadIdx.x;
-    const int p = blockIdx.x, bh = blockIdx.y;
+    int bh, p;
+    apply_item_of_block(a.P, a.g.BH, bh, p);
     const int ntok = a.g.ntok;
     const int c0 = p * a.chunk;
     const int c1 = min(c0 + a.chunk, ntok);
@@ -214,7 +275,7 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
         build_rope_table(tab, t_lo, nt, a.g);
     }
     for (int t0 = c0; t0 < c1; t0 += C::TT) {
-        __syncthreads();
+        lds_barrier();
         for (int i = tid; i < C::TT * D / 2; i += 256) {
             const int tl = i / (D / 2), pp = i % (D / 2);
             const int tok = t0 + tl;
@@ -233,13 +294,13 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
             qq[tl * D + 2 * pp] = x0;
             qq[tl * D + 2 * pp + 1] = x1;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < C::TT) {
             float s = 0.0f;
             for (int c = 0; c < D; ++c) s = fmaf(qp[tid * D + c], zs[c], s);
             dn[tid] = s + a.eps;
         }
-        __syncthreads();
+        lds_barrier();
         for (int i = tid; i < C::TT * D; i += 256) {
             const int tl = i / D, co = i % D;
             const int tok = t0 + tl;

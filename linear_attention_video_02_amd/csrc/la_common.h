@@ -10,29 +10,34 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 // ---------------------------------------------------------------------------
-// exact division by a runtime constant: q = floor(n / d) for 0 <= n < 2^31
-// (Granlund-Montgomery round-up multiplier: m = floor(2^(31+l) / d) + 1 with
-//  l = ceil(log2 d); then m*d - 2^(31+l) <= d <= 2^l, which makes
-//  floor(n*m / 2^(31+l)) exact for every n < 2^31, and n*m < 2^64.)
+// exact division by a runtime constant: q = floor(n / d) for 0 <= n < 2^31.
+// With l = ceil(log2 d) >= 1 and m = ceil(2^(31+l) / d) (which fits 32 bits
+// because d > 2^(l-1)), m*d - 2^(31+l) <= d - 1, so floor(n*m / 2^(31+l)) is
+// exact whenever n*(d-1) < 2^(31+l), i.e. for every n < 2^31.  On the device
+// that is one v_mul_hi_u32 and one shift.  d = 1 is flagged separately.
 // ---------------------------------------------------------------------------
 struct FastDiv {
-    uint64_t m;
-    uint32_t shift;  // 31 + l
+    uint32_t m;
+    uint32_t shift;  // l - 1
+    uint32_t one;    // d == 1
     uint32_t d;
 };
 
 static inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.one = d == 1;
     uint32_t l = 0;
     while ((1ull << l) < d) ++l;
-    FastDiv f;
-    f.shift = 31 + l;
-    f.m = ((1ull << f.shift) / d) + 1;
-    f.d = d;
+    if (l == 0) l = 1;
+    const uint64_t k = 1ull << (31 + l);
+    f.m = (uint32_t)((k + d - 1) / d);
+    f.shift = l - 1;
     return f;
 }
 
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
-    return (uint32_t)(((uint64_t)n * f.m) >> f.shift);
+    return f.one ? n : (__umulhi(n, f.m) >> f.shift);
 }
 
 // ---------------------------------------------------------------------------
@@ -49,6 +54,61 @@ struct LaGeom {
 };
 
 // ---------------------------------------------------------------------------
+// buffer loads/stores through a resource descriptor bounded to a byte range:
+// reads past the range return 0 and writes past it are dropped, in hardware,
+// so the ragged end of a token chunk needs no branches (and the compiler can
+// keep counting outstanding loads exactly instead of draining them).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+
+__device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t nbytes) {
+    // third descriptor word for gfx9-family raw (stride 0) buffers
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(BufRsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store16(u32x4 v, BufRsrc r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// Workgroup barrier for an LDS hand-off only.  __syncthreads() also orders
+// global memory, which on gfx9 (loads and stores share vmcnt) drains every
+// prefetched load before each barrier; this one waits for LDS operations only.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane j,
+// element e is element (j % 4) of what input lane 4e + j/4 addressed.  So if
+// lane i of a group addresses X[r0 + i/4][c0 + 4*(i%4)] of a row-major bf16
+// tile X[row][col], lane j receives X[r0 .. r0+3][c0 + j]: four consecutive
+// rows of one column, which is half of an MFMA operand fragment whose k index
+// runs along rows.  (Checked on the device with an in-bounds layout probe.)
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr4(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(p));
+}
+
+// Two transposed reads -> one 8-element bf16 operand (rows r0..r0+7 of one column).
+__device__ __forceinline__ bf16x8 lds_read_tr8(const uint16_t* p_rows0_3, const uint16_t* p_rows4_7) {
+    const s16x4 a = lds_read_tr4(p_rows0_3);
+    const s16x4 b = lds_read_tr4(p_rows4_7);
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
 // bf16 <-> fp32
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -63,8 +123,27 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Split two floats into bf16 hi (truncated: the top 16 bits) and bf16 lo
+// (x - hi, rounded to nearest even).  hi + lo equals x to 2^-16 relative.
+// Returns (packed hi, packed lo).
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    hi = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // high halves: a in bits 0-15, b in 16-31
+    lo = pack_bf16(a - __uint_as_float(ua & 0xffff0000u), b - __uint_as_float(ub & 0xffff0000u));
+}
+
 __device__ __forceinline__ float bf16_round(float a) {
     return bf_lo(pack_bf16(a, 0.0f) & 0xffffu);
+}
+
+// relu of two packed bf16 values: a bf16 with the sign bit set reads as a
+// negative int16 and a non-negative one as a non-negative int16, so a signed
+// 16-bit max against 0 is relu (and maps -0 to +0).  One v_pk_max_i16.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
+    typedef __attribute__((ext_vector_type(2))) short s16x2;
+    s16x2 v = __builtin_bit_cast(s16x2, w);
+    s16x2 z = {0, 0};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(v, z));
 }
 
 // ---------------------------------------------------------------------------
@@ -105,24 +184,18 @@ __device__ inline void build_rope_table(float2* tab, int t_lo, int nt, const LaG
     }
 }
 
-// Where pair p's (cos, sin) lives: entry = base + pos_axis * stride.
-struct PairRef {
-    int base, stride, axis;
-};
+// Where pair p's (cos, sin) lives: entry = base + row offset of its axis,
+// where the row offsets of a token are (t - t_lo) * pt, h * ph, w * pw.
+// Packed in one register as base * 4 + axis.
+typedef int PairRef;
 
 __device__ __forceinline__ PairRef pair_ref(int p, int nt, const LaGeom& g) {
-    PairRef r;
-    if (p < g.pt) {
-        r.base = p; r.stride = g.pt; r.axis = 0;
-    } else if (p < g.pt + g.ph) {
-        r.base = nt * g.pt + (p - g.pt); r.stride = g.ph; r.axis = 1;
-    } else {
-        r.base = nt * g.pt + g.gh * g.ph + (p - g.pt - g.ph); r.stride = g.pw; r.axis = 2;
-    }
-    return r;
+    if (p < g.pt) return p * 4;
+    if (p < g.pt + g.ph) return (nt * g.pt + (p - g.pt)) * 4 + 1;
+    return (nt * g.pt + g.gh * g.ph + (p - g.pt - g.ph)) * 4 + 2;
 }
 
-// (t - t_lo, h, w) of global token n
+// Table row offsets of global token n: ((t - t_lo) * pt, h * ph, w * pw)
 struct Pos3 {
     int t, h, w;
 };
@@ -132,15 +205,21 @@ __device__ __forceinline__ Pos3 token_pos(uint32_t n, int t_lo, const LaGeom& g)
     uint32_t r = n - t * (uint32_t)(g.gh * g.gw);
     uint32_t h = fdiv(r, g.div_w);
     Pos3 p;
-    p.t = (int)t - t_lo;
-    p.h = (int)h;
-    p.w = (int)(r - h * (uint32_t)g.gw);
+    p.t = ((int)t - t_lo) * g.pt;
+    p.h = (int)h * g.ph;
+    p.w = (int)(r - h * (uint32_t)g.gw) * g.pw;
     return p;
 }
 
-__device__ __forceinline__ int pair_entry(const PairRef& r, const Pos3& p) {
-    int pos = r.axis == 0 ? p.t : (r.axis == 1 ? p.h : p.w);
-    return r.base + pos * r.stride;
+// Table entry of a pair for a token: base + the row offset of the pair's axis.
+// Everything is passed by value and selected arithmetically: a select between
+// fields of a struct held by reference gets turned into an indexed load from a
+// private (scratch) array.
+__device__ __forceinline__ int pair_entry(PairRef r, Pos3 p) {
+    const int axis = r & 3;
+    const int dh = axis >= 1 ? p.h - p.t : 0;
+    const int dw = axis >= 2 ? p.w - p.h : 0;
+    return (r >> 2) + p.t + dh + dw;
 }
 
 // rotate (x0, x1) by the angle whose (cos, sin) is cs

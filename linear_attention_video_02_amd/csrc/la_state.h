@@ -91,75 +91,112 @@ __global__ __launch_bounds__(256) void la_state_combine_kernel(CombineArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Work item of a workgroup: (head, chunk).  Workgroups are dealt round-robin
+// to the 8 XCDs by linear id; this mapping gives XCD x a contiguous run of
+// items (whole heads) instead of one chunk position of every head.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void item_of_block(int P, int BH, int& bh, int& p) {
+    const int T = P * BH;
+    const int i = blockIdx.x;
+    const int k = (T % 8 == 0) ? (i % 8) * (T / 8) + i / 8 : i;
+    bh = k / P;
+    p = k % P;
+}
+
+// ---------------------------------------------------------------------------
 // bf16 inputs: MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation.
 //
-// Per 64-token tile: every thread loads 16-byte pieces (8 channels of one
-// token) of K and V, coalesced.  K gets relu, the z partial (un-rotated),
-// RoPE at the token's global grid position, and bf16 rounding; K and V are
-// then written to LDS TRANSPOSED (row = channel, 64 tokens per row) so that
-// an MFMA operand -- 8 consecutive tokens of one channel -- is one 16-byte
-// LDS read.  8-token column blocks are XOR-swizzled by channel block to
-// spread LDS banks.  MFMA: C[c_in][c_out] += A[c_in][tok] B[tok][c_out] with
-// A = RoPE(relu K)^T, B = V.
-//   d = 32, 64: wave w takes tokens 16w..16w+15 of the tile and all d x d
-//               outputs; the 4 waves are summed in LDS at the end in the
-//               fixed order (w0 + w1) + (w2 + w3).
-//   d = 128:    wave w takes key channels 32w..32w+31, all 64 tokens.
+// One 512-thread workgroup (8 waves) per CU: two workgroups sharing a CU run
+// at unequal speed (the sequencer favours older waves), which left half of
+// every CU idle at the end of the pass.
+//
+// Per tile of TT tokens: every thread loads 16-byte pieces (8 channels of one
+// token) of K and V through bounded buffer descriptors, coalesced.  K gets
+// relu, the z partial (un-rotated), RoPE at the token's global grid position,
+// and a split into bf16 hi + lo (hi + lo = RoPE(relu K) to 2^-16: a single
+// bf16 rounding costs up to ~2% in rows whose sum over tokens cancels, e.g.
+// the pair partners of outlier channels).  hi, lo and V go to LDS row-major
+// (row = token, no padding) with one 16-byte write each; 32-channel column
+// blocks are XOR-swizzled by row so that the four rows a transposed read
+// touches fall in distinct banks.  MFMA operands -- 8 consecutive tokens of
+// one channel -- come back with two ds_read_b64_tr_b16.
+// MFMA: C[c_in][c_out] += A[c_in][tok] B[tok][c_out], A = (hi, lo)^T, B = V.
+//   d = 32, 64: TT = 128; wave w takes tokens 16w..16w+15 of the tile and all
+//               d x d outputs; the 8 waves are summed in LDS at the end in
+//               the fixed order ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7)).
+//   d = 128:    TT = 64; wave w takes key channels 32(w%4).., tokens
+//               32(w/4)..+31; waves w and w+4 are summed in that order.
+// Two LDS buffers: tile t's MFMAs read one while tile t+1 is staged into the
+// other, with one barrier per tile.  DEPTH tiles of K/V are in flight per
+// workgroup (a register ring refilled right after each tile is staged).
 // ---------------------------------------------------------------------------
+constexpr int kStateThreads = 512;
+
 template <int D>
 struct StateBf16Cfg {
+    static constexpr int NW = kStateThreads / 64;
     static constexpr int CH = D / 8;          // 16-byte pieces per token row
-    static constexpr int ROWS = 256 / CH;     // token rows per load pass
-    static constexpr int TT = 64;             // tokens per tile
+    static constexpr int ROWS = kStateThreads / CH;  // token rows per load pass
+    static constexpr int TT = D <= 64 ? 128 : 64;   // tokens per tile
     static constexpr int LP = TT / ROWS;      // load passes per tile
-    static constexpr int PITCH = TT + 8;      // LDS row pitch (bf16) of the transposed tiles
+    static constexpr int DEPTH = D <= 64 ? 4 : 2;  // tiles of K/V in flight per workgroup
+    static constexpr int TILE = TT * D;       // elements per LDS tile (unpadded)
+    static constexpr int BUF = 3 * TILE;      // K hi, K lo, V
     static constexpr bool SPLIT_TOK = D <= 64;
     static constexpr int NI = SPLIT_TOK ? D / 32 : 1;   // key-channel tiles per wave
     static constexpr int NJ = D / 32;                   // value-channel tiles per wave
-    static constexpr int KSTEPS = SPLIT_TOK ? 1 : 4;    // 16-token steps per wave per tile
-    static constexpr int STAGE_BYTES = 2 * D * PITCH * 2;
-    static constexpr int RED_BYTES = SPLIT_TOK ? 64 * NI * NJ * 16 * 4 : 0;
-    static constexpr int ZRED_BYTES = 256 * 8 * 4;
+    static constexpr int KSTEPS = SPLIT_TOK ? 1 : TT / 32;  // 16-token steps per wave per tile
+    static constexpr int STAGE_BYTES = 2 * BUF * 2;
+    static constexpr int RED_BYTES = (SPLIT_TOK ? NW / 2 : 4) * 64 * NI * NJ * 16 * 4;
+    static constexpr int ZRED_BYTES = kStateThreads * 8 * 4;
     static constexpr int m1 = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
     static constexpr int SMEM_FIXED = m1 > ZRED_BYTES ? m1 : ZRED_BYTES;
+    static_assert(LP >= 1 && ROWS * LP == TT, "tile / load-pass shape");
+    static_assert(SPLIT_TOK ? TT == 16 * NW : KSTEPS * 32 == TT, "k-steps");
 };
 
-__device__ __forceinline__ int swz_col(int c, int tok) {
-    return (((tok >> 3) ^ ((c >> 3) & 7)) << 3) | (tok & 7);
+// Element offset of (row, ch) in a swizzled row-major tile: 32-channel block
+// b of row r is stored at block b ^ s(r), with s chosen per d so that rows
+// r0..r0+3 (r0 % 4 == 0) start in different 16-bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int row, int ch) {
+    const int s = D == 32 ? 0 : (D == 64 ? ((row >> 1) & 1) : (row & 3));
+    return row * D + (((ch >> 5) ^ s) << 5) + (ch & 31);
 }
 
 template <int D, bool ROPE>
-__global__ __launch_bounds__(256) void la_state_bf16_kernel(StateArgs a) {
+__global__ __launch_bounds__(kStateThreads) void la_state_bf16_kernel(StateArgs a) {
     using C = StateBf16Cfg<D>;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* ks = (uint16_t*)smem;
-    uint16_t* vs = ks + D * C::PITCH;
+    uint16_t* lds = (uint16_t*)smem;   // [2][3][TT*D]: buffer, (K hi, K lo, V)
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int p = blockIdx.x, bh = blockIdx.y;
+    int bh, p;
+    item_of_block(a.P, a.g.BH, bh, p);
     const int ntok = a.g.ntok;
     const int c0 = p * a.chunk;
     const int c1 = min(c0 + a.chunk, ntok);
-    const size_t head = (size_t)bh * ntok * D;
-    const uint16_t* Kh = (const uint16_t*)a.K + head;
-    const uint16_t* Vh = (const uint16_t*)a.V + head;
+    // K and V of this chunk through descriptors bounded to [c0, c1): tokens
+    // past c1 read as zeros, which add nothing to S or z.
+    const size_t chunk_off = ((size_t)bh * ntok + c0) * D;
+    const uint32_t chunk_bytes = c1 > c0 ? (uint32_t)(c1 - c0) * D * 2 : 0u;
+    const BufRsrc Kr = make_rsrc((const uint16_t*)a.K + chunk_off, chunk_bytes);
+    const BufRsrc Vr = make_rsrc((const uint16_t*)a.V + chunk_off, chunk_bytes);
     const int cc = tid % C::CH, trow = tid / C::CH;
 
-    u32x4 kr[C::LP], vr[C::LP];
-    auto load_tile = [&](int t0) {
+    // ring of DEPTH tiles in registers: tile i lives in slot i % DEPTH
+    u32x4 kr[C::DEPTH][C::LP], vr[C::DEPTH][C::LP];
+    auto load_tile = [&](u32x4 (&kk)[C::LP], u32x4 (&vv)[C::LP], int tile) {
 #pragma unroll
         for (int j = 0; j < C::LP; ++j) {
-            int tok = t0 + trow + j * C::ROWS;
-            if (tok < c1) {
-                kr[j] = *(const u32x4*)(Kh + (size_t)tok * D + 8 * cc);
-                vr[j] = *(const u32x4*)(Vh + (size_t)tok * D + 8 * cc);
-            } else {
-                kr[j] = u32x4{0u, 0u, 0u, 0u};
-                vr[j] = u32x4{0u, 0u, 0u, 0u};
-            }
+            const uint32_t off = (uint32_t)((tile * C::TT + trow + j * C::ROWS) * D + 8 * cc) * 2u;
+            kk[j] = buf_load16(Kr, off);
+            vv[j] = buf_load16(Vr, off);
         }
     };
-    if (c0 < c1) load_tile(c0);
+#pragma unroll
+    for (int s = 0; s < C::DEPTH; ++s) load_tile(kr[s], vr[s], s);
 
     int t_lo = 0;
     PairRef pr[4];
@@ -175,6 +212,45 @@ __global__ __launch_bounds__(256) void la_state_bf16_kernel(StateArgs a) {
     float zp[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) zp[e] = 0.0f;
+
+    // stage tile `tile` (held in ring slot s) into LDS buffer `buf`
+    auto stage = [&](int s, int buf, int tile) {
+        uint16_t* khi = lds + buf * C::BUF;
+        uint16_t* klo = khi + C::TILE;
+        uint16_t* vt = klo + C::TILE;
+#pragma unroll
+        for (int j = 0; j < C::LP; ++j) {
+            const int tl = trow + j * C::ROWS;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w = relu_bf16x2(kr[s][j][i]);
+                x[2 * i] = bf_lo(w);
+                x[2 * i + 1] = bf_hi(w);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zp[e] += x[e];
+            if (ROPE) {
+                const int tok = min(c0 + tile * C::TT + tl, c1 - 1);
+                const Pos3 ps = token_pos((uint32_t)(a.g.n_offset + tok), t_lo, a.g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[i], ps)]);
+            }
+            u32x4 hw, lw;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t h, l;
+                split_bf16x2(x[2 * i], x[2 * i + 1], h, l);
+                hw[i] = h;
+                lw[i] = l;
+            }
+            const int o = swz<D>(tl, 8 * cc);
+            *(u32x4*)(khi + o) = hw;
+            *(u32x4*)(klo + o) = lw;
+            *(u32x4*)(vt + o) = vr[s][j];
+        }
+    };
+
     f32x16 acc[C::NI][C::NJ];
 #pragma unroll
     for (int i = 0; i < C::NI; ++i)
@@ -183,124 +259,135 @@ __global__ __launch_bounds__(256) void la_state_bf16_kernel(StateArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int m = lane & 31, gq = lane >> 5;
+    // transposed-read addressing: 16-lane group (q, g) reads rows
+    // kb0 + 8g + 4h + i16/4, columns 32*tile + 16q + 4*(i16%4)
+    const int i16 = lane & 15, q = (lane >> 4) & 1, gq = lane >> 5, m = lane & 31;
+    const int rd_row = 8 * gq + (i16 >> 2);
+    const int rd_col = 16 * q + 4 * (i16 & 3);
+    const int ctile = C::SPLIT_TOK ? 0 : (wave & 3);      // key-channel tile (d = 128)
+    const int tgrp = C::SPLIT_TOK ? wave : (wave >> 2);   // token group of this wave
 
-    for (int t0 = c0; t0 < c1; t0 += C::TT) {
-        __syncthreads();  // LDS tiles free (and RoPE table complete)
+    const int ntiles = c1 > c0 ? (c1 - c0 + C::TT - 1) / C::TT : 0;
+    if (ntiles > 0) {
+        lds_barrier();  // RoPE table complete
+        stage(0, 0, 0);
+        load_tile(kr[0], vr[0], C::DEPTH);
+        lds_barrier();
+    }
+    // Whole rounds of the ring, no early exit: tiles past the chunk end are
+    // zeros from the bounded descriptor and add nothing, and a uniform trip
+    // count keeps the compiler's count of outstanding loads exact.
+    for (int tb = 0; tb < ntiles; tb += C::DEPTH) {
 #pragma unroll
-        for (int j = 0; j < C::LP; ++j) {
-            const int tl = trow + j * C::ROWS;
-            float x[8];
-            const uint32_t w4[4] = {kr[j][0], kr[j][1], kr[j][2], kr[j][3]};
+        for (int s = 0; s < C::DEPTH; ++s) {
+            const int t = tb + s;            // tile consumed now, in LDS buffer s & 1
+            const int cur = s & 1;           // (DEPTH is even)
+            const uint16_t* khi = lds + cur * C::BUF;
+            const uint16_t* klo = khi + C::TILE;
+            const uint16_t* vt = klo + C::TILE;
+            bf16x8 Ah[C::KSTEPS][C::NI], Al[C::KSTEPS][C::NI], Bv[C::KSTEPS][C::NJ];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = fmaxf(bf_lo(w4[i]), 0.0f);
-                x[2 * i + 1] = fmaxf(bf_hi(w4[i]), 0.0f);
+            for (int st = 0; st < C::KSTEPS; ++st) {
+                const int kb0 = C::SPLIT_TOK ? 16 * tgrp : 32 * tgrp + 16 * st;
+                const int r0 = kb0 + rd_row, r1 = r0 + 4;
+#pragma unroll
+                for (int i = 0; i < C::NI; ++i) {
+                    const int col = 32 * (C::SPLIT_TOK ? i : ctile) + rd_col;
+                    Ah[st][i] = lds_read_tr8(khi + swz<D>(r0, col), khi + swz<D>(r1, col));
+                    Al[st][i] = lds_read_tr8(klo + swz<D>(r0, col), klo + swz<D>(r1, col));
+                }
+#pragma unroll
+                for (int j = 0; j < C::NJ; ++j) {
+                    const int col = 32 * j + rd_col;
+                    Bv[st][j] = lds_read_tr8(vt + swz<D>(r0, col), vt + swz<D>(r1, col));
+                }
             }
+            // stage the next tile into the other buffer while these MFMAs run
+            const int sn = (s + 1) % C::DEPTH;
+            stage(sn, cur ^ 1, t + 1);
+            load_tile(kr[sn], vr[sn], t + 1 + C::DEPTH);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) zp[e] += x[e];
-            if (ROPE) {
-                int tok = min(t0 + tl, c1 - 1);
-                Pos3 ps = token_pos((uint32_t)(a.g.n_offset + tok), t_lo, a.g);
+            for (int st = 0; st < C::KSTEPS; ++st)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[i], ps)]);
-            }
-            uint32_t kw[4];
+                for (int i = 0; i < C::NI; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) kw[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = 8 * cc + e;
-                const int col = swz_col(c, tl);
-                ks[c * C::PITCH + col] = (uint16_t)(kw[e >> 1] >> ((e & 1) * 16));
-                vs[c * C::PITCH + col] = (uint16_t)(vr[j][e >> 1] >> ((e & 1) * 16));
-            }
-        }
-        __syncthreads();
-        if (t0 + C::TT < c1) load_tile(t0 + C::TT);
-
-#pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s) {
-            const int kb = C::SPLIT_TOK ? 2 * wave + gq : 2 * s + gq;  // 8-token block
-            bf16x8 A[C::NI], Bv[C::NJ];
-#pragma unroll
-            for (int i = 0; i < C::NI; ++i) {
-                const int c = 32 * (C::SPLIT_TOK ? i : wave) + m;
-                A[i] = *(const bf16x8*)(ks + c * C::PITCH + ((kb ^ ((c >> 3) & 7)) << 3));
-            }
-#pragma unroll
-            for (int j = 0; j < C::NJ; ++j) {
-                const int c = 32 * j + m;
-                Bv[j] = *(const bf16x8*)(vs + c * C::PITCH + ((kb ^ ((c >> 3) & 7)) << 3));
-            }
-#pragma unroll
-            for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-                for (int j = 0; j < C::NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[i], Bv[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < C::NJ; ++j) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah[st][i], Bv[st][j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al[st][i], Bv[st][j], acc[i][j], 0, 0, 0);
+                    }
+            lds_barrier();
         }
     }
 
-    // ---- fold the waves (d <= 64): fixed order (w0 + w1) + (w2 + w3) ----
+    // ---- fold the waves' accumulators in a fixed order ----
     float* red = (float*)smem;
     constexpr int NACC = C::NI * C::NJ * 16;
+    static_assert(NACC * 64 * 4 * (C::SPLIT_TOK ? C::NW / 2 : 4) <= C::SMEM_FIXED, "reduction buffer");
+    // wave `src` parks its accumulators in slot `slot`; wave `dst` adds them
+    auto put = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    red[((slot * NACC) + (i * C::NJ + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    };
+    auto add = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] += red[((slot * NACC) + (i * C::NJ + j) * 16 + r) * 64 + lane];
+    };
+    lds_barrier();
     if (C::SPLIT_TOK) {
-        auto put = [&]() {
-#pragma unroll
-            for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-                for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) red[((i * C::NJ + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-        };
-        auto add = [&]() {
-#pragma unroll
-            for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-                for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * C::NJ + j) * 16 + r) * 64 + lane];
-        };
-        static_assert(NACC * 64 * 4 <= C::SMEM_FIXED, "reduction buffer");
-        __syncthreads();
-        if (wave == 1) put();
-        __syncthreads();
-        if (wave == 0) add();
-        __syncthreads();
-        if (wave == 3) put();
-        __syncthreads();
-        if (wave == 2) add();
-        __syncthreads();
-        if (wave == 2) put();
-        __syncthreads();
-        if (wave == 0) add();
+        // ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7))
+        if (wave & 1) put(wave >> 1);
+        lds_barrier();
+        if (!(wave & 1)) add(wave >> 1);
+        lds_barrier();
+        if ((wave & 3) == 2) put(wave >> 2);
+        lds_barrier();
+        if ((wave & 3) == 0) add(wave >> 2);
+        lds_barrier();
+        if (wave == 4) put(0);
+        lds_barrier();
+        if (wave == 0) add(0);
+    } else {
+        // w + (w + 4) for each key-channel tile
+        if (wave >= 4) put(wave & 3);
+        lds_barrier();
+        if (wave < 4) add(wave);
     }
 
     // ---- write this workgroup's partial ----
     constexpr int E = D * D + D;
     float* part = a.partial + ((size_t)bh * a.P + p) * E;
-    if (!C::SPLIT_TOK || wave == 0) {
+    if (C::SPLIT_TOK ? wave == 0 : wave < 4) {
 #pragma unroll
         for (int i = 0; i < C::NI; ++i)
 #pragma unroll
             for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * (C::SPLIT_TOK ? i : wave) + 8 * (r >> 2) + 4 * gq + (r & 3);
+                    const int row = 32 * (C::SPLIT_TOK ? i : ctile) + 8 * (r >> 2) + 4 * gq + (r & 3);
                     const int col = 32 * j + m;
                     part[row * D + col] = acc[i][j][r];
                 }
     }
     // ---- z partial: threads sharing a channel block, summed in thread order ----
-    __syncthreads();
+    lds_barrier();
     float* zr = (float*)smem;
 #pragma unroll
     for (int e = 0; e < 8; ++e) zr[tid * 8 + e] = zp[e];
-    __syncthreads();
+    lds_barrier();
     if (tid < D) {
-        float s = 0.0f;
-        for (int r = 0; r < C::ROWS; ++r) s += zr[((tid >> 3) + C::CH * r) * 8 + (tid & 7)];
-        part[D * D + tid] = s;
+        float sum = 0.0f;
+        for (int r = 0; r < C::ROWS; ++r) sum += zr[((tid >> 3) + C::CH * r) * 8 + (tid & 7)];
+        part[D * D + tid] = sum;
     }
 }
 
@@ -324,7 +411,8 @@ __global__ __launch_bounds__(256) void la_state_f32_kernel(StateArgs a) {
     float* vv = kq + C::TT * D;    // V
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
     const int tid = threadIdx.x;
-    const int p = blockIdx.x, bh = blockIdx.y;
+    int bh, p;
+    item_of_block(a.P, a.g.BH, bh, p);
     const int ntok = a.g.ntok;
     const int c0 = p * a.chunk;
     const int c1 = min(c0 + a.chunk, ntok);
@@ -345,7 +433,7 @@ __global__ __launch_bounds__(256) void la_state_f32_kernel(StateArgs a) {
     float zacc = 0.0f;
 
     for (int t0 = c0; t0 < c1; t0 += C::TT) {
-        __syncthreads();
+        lds_barrier();
         for (int i = tid; i < C::TT * D / 2; i += 256) {
             const int tl = i / (D / 2), pp = i % (D / 2);
             const int tok = t0 + tl;
@@ -366,7 +454,7 @@ __global__ __launch_bounds__(256) void la_state_f32_kernel(StateArgs a) {
             vv[tl * D + 2 * pp] = v0;
             vv[tl * D + 2 * pp + 1] = v1;
         }
-        __syncthreads();
+        lds_barrier();
         for (int tl = 0; tl < C::TT; ++tl) {
 #pragma unroll
             for (int j = 0; j < C::NE; ++j) {
