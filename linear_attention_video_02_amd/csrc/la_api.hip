@@ -259,8 +259,11 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     a.chunk = pl.chunk;
     a.P = pl.P;
     a.g = g;
-    rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a,
-                                  dtype == LA_BF16 ? kStateThreads : 256);
+    const int threads = dtype != LA_BF16 ? 256
+                        : d == 32        ? StateBf16Cfg<32>::THREADS
+                        : d == 64        ? StateBf16Cfg<64>::THREADS
+                                         : StateBf16Cfg<128>::THREADS;
+    rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
     if (rc != LA_OK) return rc;
     CombineArgs c;
     c.partial = a.partial;

@@ -106,9 +106,9 @@ __device__ __forceinline__ void item_of_block(int P, int BH, int& bh, int& p) {
 // ---------------------------------------------------------------------------
 // bf16 inputs: MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation.
 //
-// One 512-thread workgroup (8 waves) per CU: two workgroups sharing a CU run
-// at unequal speed (the sequencer favours older waves), which left half of
-// every CU idle at the end of the pass.
+// One workgroup per CU (two workgroups sharing a CU run at unequal speed:
+// the sequencer favours older waves).  d <= 64: 1024 threads (4 waves per
+// SIMD, <= 128 registers a lane); d = 128: 512 threads.
 //
 // Per tile of TT tokens: every thread loads 16-byte pieces (8 channels of one
 // token) of K and V through bounded buffer descriptors, coalesced.  K gets
@@ -121,38 +121,36 @@ __device__ __forceinline__ void item_of_block(int P, int BH, int& bh, int& p) {
 // touches fall in distinct banks.  MFMA operands -- 8 consecutive tokens of
 // one channel -- come back with two ds_read_b64_tr_b16.
 // MFMA: C[c_in][c_out] += A[c_in][tok] B[tok][c_out], A = (hi, lo)^T, B = V.
-//   d = 32, 64: TT = 128; wave w takes tokens 16w..16w+15 of the tile and all
-//               d x d outputs; the 8 waves are summed in LDS at the end in
-//               the fixed order ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7)).
-//   d = 128:    TT = 64; wave w takes key channels 32(w%4).., tokens
-//               32(w/4)..+31; waves w and w+4 are summed in that order.
+// Wave w owns key-channel tile w % NCI (32 rows of S, all value channels)
+// and token group w / NCI of every tile; at the end the NTG token groups of
+// each key-channel tile are summed in LDS in a fixed pairwise-tree order.
 // Two LDS buffers: tile t's MFMAs read one while tile t+1 is staged into the
 // other, with one barrier per tile.  DEPTH tiles of K/V are in flight per
 // workgroup (a register ring refilled right after each tile is staged).
 // ---------------------------------------------------------------------------
-constexpr int kStateThreads = 512;
-
 template <int D>
 struct StateBf16Cfg {
-    static constexpr int NW = kStateThreads / 64;
+    static constexpr int THREADS = D <= 64 ? 1024 : 512;
+    static constexpr int NW = THREADS / 64;
     static constexpr int CH = D / 8;          // 16-byte pieces per token row
-    static constexpr int ROWS = kStateThreads / CH;  // token rows per load pass
-    static constexpr int TT = D <= 64 ? 128 : 64;   // tokens per tile
-    static constexpr int LP = TT / ROWS;      // load passes per tile
-    static constexpr int DEPTH = D <= 64 ? 4 : 2;  // tiles of K/V in flight per workgroup
+    static constexpr int ROWS = THREADS / CH; // token rows per load pass
+    static constexpr int LP = D <= 64 ? 1 : 2;  // load passes per tile
+    static constexpr int TT = ROWS * LP;      // tokens per tile: 256, 128, 64
+    static constexpr int DEPTH = 2;           // tiles of K/V in flight per workgroup
     static constexpr int TILE = TT * D;       // elements per LDS tile (unpadded)
     static constexpr int BUF = 3 * TILE;      // K hi, K lo, V
-    static constexpr bool SPLIT_TOK = D <= 64;
-    static constexpr int NI = SPLIT_TOK ? D / 32 : 1;   // key-channel tiles per wave
-    static constexpr int NJ = D / 32;                   // value-channel tiles per wave
-    static constexpr int KSTEPS = SPLIT_TOK ? 1 : TT / 32;  // 16-token steps per wave per tile
+    static constexpr int NCI = D / 32;        // key-channel tiles = wave groups
+    static constexpr int NTG = NW / NCI;      // token groups
+    static constexpr int NJ = D / 32;         // value-channel tiles per wave
+    static constexpr int KSTEPS = TT / (16 * NTG);  // 16-token steps per wave per tile
+    static constexpr int NACC = NJ * 16;      // accumulators per lane
     static constexpr int STAGE_BYTES = 2 * BUF * 2;
-    static constexpr int RED_BYTES = (SPLIT_TOK ? NW / 2 : 4) * 64 * NI * NJ * 16 * 4;
-    static constexpr int ZRED_BYTES = kStateThreads * 8 * 4;
+    static constexpr int RED_BYTES = (NW / 2) * 64 * NACC * 4;
+    static constexpr int ZRED_BYTES = THREADS * 8 * 4;
     static constexpr int m1 = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
     static constexpr int SMEM_FIXED = m1 > ZRED_BYTES ? m1 : ZRED_BYTES;
-    static_assert(LP >= 1 && ROWS * LP == TT, "tile / load-pass shape");
-    static_assert(SPLIT_TOK ? TT == 16 * NW : KSTEPS * 32 == TT, "k-steps");
+    static_assert(KSTEPS >= 1 && KSTEPS * 16 * NTG == TT, "k-steps");
+    static_assert((NTG & (NTG - 1)) == 0, "token groups: power of two");
 };
 
 // Element offset of (row, ch) in a swizzled row-major tile: 32-channel block
@@ -165,7 +163,7 @@ __device__ __forceinline__ int swz(int row, int ch) {
 }
 
 template <int D, bool ROPE>
-__global__ __launch_bounds__(kStateThreads) void la_state_bf16_kernel(StateArgs a) {
+__global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel(StateArgs a) {
     using C = StateBf16Cfg<D>;
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* lds = (uint16_t*)smem;   // [2][3][TT*D]: buffer, (K hi, K lo, V)
@@ -251,21 +249,19 @@ __global__ __launch_bounds__(kStateThreads) void la_state_bf16_kernel(StateArgs 
         }
     };
 
-    f32x16 acc[C::NI][C::NJ];
+    f32x16 acc[C::NJ];
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i)
+    for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
-        for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
 
     // transposed-read addressing: 16-lane group (q, g) reads rows
     // kb0 + 8g + 4h + i16/4, columns 32*tile + 16q + 4*(i16%4)
     const int i16 = lane & 15, q = (lane >> 4) & 1, gq = lane >> 5, m = lane & 31;
     const int rd_row = 8 * gq + (i16 >> 2);
     const int rd_col = 16 * q + 4 * (i16 & 3);
-    const int ctile = C::SPLIT_TOK ? 0 : (wave & 3);      // key-channel tile (d = 128)
-    const int tgrp = C::SPLIT_TOK ? wave : (wave >> 2);   // token group of this wave
+    const int ctile = wave % C::NCI;   // key-channel tile of this wave
+    const int tgrp = wave / C::NCI;    // token group of this wave
 
     const int ntiles = c1 > c0 ? (c1 - c0 + C::TT - 1) / C::TT : 0;
     if (ntiles > 0) {
@@ -285,21 +281,18 @@ __global__ __launch_bounds__(kStateThreads) void la_state_bf16_kernel(StateArgs 
             const uint16_t* khi = lds + cur * C::BUF;
             const uint16_t* klo = khi + C::TILE;
             const uint16_t* vt = klo + C::TILE;
-            bf16x8 Ah[C::KSTEPS][C::NI], Al[C::KSTEPS][C::NI], Bv[C::KSTEPS][C::NJ];
+            bf16x8 Ah[C::KSTEPS], Al[C::KSTEPS], Bv[C::KSTEPS][C::NJ];
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st) {
-                const int kb0 = C::SPLIT_TOK ? 16 * tgrp : 32 * tgrp + 16 * st;
+                const int kb0 = 16 * (tgrp * C::KSTEPS + st);
                 const int r0 = kb0 + rd_row, r1 = r0 + 4;
-#pragma unroll
-                for (int i = 0; i < C::NI; ++i) {
-                    const int col = 32 * (C::SPLIT_TOK ? i : ctile) + rd_col;
-                    Ah[st][i] = lds_read_tr8(khi + swz<D>(r0, col), khi + swz<D>(r1, col));
-                    Al[st][i] = lds_read_tr8(klo + swz<D>(r0, col), klo + swz<D>(r1, col));
-                }
+                const int col = 32 * ctile + rd_col;
+                Ah[st] = lds_read_tr8(khi + swz<D>(r0, col), khi + swz<D>(r1, col));
+                Al[st] = lds_read_tr8(klo + swz<D>(r0, col), klo + swz<D>(r1, col));
 #pragma unroll
                 for (int j = 0; j < C::NJ; ++j) {
-                    const int col = 32 * j + rd_col;
-                    Bv[st][j] = lds_read_tr8(vt + swz<D>(r0, col), vt + swz<D>(r1, col));
+                    const int vcol = 32 * j + rd_col;
+                    Bv[st][j] = lds_read_tr8(vt + swz<D>(r0, vcol), vt + swz<D>(r1, vcol));
                 }
             }
             // stage the next tile into the other buffer while these MFMAs run
@@ -309,77 +302,55 @@ __global__ __launch_bounds__(kStateThreads) void la_state_bf16_kernel(StateArgs 
 #pragma unroll
             for (int st = 0; st < C::KSTEPS; ++st)
 #pragma unroll
-                for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::NJ; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah[st][i], Bv[st][j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al[st][i], Bv[st][j], acc[i][j], 0, 0, 0);
-                    }
+                for (int j = 0; j < C::NJ; ++j) {
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah[st], Bv[st][j], acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al[st], Bv[st][j], acc[j], 0, 0, 0);
+                }
             lds_barrier();
         }
     }
 
-    // ---- fold the waves' accumulators in a fixed order ----
+    // ---- fold the token groups of each key-channel tile: pairwise tree in a
+    //      fixed order, level by level (group g += group g + 2^l) ----
     float* red = (float*)smem;
-    constexpr int NACC = C::NI * C::NJ * 16;
-    static_assert(NACC * 64 * 4 * (C::SPLIT_TOK ? C::NW / 2 : 4) <= C::SMEM_FIXED, "reduction buffer");
-    // wave `src` parks its accumulators in slot `slot`; wave `dst` adds them
-    auto put = [&](int slot) {
-#pragma unroll
-        for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    red[((slot * NACC) + (i * C::NJ + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-    };
-    auto add = [&](int slot) {
-#pragma unroll
-        for (int i = 0; i < C::NI; ++i)
-#pragma unroll
-            for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    acc[i][j][r] += red[((slot * NACC) + (i * C::NJ + j) * 16 + r) * 64 + lane];
-    };
+    static_assert(C::RED_BYTES <= C::SMEM_FIXED, "reduction buffer");
     lds_barrier();
-    if (C::SPLIT_TOK) {
-        // ((w0+w1)+(w2+w3)) + ((w4+w5)+(w6+w7))
-        if (wave & 1) put(wave >> 1);
+#pragma unroll
+    for (int lvl = 1; lvl < C::NTG; lvl <<= 1) {
+        const bool sender = (tgrp & (2 * lvl - 1)) == lvl;
+        const bool receiver = (tgrp & (2 * lvl - 1)) == 0;
+        // slot of the sending wave: one per (receiver group, key-channel tile)
+        const int slot = (tgrp / (2 * lvl)) * C::NCI + ctile;
+        if (sender) {
+#pragma unroll
+            for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) red[(slot * C::NACC + j * 16 + r) * 64 + lane] = acc[j][r];
+        }
         lds_barrier();
-        if (!(wave & 1)) add(wave >> 1);
+        if (receiver) {
+#pragma unroll
+            for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[j][r] += red[(slot * C::NACC + j * 16 + r) * 64 + lane];
+        }
         lds_barrier();
-        if ((wave & 3) == 2) put(wave >> 2);
-        lds_barrier();
-        if ((wave & 3) == 0) add(wave >> 2);
-        lds_barrier();
-        if (wave == 4) put(0);
-        lds_barrier();
-        if (wave == 0) add(0);
-    } else {
-        // w + (w + 4) for each key-channel tile
-        if (wave >= 4) put(wave & 3);
-        lds_barrier();
-        if (wave < 4) add(wave);
     }
 
-    // ---- write this workgroup's partial ----
+    // ---- write this workgroup's partial (token group 0 holds the sums) ----
     constexpr int E = D * D + D;
     float* part = a.partial + ((size_t)bh * a.P + p) * E;
-    if (C::SPLIT_TOK ? wave == 0 : wave < 4) {
+    if (tgrp == 0) {
 #pragma unroll
-        for (int i = 0; i < C::NI; ++i)
+        for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
-            for (int j = 0; j < C::NJ; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * (C::SPLIT_TOK ? i : ctile) + 8 * (r >> 2) + 4 * gq + (r & 3);
-                    const int col = 32 * j + m;
-                    part[row * D + col] = acc[i][j][r];
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int row = 32 * ctile + 8 * (r >> 2) + 4 * gq + (r & 3);
+                const int col = 32 * j + m;
+                part[row * D + col] = acc[j][r];
+            }
     }
     // ---- z partial: threads sharing a channel block, summed in thread order ----
-    lds_barrier();
     float* zr = (float*)smem;
 #pragma unroll
     for (int e = 0; e < 8; ++e) zr[tid * 8 + e] = zp[e];
