@@ -36,25 +36,46 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, src_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+STATE_KERNELS = ("la_state_bf16_kernel", "la_state_combine_kernel")
+APPLY_KERNELS = ("la_apply_bf16_kernel",)
+CALIB_KERNEL = "MulFunctor"   # torch's elementwise o = q * 1: a plain copy of known size
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_720p5s.json")
+
+# The profiler runs whose summaries are committed (run from /tmp, with the
+# repository at $REPO); the summaries are then written by --summarize-*.
+PROFILE_COMMANDS = {
+    "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/la_prof/trace -o trace "
+             "-- python3 $REPO/bench.py --steps 50 --warmup 5 --no-cpu-baseline",
+    "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/la_prof/fetch -o fetch "
+             "-- python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+    "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/la_prof/write -o write "
+             "-- python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+}
+
+
+def load_traffic(kernels, src_hash):
+    """HBM bytes per launch of a pass from the committed counter summary, or None.
 
     The summary records the kernel-source hash it was taken with; if the
     kernels changed since, the counters no longer describe them.
     """
-    path = os.path.join(ROOT, "profiles", "traffic_720p5s.json")
     try:
-        with open(path) as f:
+        with open(TRAFFIC_JSON) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("src_hash") != src_hash or kernel not in t.get("kernels", {}):
+    per = t.get("kernels", {})
+    if t.get("src_hash") != src_hash or any(k not in per for k in kernels):
         return None
-    return t["kernels"][kernel].get("hbm_bytes_per_launch")
+    return sum(per[k]["hbm_bytes_per_launch"] for k in kernels)
 
 
 def cpu_baseline(q, k, v, spec, budget_s=12.0):
-    """Time the fp64 oracle on whole (batch, head) slices until ~budget_s."""
+    """Time the fp64 oracle on the workload's (batch, head) slices.
+
+    Whole slices (all N tokens of one head), in order, pass after pass over the
+    workload, until about budget_s of oracle time has been spent.
+    """
     import numpy as np
 
     import oracle
@@ -66,27 +87,144 @@ def cpu_baseline(q, k, v, spec, budget_s=12.0):
         blas_threads = 1
     slices, t_used = 0, 0.0
     order = [(b, h) for b in range(B) for h in range(H)]
-    for (b, h) in order:
-        qh = q[b, h].float().cpu().numpy().astype(np.float64)
-        kh = k[b, h].float().cpu().numpy().astype(np.float64)
-        vh = v[b, h].float().cpu().numpy().astype(np.float64)
+    host = {}
+    while t_used < budget_s:
+        b, h = order[slices % len(order)]
+        if (b, h) not in host:
+            host[(b, h)] = tuple(x[b, h].float().cpu().numpy().astype(np.float64) for x in (q, k, v))
+        qh, kh, vh = host[(b, h)]
         t0 = time.perf_counter()
         S, z = oracle.state(kh, vh, grid)
         oracle.apply(qh, S, z, grid, eps)
         t_used += time.perf_counter() - t0
         slices += 1
-        if t_used >= budget_s:
-            break
     tokens = slices * N / H  # a token is one grid position across all H heads
     return {
         "value": tokens / t_used,
         "unit": "tokens/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"{slices} of {B * H} (batch, head) slices of the {WORKLOAD} workload, "
-                  f"all {N} tokens each, fp64 numpy, {t_used:.1f} s "
+        "sample": f"{slices} (batch, head) slices of the {WORKLOAD} workload in order "
+                  f"({slices / len(order):.1f} passes over its {len(order)} slices), all {N} "
+                  f"tokens each, fp64 numpy, {t_used:.1f} s of oracle time "
                   f"({len(os.sched_getaffinity(0))} host cores visible)",
     }
+
+
+def _find(path, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {path}")
+    return hits[0]
+
+
+def _short(name):
+    for k in STATE_KERNELS + APPLY_KERNELS:
+        if k + "<" in name or name.startswith(k):
+            return k
+    if CALIB_KERNEL in name:
+        return "calibration copy (torch mul by 1)"
+    return None
+
+
+def summarize_trace(trace_dir, command, out_path):
+    """Per-kernel durations of the timed steps from a rocprofv3 --kernel-trace run."""
+    import csv
+    rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    la = [r for r in rows if _short(r["Kernel_Name"]) in STATE_KERNELS + APPLY_KERNELS]
+    # the timed steps are the last `steps` state/combine/apply triples
+    steps = len(la) // 3
+    dur = {}
+    for r in la:
+        dur.setdefault(_short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    stats = list(csv.DictReader(open(_find(trace_dir, "kernel_stats.csv"))))
+    lines = [f"# Kernel durations, {WORKLOAD} workload (bf16, B=2 H=32 N=19320 d=64, RoPE)", "",
+             "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
+             "rocprofv3 --stats summary, this library's kernels (all launches, warm-up included):", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for st in stats:
+        k = _short(st["Name"])
+        if k in STATE_KERNELS + APPLY_KERNELS:
+            lines.append(f"| {k} | {st['Calls']} | {float(st['AverageNs']) / 1e3:.1f} | "
+                         f"{float(st['MinNs']) / 1e3:.1f} | {float(st['MaxNs']) / 1e3:.1f} |")
+    # gaps inside a step, from the trace: state end -> combine start -> apply start
+    gaps = []
+    for i in range(len(la) - 2):
+        a, b, c = (_short(la[j]["Kernel_Name"]) for j in (i, i + 1, i + 2))
+        if (a, b, c) == STATE_KERNELS + APPLY_KERNELS:
+            gaps.append(((int(la[i + 1]["Start_Timestamp"]) - int(la[i]["End_Timestamp"])) / 1e3,
+                         (int(la[i + 2]["Start_Timestamp"]) - int(la[i + 1]["End_Timestamp"])) / 1e3,
+                         (int(la[i + 2]["End_Timestamp"]) - int(la[i]["Start_Timestamp"])) / 1e3,
+                         (int(la[i + 1]["End_Timestamp"]) - int(la[i]["Start_Timestamp"])) / 1e3))
+    if gaps:
+        n = len(gaps)
+        lines += ["", f"From the trace, over {n} steps (state kernel start to apply kernel end):", "",
+                  f"- state pass (state kernel start to combine kernel end): "
+                  f"{sum(g[3] for g in gaps) / n:.1f} us",
+                  f"- gap state -> combine: {sum(g[0] for g in gaps) / n:.2f} us, "
+                  f"combine -> apply: {sum(g[1] for g in gaps) / n:.2f} us",
+                  f"- whole step: {sum(g[2] for g in gaps) / n:.1f} us"]
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return steps
+
+
+def summarize_pmc(fetch_dir, write_dir, commands, out_json, out_md, src_hash, tensor_bytes):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs, scaled by a copy kernel.
+
+    Both counters are in KiB per dispatch.  The calibration kernel reads
+    `tensor_bytes` and writes `tensor_bytes`; the ratio of those to what the
+    counters report for it scales every other kernel's counts.
+    """
+    import csv
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            k = _short(r["Kernel_Name"])
+            if k is None or r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(k, []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    cal = "calibration copy (torch mul by 1)"
+    if cal not in fetch or cal not in write:
+        raise SystemExit("calibration copy kernel missing from the counter runs")
+    f_scale = tensor_bytes / fetch[cal]
+    w_scale = tensor_bytes / write[cal]
+    algo = {"la_state_bf16_kernel": 2 * tensor_bytes, "la_apply_bf16_kernel": 2 * tensor_bytes}
+    kernels = {}
+    for k in STATE_KERNELS + APPLY_KERNELS:
+        if k in fetch and k in write:
+            rd, wr = fetch[k] * f_scale, write[k] * w_scale
+            kernels[k] = {"fetch_bytes_raw": fetch[k], "write_bytes_raw": write[k],
+                          "read_bytes": rd, "write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
+                          "algorithmic_bytes": algo.get(k)}
+    out = {"workload": WORKLOAD, "src_hash": src_hash, "fetch_scale": f_scale, "write_scale": w_scale,
+           "calibration": f"{cal}: reads {tensor_bytes} B and writes {tensor_bytes} B per launch",
+           "commands": commands, "kernels": kernels}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# HBM traffic per launch, {WORKLOAD} workload", "", "Commands (repository root, one MI355X):",
+             "", "```", *commands, "```", "",
+             f"Scale factors from the calibration copy (reads and writes {tensor_bytes / 1e6:.1f} MB): "
+             f"FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.", "",
+             "| kernel | FETCH_SIZE raw MB | WRITE_SIZE raw MB | read MB (scaled) | write MB (scaled) | "
+             "algorithmic MB |", "|---|---|---|---|---|---|"]
+    for k, v in kernels.items():
+        a = v["algorithmic_bytes"]
+        lines.append(f"| {k} | {v['fetch_bytes_raw'] / 1e6:.1f} | {v['write_bytes_raw'] / 1e6:.2f} | "
+                     f"{v['read_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.2f} | "
+                     f"{a / 1e6 if a else 0:.1f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main():
@@ -96,10 +234,32 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write the kernel-duration summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic summary of rocprofv3 FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--out", default=os.path.join(ROOT, "profiles"), help="where summaries go")
     args = ap.parse_args()
+    if args.summarize_trace or args.summarize_pmc:
+        from linear_attention_video_02_amd.inputs import WORKLOADS
+        w = WORKLOADS[WORKLOAD]
+        tensor_bytes = w["B"] * w["H"] * w["N"] * w["d"] * 2
+        os.makedirs(args.out, exist_ok=True)
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace,
+                            PROFILE_COMMANDS["trace"] + "\npython3 bench.py --summarize-trace /tmp/la_prof/trace",
+                            os.path.join(args.out, f"kernels_{WORKLOAD}.md"))
+        if args.summarize_pmc:
+            cmds = [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"],
+                    "python3 bench.py --summarize-pmc /tmp/la_prof/fetch /tmp/la_prof/write"]
+            summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], cmds,
+                          os.path.join(args.out, f"traffic_{WORKLOAD}.json"),
+                          os.path.join(args.out, f"traffic_{WORKLOAD}.md"), kernel_source_hash(), tensor_bytes)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the path shards by head or by sequence, see the design notes", file=sys.stderr)
+              "across GPUs the bidirectional path would shard by (batch, head), with no "
+              "communication", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -159,27 +319,30 @@ def main():
     # algorithmic bytes per launch: K + V read (state), Q read + O write (apply)
     kv_bytes = 2 * tensor_bytes
     qo_bytes = 2 * tensor_bytes
-    dominant = ("la_state_bf16_kernel", st_avg, kv_bytes) if st_avg >= ap_avg else \
-        ("la_apply_bf16_kernel", ap_avg, qo_bytes)
-    name, dur_ms, nbytes = dominant
+    # The state pass is two launches on one stream (the partial-state kernel
+    # and the fixed-order combine of its partials), timed together.
+    dominant = (STATE_KERNELS, st_avg, kv_bytes) if st_avg >= ap_avg else (APPLY_KERNELS, ap_avg, qo_bytes)
+    kernels, dur_ms, nbytes = dominant
     achieved = nbytes / (dur_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     tokens_per_s = B * N / (ms_step * 1e-3)
+    traffic = load_traffic(kernels, src_hash)
 
-    # a plain device copy of the same size, as the practical HBM ceiling
-    src = torch.empty(2 * tensor_bytes // 2, dtype=torch.bfloat16, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
+    # Calibration copy o_i = q_i * 1 over the same rotating sets: a plain
+    # elementwise copy of known size (reads and writes tensor_bytes), timed as
+    # the practical HBM ceiling for a read+write stream and used to scale the
+    # HBM byte counters.
+    for i in range(3):
+        torch.mul(sets[i % n_sets][0], 1, out=sets[i % n_sets][3])
     torch.cuda.synchronize()
     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_copy = 4 * n_sets
     c0.record()
-    for _ in range(20):
-        dst.copy_(src)
+    for i in range(n_copy):
+        torch.mul(sets[i % n_sets][0], 1, out=sets[i % n_sets][3])
     c1.record()
     torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 2 / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
-    del src, dst
+    copy_gbps = 2 * tensor_bytes / (c0.elapsed_time(c1) / n_copy * 1e-3) / 1e9
 
     out = {
         "metric": METRIC,
@@ -198,17 +361,21 @@ def main():
                    "eps": eps, "input_sets": n_sets},
         "roofline": {
             "bound": "hbm",
-            "kernel": name,
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": load_traffic(name, src_hash),
+            "traffic": traffic,
+            "kernel": "+".join(kernels),
+            "algorithmic_bytes": nbytes,
+            "duration_us": dur_ms * 1e3,
+            "traffic_over_algorithmic": traffic / nbytes if traffic else None,
         },
         "step_GBps": 4 * tensor_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": 4 * tensor_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernels_us": {"state": st_avg * 1e3, "apply": ap_avg * 1e3},
         "copy_GBps": copy_gbps,
+        "copy_kind": "torch mul by 1 (read + write, rotating sets)",
         "wall_s": wall,
         "src_hash": src_hash,
     }

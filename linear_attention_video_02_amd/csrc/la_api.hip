@@ -23,8 +23,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int env_int(const char* name, int dflt) {
     const char* s = getenv(name);
     if (!s || !*s) return dflt;
-    int v = atoi(s);
-    return v > 0 ? v : dflt;
+    const int v = atoi(s);
+    return v > 0 ? v : dflt;  // only positive overrides (workgroup counts)
 }
 
 struct WsLayout {
