@@ -111,6 +111,56 @@ def cpu_baseline(q, k, v, spec, budget_s=12.0):
     }
 
 
+class FenceFreeEvents:
+    """Timing events without the system-scope fence (hipEventDisableSystemFence).
+
+    A default HIP event makes its recording a system-scope release and acquire:
+    L2 write-back and invalidation between the kernels it separates, which
+    both adds a gap and slows the next kernel.  Events used only for timing do
+    not need it.  Created through the HIP runtime PyTorch already loaded.
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        import torch
+        torch.cuda.init()
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime already in the process
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.events = []
+
+    def new(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev):
+        rc = self.hip.hipEventRecord(ev, self.stream())
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
+
+
 def _find(path, suffix):
     import glob
     hits = sorted(glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True))
@@ -234,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record per-kernel events on every n-th timed step (each event costs ~2 us)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write the kernel-duration summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -285,36 +337,44 @@ def main():
         sets.append((qi, ki, vi, torch.empty_like(q), S, z))
     ws = la.workspace(B, H, N, d, dev)
 
+    tev = FenceFreeEvents()
+
     def step(i, ev=None):
         qi, ki, vi, oi, S, z = sets[i % n_sets]
         if ev is not None:
-            ev[0].record()
+            tev.record(ev[0])
         la.state_reduce(ki, vi, grid, S=S, z=z, ws=ws)
         if ev is not None:
-            ev[1].record()
+            tev.record(ev[1])
         la.apply(qi, S, z, grid, eps, out=oi)
         if ev is not None:
-            ev[2].record()
+            tev.record(ev[2])
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    every = max(1, args.event_every)
+    evs = {i: [tev.new() for _ in range(3)] for i in range(0, args.steps, every)}
+    start, stop = tev.new(), tev.new()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
+    tev.record(start)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    stop.record()
+        step(args.warmup + i, evs.get(i))
+    tev.record(stop)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(stop) / args.steps
-    state_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    apply_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = tev.ms(start, stop) / args.steps
+    state_ms = [tev.ms(e[0], e[1]) for e in evs.values()]
+    apply_ms = [tev.ms(e[1], e[2]) for e in evs.values()]
+    # time per step between consecutive sampled steps
+    keys = sorted(evs)
+    step_ms = sorted([tev.ms(evs[a][0], evs[b][0]) / (b - a) for a, b in zip(keys, keys[1:])]) or [ms_step]
     st_avg = sum(state_ms) / len(state_ms)
     ap_avg = sum(apply_ms) / len(apply_ms)
+
+    def pct(xs, f):
+        return xs[min(len(xs) - 1, int(f * len(xs)))]
 
     # algorithmic bytes per launch: K + V read (state), Q read + O write (apply)
     kv_bytes = 2 * tensor_bytes
@@ -335,14 +395,15 @@ def main():
     for i in range(3):
         torch.mul(sets[i % n_sets][0], 1, out=sets[i % n_sets][3])
     torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0, c1 = tev.new(), tev.new()
     n_copy = 4 * n_sets
-    c0.record()
+    tev.record(c0)
     for i in range(n_copy):
         torch.mul(sets[i % n_sets][0], 1, out=sets[i % n_sets][3])
-    c1.record()
+    tev.record(c1)
     torch.cuda.synchronize()
-    copy_gbps = 2 * tensor_bytes / (c0.elapsed_time(c1) / n_copy * 1e-3) / 1e9
+    copy_gbps = 2 * tensor_bytes / (tev.ms(c0, c1) / n_copy * 1e-3) / 1e9
+    tev.close()
 
     out = {
         "metric": METRIC,
@@ -374,6 +435,9 @@ def main():
         "step_GBps": 4 * tensor_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": 4 * tensor_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernels_us": {"state": st_avg * 1e3, "apply": ap_avg * 1e3},
+        "step_us_p10_p50_p90": [pct(step_ms, 0.1) * 1e3, pct(step_ms, 0.5) * 1e3, pct(step_ms, 0.9) * 1e3],
+        "timing": f"HIP events without system-scope fence on the launch stream; per-kernel events "
+                  f"on every {every}th timed step ({len(evs)} samples)",
         "copy_GBps": copy_gbps,
         "copy_kind": "torch mul by 1 (read + write, rotating sets)",
         "wall_s": wall,
