@@ -284,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s"],
+                    help="default: the headline 720p-5s bidirectional step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel events on every n-th timed step (each event costs ~2 us)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -317,97 +319,67 @@ def main():
     import torch
 
     import linear_attention_video_02_amd as la
-    from linear_attention_video_02_amd.inputs import WORKLOADS, make_qkv_device
 
     if not os.path.exists(la.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
-    spec = WORKLOADS[WORKLOAD]
-    B, H, N, d, grid, eps = spec["B"], spec["H"], spec["N"], spec["d"], spec["grid"], spec["eps"]
     dev = torch.device("cuda:0")
-    q, k, v = make_qkv_device(B, H, N, d, "bf16", spec["seed"], dev)
-    tensor_bytes = q.numel() * q.element_size()
-    set_bytes = 4 * tensor_bytes
-    n_sets = max(2, math.ceil(2 * 2**30 / set_bytes))
-    sets = []
-    for i in range(n_sets):
-        qi, ki, vi = (q, k, v) if i == 0 else (q.clone(), k.clone(), v.clone())
-        S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
-        z = torch.empty((B, H, d), dtype=torch.float32, device=dev)
-        sets.append((qi, ki, vi, torch.empty_like(q), S, z))
-    ws = la.workspace(B, H, N, d, dev)
-
+    wl = setup_workload(args.workload, la, dev)
     tev = FenceFreeEvents()
-
-    def step(i, ev=None):
-        qi, ki, vi, oi, S, z = sets[i % n_sets]
-        if ev is not None:
-            tev.record(ev[0])
-        la.state_reduce(ki, vi, grid, S=S, z=z, ws=ws)
-        if ev is not None:
-            tev.record(ev[1])
-        la.apply(qi, S, z, grid, eps, out=oi)
-        if ev is not None:
-            tev.record(ev[2])
+    step = wl["step"]
 
     for i in range(args.warmup):
-        step(i)
+        step(i, None, tev)
     torch.cuda.synchronize()
     every = max(1, args.event_every)
-    evs = {i: [tev.new() for _ in range(3)] for i in range(0, args.steps, every)}
+    ngroups = len(wl["groups"])
+    evs = {i: [tev.new() for _ in range(ngroups + 1)] for i in range(0, args.steps, every)}
     start, stop = tev.new(), tev.new()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     tev.record(start)
     for i in range(args.steps):
-        step(args.warmup + i, evs.get(i))
+        step(args.warmup + i, evs.get(i), tev)
     tev.record(stop)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = tev.ms(start, stop) / args.steps
-    state_ms = [tev.ms(e[0], e[1]) for e in evs.values()]
-    apply_ms = [tev.ms(e[1], e[2]) for e in evs.values()]
-    # time per step between consecutive sampled steps
+    group_ms = [sum(tev.ms(e[g], e[g + 1]) for e in evs.values()) / len(evs) for g in range(ngroups)]
     keys = sorted(evs)
     step_ms = sorted([tev.ms(evs[a][0], evs[b][0]) / (b - a) for a, b in zip(keys, keys[1:])]) or [ms_step]
-    st_avg = sum(state_ms) / len(state_ms)
-    ap_avg = sum(apply_ms) / len(apply_ms)
 
     def pct(xs, f):
         return xs[min(len(xs) - 1, int(f * len(xs)))]
 
-    # algorithmic bytes per launch: K + V read (state), Q read + O write (apply)
-    kv_bytes = 2 * tensor_bytes
-    qo_bytes = 2 * tensor_bytes
-    # The state pass is two launches on one stream (the partial-state kernel
-    # and the fixed-order combine of its partials), timed together.
-    dominant = (STATE_KERNELS, st_avg, kv_bytes) if st_avg >= ap_avg else (APPLY_KERNELS, ap_avg, qo_bytes)
-    kernels, dur_ms, nbytes = dominant
+    # dominant launch group: algorithmic bytes per launch / its mean event duration
+    g = max(range(ngroups), key=lambda i: group_ms[i])
+    gname, kernels, nbytes = wl["groups"][g]
+    dur_ms = group_ms[g]
     achieved = nbytes / (dur_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    tokens_per_s = B * N / (ms_step * 1e-3)
-    traffic = load_traffic(kernels, src_hash)
+    traffic = load_traffic(kernels, src_hash) if args.workload == WORKLOAD else None
 
-    # Calibration copy o_i = q_i * 1 over the same rotating sets: a plain
-    # elementwise copy of known size (reads and writes tensor_bytes), timed as
-    # the practical HBM ceiling for a read+write stream and used to scale the
-    # HBM byte counters.
+    # Calibration copy o = q * 1 over rotating buffers: a plain elementwise
+    # copy of known size (reads and writes copy_bytes), timed as the practical
+    # HBM ceiling for a read+write stream and used to scale the byte counters.
+    pairs = wl["copy_pairs"]
+    copy_bytes = pairs[0][0].numel() * pairs[0][0].element_size()
     for i in range(3):
-        torch.mul(sets[i % n_sets][0], 1, out=sets[i % n_sets][3])
+        torch.mul(pairs[i % len(pairs)][0], 1, out=pairs[i % len(pairs)][1])
     torch.cuda.synchronize()
     c0, c1 = tev.new(), tev.new()
-    n_copy = 4 * n_sets
+    n_copy = 4 * len(pairs)
     tev.record(c0)
     for i in range(n_copy):
-        torch.mul(sets[i % n_sets][0], 1, out=sets[i % n_sets][3])
+        torch.mul(pairs[i % len(pairs)][0], 1, out=pairs[i % len(pairs)][1])
     tev.record(c1)
     torch.cuda.synchronize()
-    copy_gbps = 2 * tensor_bytes / (tev.ms(c0, c1) / n_copy * 1e-3) / 1e9
+    copy_gbps = 2 * copy_bytes / (tev.ms(c0, c1) / n_copy * 1e-3) / 1e9
     tev.close()
 
     out = {
-        "metric": METRIC,
-        "value": tokens_per_s,
+        "metric": wl["metric"],
+        "value": wl["tokens_per_step"] / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -418,8 +390,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "B": B, "H": H, "N": N, "d": d, "grid": list(grid),
-                   "eps": eps, "input_sets": n_sets},
+        "config": wl["config"],
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
@@ -432,20 +403,143 @@ def main():
             "duration_us": dur_ms * 1e3,
             "traffic_over_algorithmic": traffic / nbytes if traffic else None,
         },
-        "step_GBps": 4 * tensor_bytes / (ms_step * 1e-3) / 1e9,
-        "step_frac_of_peak": 4 * tensor_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "kernels_us": {"state": st_avg * 1e3, "apply": ap_avg * 1e3},
+        "step_GBps": wl["step_bytes"] / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": wl["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "kernels_us": {wl["groups"][i][0]: group_ms[i] * 1e3 for i in range(ngroups)},
         "step_us_p10_p50_p90": [pct(step_ms, 0.1) * 1e3, pct(step_ms, 0.5) * 1e3, pct(step_ms, 0.9) * 1e3],
-        "timing": f"HIP events without system-scope fence on the launch stream; per-kernel events "
+        "timing": f"HIP events without system-scope fence on the launch stream; per-group events "
                   f"on every {every}th timed step ({len(evs)} samples)",
         "copy_GBps": copy_gbps,
-        "copy_kind": "torch mul by 1 (read + write, rotating sets)",
+        "copy_kind": "torch mul by 1 (read + write, rotating buffers)",
         "wall_s": wall,
         "src_hash": src_hash,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(q, k, v, spec, args.cpu_budget)
+    if not args.no_cpu_baseline and "cpu_baseline" in wl:
+        out["cpu_baseline"] = wl["cpu_baseline"](args.cpu_budget)
     print(json.dumps(out), flush=True)
+
+
+def setup_workload(name, la, dev):
+    """Device inputs, the step function and the launch groups of one workload.
+
+    Every workload rotates through enough independent input sets (>= 2 GiB in
+    all) that no step finds its operands in the Infinity Cache or in L2.
+    """
+    import torch
+
+    from linear_attention_video_02_amd.inputs import CROSS, WORKLOADS, make_cross_device, make_qkv_device
+
+    def rotating(tensors_of_set0, clone_count):
+        sets = [tensors_of_set0]
+        for _ in range(clone_count - 1):
+            sets.append(tuple(t.clone() for t in tensors_of_set0))
+        return sets
+
+    def n_sets_for(set_bytes):
+        return max(2, math.ceil(2 * 2**30 / set_bytes))
+
+    if name == "720p5s":
+        spec = WORKLOADS[name]
+        B, H, N, d, grid, eps = spec["B"], spec["H"], spec["N"], spec["d"], spec["grid"], spec["eps"]
+        q, k, v = make_qkv_device(B, H, N, d, "bf16", spec["seed"], dev)
+        tb = q.numel() * q.element_size()
+        base = rotating((q, k, v), n_sets_for(4 * tb))
+        sets = [(qi, ki, vi, torch.empty_like(q), torch.empty((B, H, d, d), dtype=torch.float32, device=dev),
+                 torch.empty((B, H, d), dtype=torch.float32, device=dev)) for (qi, ki, vi) in base]
+        ws = la.workspace(B, H, N, d, dev)
+
+        def step(i, ev, tev):
+            qi, ki, vi, oi, S, z = sets[i % len(sets)]
+            if ev is not None:
+                tev.record(ev[0])
+            la.state_reduce(ki, vi, grid, S=S, z=z, ws=ws)
+            if ev is not None:
+                tev.record(ev[1])
+            la.apply(qi, S, z, grid, eps, out=oi)
+            if ev is not None:
+                tev.record(ev[2])
+
+        return {
+            "metric": METRIC, "step": step, "tokens_per_step": B * N, "step_bytes": 4 * tb,
+            "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "eps": eps,
+                       "input_sets": len(sets)},
+            # the state pass is two launches (partial states, fixed-order combine) timed together
+            "groups": [("state", STATE_KERNELS, 2 * tb), ("apply", APPLY_KERNELS, 2 * tb)],
+            "copy_pairs": [(s[0], s[3]) for s in sets],
+            "cpu_baseline": lambda budget: cpu_baseline(q, k, v, spec, budget),
+        }
+
+    if name == "cross720p":
+        w = CROSS[name]
+        B, H, Nq, Nkv, d, eps = w["B"], w["H"], w["Nq"], w["Nkv"], w["d"], w["eps"]
+        q, k, v = make_cross_device(B, H, Nq, Nkv, d, "bf16", w["seed"], dev)
+        tq = q.numel() * q.element_size()
+        tkv = k.numel() * k.element_size()
+        base = rotating((q, k, v), n_sets_for(2 * tq + 2 * tkv))
+        sets = [(qi, ki, vi, torch.empty_like(q), torch.empty((B, H, d, d), dtype=torch.float32, device=dev),
+                 torch.empty((B, H, d), dtype=torch.float32, device=dev)) for (qi, ki, vi) in base]
+        ws = la.workspace(B, H, Nq, d, dev)
+
+        def step(i, ev, tev):
+            qi, ki, vi, oi, S, z = sets[i % len(sets)]
+            if ev is not None:
+                tev.record(ev[0])
+            la.state_reduce(ki, vi, None, S=S, z=z, ws=ws)
+            if ev is not None:
+                tev.record(ev[1])
+            la.apply(qi, S, z, None, eps, out=oi)
+            if ev is not None:
+                tev.record(ev[2])
+
+        return {
+            "metric": "linear cross-attn video tokens/sec and achieved HBM GB/s (% peak), 720p-5s video "
+                      "queries over 300 text tokens, 1 GPU",
+            "step": step, "tokens_per_step": B * Nq, "step_bytes": 2 * tq + 2 * tkv,
+            "config": {"workload": name, "B": B, "H": H, "N_q": Nq, "N_kv": Nkv, "d": d, "eps": eps,
+                       "input_sets": len(sets)},
+            "groups": [("state", STATE_KERNELS, 2 * tkv), ("apply", APPLY_KERNELS, 2 * tq)],
+            "copy_pairs": [(s[0], s[3]) for s in sets],
+        }
+
+    if name == "720p60s":
+        spec = WORKLOADS[name]
+        B, H, N, d, grid, eps, L = (spec["B"], spec["H"], spec["N"], spec["d"], spec["grid"], spec["eps"],
+                                    spec["block"])
+        q, k, v = make_qkv_device(B, H, N, d, "bf16", spec["seed"], dev)
+        blocks = [tuple(la.split_blocks(t, L)) for t in (q, k, v)]
+        del q, k, v
+        outs = [torch.empty_like(x) for x in blocks[0]]
+        S = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+        z = torch.zeros((B, H, d), dtype=torch.float32, device=dev)
+        ws = la.workspace(B, H, N, d, dev)
+        nb = len(blocks[0])
+        blk_bytes = 4 * blocks[0][0].numel() * blocks[0][0].element_size()
+        step_bytes = 4 * sum(x.numel() * x.element_size() for x in blocks[0])
+
+        def step(i, ev, tev):
+            # one step = the whole 60 s sequence, block after block from an empty cache
+            S.zero_()
+            z.zero_()
+            if ev is not None:
+                tev.record(ev[0])
+            for b in range(nb):
+                la.block_causal_step(blocks[0][b], blocks[1][b], blocks[2][b], S, z, N, grid, L, b, True,
+                                     eps, out=outs[b], ws=ws)
+            if ev is not None:
+                tev.record(ev[1])
+
+        return {
+            "metric": "block-causal linear-attn tokens/sec and achieved HBM GB/s (% peak), 720p-60s, "
+                      "10 blocks, 1 GPU",
+            "step": step, "tokens_per_step": B * N, "step_bytes": step_bytes,
+            "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "block": L,
+                       "eps": eps, "input_sets": 1},
+            # one group = all block steps (state, combine and apply launches of 10 blocks)
+            "groups": [("block_steps", STATE_KERNELS + APPLY_KERNELS, step_bytes)],
+            "copy_pairs": [(blocks[0][b], outs[b]) for b in range(nb)],
+            "block_bytes": blk_bytes,
+        }
+    raise SystemExit(f"unknown workload {name}")
 
 
 if __name__ == "__main__":

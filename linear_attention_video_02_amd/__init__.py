@@ -183,6 +183,19 @@ def bidirectional(q, k, v, grid=None, eps=1e-6, out=None, ws=None):
     return apply(q, S, z, grid, eps, out)
 
 
+def cross_attention(q, k, v, eps=1e-6, out=None, ws=None):
+    """Linear cross-attention: q [B, H, N_q, d] over k, v [B, H, N_kv, d], no RoPE.
+
+    The same two library calls as self-attention (la_state_reduce over the
+    N_kv keys/values, la_apply over the N_q queries); N_kv = 0 gives zeros.
+    """
+    _check_qkv(q, k, v)
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("k and v must be [B, H, N_kv, d] with q's B, H and d")
+    S, z = state_reduce(k, v, None, ws=ws)
+    return apply(q, S, z, None, eps, out)
+
+
 def block_causal_step(q, k, v, S_carry, z_carry, N, grid, block_tokens, block_idx,
                       commit=True, eps=1e-6, out=None, ws=None):
     """One block of block-causal mode; q/k/v/out hold only this block."""

@@ -12,6 +12,8 @@ Workloads (latent token grids of the pages' video shapes; DCAE-V compresses
   720p5s  B2 H32 N19320  d64  bf16, grid 21x23x40
   720p60s B1 H32 N220800 d64  bf16, grid 240x23x40, 10 blocks of 22080 tokens
   sweep   B1 H32 d in {32,64,128}, N in {4096,16384,65536,220800}, grid ceil(N/920)x23x40
+  cross720p  B2 H32, 19320 video queries over 300 text keys/values, d64 bf16, no RoPE
+             (the pages give no text length; 300 is a parameter)
 """
 from __future__ import annotations
 
@@ -107,6 +109,23 @@ def make_qkv_device(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: i
         a = torch.randn((B, H, N, d), generator=gen, dtype=torch.float32, device=device)
         out.append(a.to(torch.bfloat16) if dtype == "bf16" else a)
         del a
+    return tuple(out)
+
+
+CROSS = {"cross720p": dict(name="cross720p", B=2, H=32, Nq=19320, Nkv=300, d=64, dtype="bf16",
+                           seed=1006, eps=1e-6)}
+
+
+def make_cross_device(B: int, H: int, Nq: int, Nkv: int, d: int, dtype: str = "bf16", seed: int = 0,
+                      device="cuda:0"):
+    """Q [B, H, Nq, d] and K, V [B, H, Nkv, d] ~ N(0, 1) drawn on a GPU (order Q, K, V)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = []
+    for n in (Nq, Nkv, Nkv):
+        a = torch.randn((B, H, n, d), generator=gen, dtype=torch.float32, device=device)
+        out.append(a.to(torch.bfloat16) if dtype == "bf16" else a)
     return tuple(out)
 
 

@@ -190,6 +190,23 @@ def weights_form_head(Q, K, V, grid, eps, block_tokens: int | None = None):
     return out
 
 
+def cross_attention_head(Q, K, V, eps):
+    """Linear cross-attention of one slice: N_q queries over N_kv keys/values.
+
+    The analysis page ("How SANA-Video Positions Itself", the architectural
+    lens; and the Linear DiT block of section 3.4) replaces cross-attention by
+    the same ReLU linear attention as self-attention.  Text tokens carry no
+    (t, h, w) grid position, so no RoPE; N_kv is a free parameter (the page
+    gives no text length).  N_kv = 0 gives S = 0, z = 0 and all-zero output.
+    """
+    d = np.shape(Q)[-1]
+    if np.shape(K)[0] == 0:
+        S, z = np.zeros((d, d)), np.zeros(d)
+    else:
+        S, z = state(K, V, None)
+    return apply(Q, S, z, None, eps)
+
+
 # ---------------------------------------------------------------------------
 # whole [B, H, N, d] tensors
 # ---------------------------------------------------------------------------
@@ -226,6 +243,16 @@ def block_causal(Q, K, V, grid, block_tokens, eps=1e-6):
             out[b, h], S[b, h], z[b, h] = block_causal_head(
                 Q[b, h], K[b, h], V[b, h], grid, block_tokens, eps)
     return out, S, z
+
+
+def cross_attention(Q, K, V, eps=1e-6):
+    """O[B,H,N_q,d] of linear cross-attention with K, V of shape [B,H,N_kv,d]."""
+    B, H, Nq, d = np.shape(Q)
+    out = np.empty((B, H, Nq, d))
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = cross_attention_head(Q[b, h], K[b, h], V[b, h], eps)
+    return out
 
 
 def rel_row_error(got: np.ndarray, ref: np.ndarray) -> float:

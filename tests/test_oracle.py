@@ -121,6 +121,25 @@ def brute_force_loops(Q, K, V, grid, eps, block=None, token_causal=False):
     return out
 
 
+def brute_force_cross_loops(Q, K, V, eps):
+    """Cross-attention O_i = sum_j (q.k_j) V_j / (sum_j q.k_j + eps), explicit loops, N_q != N_kv."""
+    Nq, d = Q.shape
+    out = np.zeros((Nq, d))
+    for i in range(Nq):
+        q = [max(float(a), 0.0) for a in Q[i]]
+        num = [0.0] * d
+        den = 0.0
+        for j in range(K.shape[0]):
+            k = [max(float(a), 0.0) for a in K[j]]
+            w = sum(q[c] * k[c] for c in range(d))
+            for c in range(d):
+                num[c] += w * float(V[j][c])
+            den += w
+        if any(a > 0.0 for a in q):
+            out[i] = [a / (den + eps) for a in num]
+    return out
+
+
 def rand(shape, seed):
     return np.random.default_rng(seed).standard_normal(shape)
 
@@ -154,6 +173,18 @@ def check_brute_force_block_causal():
         ref = brute_force_loops(Q, K, V, grid, 1e-6, block=L)
         got, _, _ = oracle.block_causal_head(Q, K, V, grid, L, 1e-6)
         np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12, err_msg=f"N={N} L={L}")
+
+
+def check_brute_force_cross():
+    for Nq, Nkv, d, seed in [(13, 5, 8, 21), (7, 19, 16, 22), (9, 1, 8, 23), (4, 0, 8, 24)]:
+        rng = np.random.default_rng(seed)
+        Q = rng.standard_normal((Nq, d))
+        K = rng.standard_normal((Nkv, d))
+        V = rng.standard_normal((Nkv, d))
+        for eps in (1e-6, 1e-3):  # eps > 0: a live query with no overlapping key has den = eps
+            ref = brute_force_cross_loops(Q, K, V, eps)
+            got = oracle.cross_attention_head(Q, K, V, eps)
+            np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12, err_msg=f"Nq={Nq} Nkv={Nkv}")
 
 
 def check_axis_split():
@@ -199,6 +230,28 @@ def test_brute_force_bidirectional():
 
 def test_brute_force_block_causal():
     check_brute_force_block_causal()
+
+
+def test_brute_force_cross():
+    check_brute_force_cross()
+
+
+def test_cross_attention_closed_forms():
+    """One key/value token: O_i = V_0 a/(a + eps), a = relu(q_i).relu(k_0); none: zeros."""
+    rng = np.random.default_rng(30)
+    Q = rng.standard_normal((50, 16))
+    K = np.abs(rng.standard_normal((1, 16)))
+    V = rng.standard_normal((1, 16))
+    got = oracle.cross_attention_head(Q, K, V, 1e-3)
+    a = np.maximum(Q, 0) @ K[0]
+    want = np.where((np.maximum(Q, 0) > 0).any(axis=1)[:, None], a[:, None] * V[0] / (a[:, None] + 1e-3), 0.0)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
+    assert not np.any(oracle.cross_attention_head(Q, K[:0], V[:0], 1e-6))
+    # text-token order does not matter
+    K2, V2 = rng.standard_normal((2, 40, 16))
+    perm = rng.permutation(40)
+    np.testing.assert_allclose(oracle.cross_attention_head(Q, K2, V2, 1e-6),
+                               oracle.cross_attention_head(Q, K2[perm], V2[perm], 1e-6), rtol=1e-12)
 
 
 def test_axis_split():
@@ -431,7 +484,7 @@ MUTANTS = [
     ("rope_angles", _mut_freq),
 ]
 PIN_CHECKS = [check_worked_examples, check_axis_split, check_rotation_axes_and_frequencies,
-              check_brute_force_bidirectional, check_brute_force_block_causal]
+              check_brute_force_bidirectional, check_brute_force_block_causal, check_brute_force_cross]
 
 
 @pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])

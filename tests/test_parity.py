@@ -167,3 +167,49 @@ def test_state_reduce_empty_sequence(la):
     S, z = la.state_reduce(k, k.clone(), None)
     torch.cuda.synchronize()
     assert torch.count_nonzero(S).item() == 0 and torch.count_nonzero(z).item() == 0
+
+
+CROSS_CASES = [
+    # B, H, N_q, N_kv, d, dtype, eps  (video queries over text keys/values, no RoPE)
+    (1, 2, 777, 1, 32, "fp32", 1e-6),
+    (1, 4, 100, 5000, 128, "bf16", 1e-6),
+    (2, 3, 1000, 77, 64, "bf16", 0.0),
+    (1, 1, 1, 7, 64, "fp32", 1e-6),
+    (1, 2, 64, 0, 64, "bf16", 1e-6),
+]
+
+
+@pytest.mark.parametrize("case", CROSS_CASES, ids=[f"B{c[0]}H{c[1]}Nq{c[2]}Nkv{c[3]}d{c[4]}{c[5]}"
+                                                    for c in CROSS_CASES])
+def test_cross_attention(la, case):
+    import torch
+    B, H, Nq, Nkv, d, dt, eps = case
+    say(f"[cross] {case}")
+    rng = np.random.default_rng(4000 + Nq + Nkv + d)
+    q = rng.standard_normal((B, H, Nq, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    if dt == "bf16":
+        from linear_attention_video_02_amd.inputs import round_to_bf16
+        q, k, v = (round_to_bf16(a) for a in (q, k, v))
+    out = la.cross_attention(upload(q, dt), upload(k, dt), upload(v, dt), eps)
+    torch.cuda.synchronize()
+    ref = oracle.cross_attention(q, k, v, eps)
+    if Nkv == 0:
+        assert torch.count_nonzero(out).item() == 0
+    else:
+        assert_close(host(out), ref, dt, f"cross {case}")
+
+
+def test_cross720p(la):
+    """The cross-attention workload at full size: 19320 video tokens over 300 text tokens."""
+    import torch
+    from linear_attention_video_02_amd.inputs import CROSS, make_cross_device
+    w = CROSS["cross720p"]
+    say(f"[cross720p] {w}")
+    tq, tk, tv = make_cross_device(w["B"], w["H"], w["Nq"], w["Nkv"], w["d"], w["dtype"], w["seed"])
+    out = la.cross_attention(tq, tk, tv, w["eps"])
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 0), (1, 31), (0, 17)):
+        ref = oracle.cross_attention_head(host(tq[b, h]), host(tk[b, h]), host(tv[b, h]), w["eps"])
+        assert_close(host(out[b, h]), ref, "bf16", f"cross720p head ({b},{h})")
