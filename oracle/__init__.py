@@ -8,5 +8,5 @@ from .linattn_oracle import (  # noqa: F401
     ROPE_BASE, phi, rope_axis_pairs, grid_positions, rope_angles, rope,
     state, apply, bidirectional_head, block_causal_head, weights_form_head,
     bidirectional, states, block_causal, rel_row_error,
-    cross_attention_head, cross_attention,
+    cross_attention_head, cross_attention, token_causal_head, token_causal,
 )

@@ -164,6 +164,39 @@ def block_causal_head(Q, K, V, grid, block_tokens: int, eps, carry=None):
     return out, S, z
 
 
+def token_causal_head(Q, K, V, grid, eps, n0: int = 0, carry=None):
+    """Token-causal linear attention of one slice, Eq. 3 taken literally.
+
+    Section 3.3.1 of the analysis page ("Derivation from causal linear
+    attention"): token i sees tokens j <= i.  Before token i the two
+    accumulators hold sum_{j<i} RoPE(phi K_j)^T V_j and sum_{j<i} phi(K_j);
+    token i first adds its own state S_i and key, then reads them:
+    O_i = RoPE(phi Q_i) S_acc / (phi(Q_i) z_acc + eps).  RoPE uses the global
+    index n0 + i (the page omits it only for clarity).  `carry` = the
+    accumulators before token 0 ("None" = zeros).  Returns (O, S, z) with the
+    accumulators after the last token.
+    """
+    N, d = np.shape(Q)
+    if carry is None:
+        S = np.zeros((d, d))
+        z = np.zeros(d)
+    else:
+        S, z = (np.array(c, dtype=np.float64) for c in carry)
+    q = phi(Q)
+    k = phi(K)
+    V = np.asarray(V, dtype=np.float64)
+    n = np.arange(n0, n0 + N)
+    qr = rope(q, n, grid)
+    kr = rope(k, n, grid)
+    out = np.zeros((N, d))
+    for i in range(N):
+        S = S + np.outer(kr[i], V[i])
+        z = z + k[i]
+        if np.any(q[i] > 0.0):
+            out[i] = (qr[i] @ S) / (q[i] @ z + eps)
+    return out, S, z
+
+
 def weights_form_head(Q, K, V, grid, eps, block_tokens: int | None = None):
     """O(N^2) form: explicit attention weights, no reassociation.
 
@@ -253,6 +286,18 @@ def cross_attention(Q, K, V, eps=1e-6):
         for h in range(H):
             out[b, h] = cross_attention_head(Q[b, h], K[b, h], V[b, h], eps)
     return out
+
+
+def token_causal(Q, K, V, grid=None, eps=1e-6):
+    """O[B,H,N,d] of token-causal linear attention plus the final accumulators."""
+    B, H, N, d = np.shape(Q)
+    out = np.empty((B, H, N, d))
+    S = np.empty((B, H, d, d))
+    z = np.empty((B, H, d))
+    for b in range(B):
+        for h in range(H):
+            out[b, h], S[b, h], z[b, h] = token_causal_head(Q[b, h], K[b, h], V[b, h], grid, eps)
+    return out, S, z
 
 
 def rel_row_error(got: np.ndarray, ref: np.ndarray) -> float:

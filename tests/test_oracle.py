@@ -187,6 +187,14 @@ def check_brute_force_cross():
             np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12, err_msg=f"Nq={Nq} Nkv={Nkv}")
 
 
+def check_brute_force_token_causal():
+    for N, d, grid, seed in [(20, 8, (2, 2, 5), 41), (17, 12, (3, 2, 3), 42), (9, 6, None, 43)]:
+        Q, K, V = rand((3, N, d), seed)
+        ref = brute_force_loops(Q, K, V, grid, 1e-6, token_causal=True)
+        got, _, _ = oracle.token_causal_head(Q, K, V, grid, 1e-6)
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12, err_msg=f"N={N} d={d}")
+
+
 def check_axis_split():
     for d, split in load_axis_split().items():
         assert oracle.rope_axis_pairs(d) == split, d
@@ -252,6 +260,30 @@ def test_cross_attention_closed_forms():
     perm = rng.permutation(40)
     np.testing.assert_allclose(oracle.cross_attention_head(Q, K2, V2, 1e-6),
                                oracle.cross_attention_head(Q, K2[perm], V2[perm], 1e-6), rtol=1e-12)
+
+
+def test_brute_force_token_causal():
+    check_brute_force_token_causal()
+
+
+def test_token_causal_identities():
+    """Block size 1 is token-causal; the last row sees everything; carry + offset resume."""
+    Q, K, V = rand((3, 40, 8), 44)
+    grid = (4, 2, 5)
+    o_tc, S_tc, z_tc = oracle.token_causal_head(Q, K, V, grid, 1e-6)
+    o_bc, S_bc, z_bc = oracle.block_causal_head(Q, K, V, grid, 1, 1e-6)
+    np.testing.assert_allclose(o_tc, o_bc, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S_tc, S_bc, rtol=1e-12, atol=1e-13)
+    bi = oracle.bidirectional_head(Q, K, V, grid, 1e-6)
+    np.testing.assert_allclose(o_tc[-1], bi[-1], rtol=1e-12, atol=1e-14)
+    S_all, z_all = oracle.state(K, V, grid)
+    np.testing.assert_allclose(S_tc, S_all, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z_tc, z_all, rtol=1e-12)
+    m = 23
+    o1, S1, z1 = oracle.token_causal_head(Q[:m], K[:m], V[:m], grid, 1e-6)
+    o2, S2, z2 = oracle.token_causal_head(Q[m:], K[m:], V[m:], grid, 1e-6, n0=m, carry=(S1, z1))
+    np.testing.assert_allclose(np.concatenate([o1, o2]), o_tc, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S2, S_tc, rtol=1e-12, atol=1e-13)
 
 
 def test_axis_split():
@@ -464,6 +496,21 @@ def _mut_block_exclusive(Q, K, V, grid, block_tokens, eps, carry=None):
     return out, S, z
 
 
+def _mut_token_exclusive(Q, K, V, grid, eps, n0=0, carry=None):
+    N, d = np.shape(Q)
+    S, z = np.zeros((d, d)), np.zeros(d)
+    q, k = orc.phi(Q), orc.phi(K)
+    n = np.arange(n0, n0 + N)
+    qr, kr = orc.rope(q, n, grid), orc.rope(k, n, grid)
+    out = np.zeros((N, d))
+    for i in range(N):
+        if np.any(q[i] > 0.0):
+            out[i] = (qr[i] @ S) / (q[i] @ z + eps)
+        S = S + np.outer(kr[i], np.asarray(V[i], dtype=np.float64))
+        z = z + k[i]
+    return out, S, z
+
+
 def _mut_freq(n, grid, d):
     ang = _ORIG["rope_angles"](n, grid, d)
     return ang * 1.0001
@@ -482,9 +529,11 @@ MUTANTS = [
     ("apply", _mut_apply_eps_numerator),
     ("block_causal_head", _mut_block_exclusive),
     ("rope_angles", _mut_freq),
+    ("token_causal_head", _mut_token_exclusive),
 ]
 PIN_CHECKS = [check_worked_examples, check_axis_split, check_rotation_axes_and_frequencies,
-              check_brute_force_bidirectional, check_brute_force_block_causal, check_brute_force_cross]
+              check_brute_force_bidirectional, check_brute_force_block_causal, check_brute_force_cross,
+              check_brute_force_token_causal]
 
 
 @pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
