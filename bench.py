@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "linear-attn tokens/sec and achieved HBM GB/s (% peak), 720p-5s shape, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "720p5s"
-SRC_FILES = ["la_common.h", "la_state.h", "la_apply.h", "la_api.hip"]
+SRC_FILES = ["la_common.h", "la_state.h", "la_apply.h", "la_causal.h", "la_api.hip"]
 
 
 def kernel_source_hash():
@@ -284,7 +284,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s"],
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s"],
                     help="default: the headline 720p-5s bidirectional step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel events on every n-th timed step (each event costs ~2 us)")
@@ -499,6 +499,35 @@ def setup_workload(name, la, dev):
                        "input_sets": len(sets)},
             "groups": [("state", STATE_KERNELS, 2 * tkv), ("apply", APPLY_KERNELS, 2 * tq)],
             "copy_pairs": [(s[0], s[3]) for s in sets],
+        }
+
+    if name == "tc720p5s":
+        spec = WORKLOADS["720p5s"]
+        B, H, N, d, grid, eps = spec["B"], spec["H"], spec["N"], spec["d"], spec["grid"], spec["eps"]
+        q, k, v = make_qkv_device(B, H, N, d, "bf16", spec["seed"], dev)
+        tb = q.numel() * q.element_size()
+        base = rotating((q, k, v), n_sets_for(4 * tb))
+        sets = [(qi, ki, vi, torch.empty_like(q)) for (qi, ki, vi) in base]
+        ws = la.workspace(B, H, N, d, dev)
+
+        def step(i, ev, tev):
+            qi, ki, vi, oi = sets[i % len(sets)]
+            if ev is not None:
+                tev.record(ev[0])
+            la.token_causal(qi, ki, vi, grid, eps, out=oi, ws=ws)
+            if ev is not None:
+                tev.record(ev[1])
+
+        return {
+            "metric": "token-causal linear-attn tokens/sec and achieved HBM GB/s (% peak), 720p-5s shape, "
+                      "1 GPU",
+            "step": step, "tokens_per_step": B * N, "step_bytes": 4 * tb,
+            "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "eps": eps,
+                       "input_sets": len(sets)},
+            # one call: partial states, in-place prefix, causal scan (K and V are read twice)
+            "groups": [("token_causal", ("la_state_bf16_kernel", "la_prefix_kernel", "la_causal_bf16_kernel"),
+                        4 * tb)],
+            "copy_pairs": [(s_[0], s_[3]) for s_ in sets],
         }
 
     if name == "720p60s":

@@ -14,13 +14,15 @@
  *
  *   and "Block Linear Attention with Constant-Memory KV Cache" (Eq. 3, the
  *   running-sum update, Table 1, Algorithm 1): S and z are carried from block
- *   to block; block b is applied with the sums over blocks 0..b.
+ *   to block; block b is applied with the sums over blocks 0..b.  Eq. 3 taken
+ *   token by token is the token-causal mode (la_token_causal).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Q, K, V, O are contiguous [B, H, n, d] arrays in device memory, element
  *    type `dtype` (LA_BF16 = bfloat16, LA_FP32 = float).  n is N for the
- *    bidirectional calls and the block's length for la_block_causal_step.
+ *    bidirectional and token-causal calls and the block's length for
+ *    la_block_causal_step.
  *  - S is a contiguous [B, H, d, d] float array, row index = key channel,
  *    column index = value channel.  z is a contiguous [B, H, d] float array.
  *    Both are always fp32 and always caller-owned device memory.
@@ -113,6 +115,26 @@ LA_API int la_block_causal_step(const void* Q, const void* K, const void* V, voi
                          int B, int H, int N, int d, int gt, int gh, int gw,
                          int block_tokens, float eps, int dtype,
                          int block_idx, int commit, void* stream);
+
+/* Token-causal mode (Eq. 3 literally: section 3.3.1 of the same page,
+ * "Derivation from causal linear attention"; RoPE as in Eq. 2): token i sees
+ * tokens j <= i of the sequence,
+ *   S_i = S_carry + sum_{j<=i} RoPE(relu(K_j))^T V_j,   z_i = z_carry + sum_{j<=i} relu(K_j),
+ *   O_i = RoPE(relu(Q_i)) S_i / (relu(Q_i) . z_i + eps).
+ * Q, K, V, O are [B, H, N, d]; token i sits at global position n_offset + i
+ * (gt*gh*gw must hold n_offset + N tokens), so a long sequence can be fed in
+ * segments.  S_carry/z_carry are both NULL (start from the empty state; the
+ * final state is not returned) or both non-NULL: the state before token 0 on
+ * entry, the state after token N-1 on return.  bf16 and d = 64 only
+ * (otherwise LA_E_UNSUPPORTED).  N = 0 returns LA_OK and leaves the carry as
+ * it is.  ws: at least la_workspace_bytes(B, H, N, d) bytes, no
+ * initialisation needed; it must not overlap O or the carry.  Every piece of
+ * the computation has a fixed order, so repeated calls give bitwise equal
+ * results. */
+LA_API int la_token_causal(const void* Q, const void* K, const void* V, void* O,
+                    float* S_carry, float* z_carry, void* ws, size_t ws_bytes,
+                    int B, int H, int N, int d, int gt, int gh, int gw, int n_offset,
+                    float eps, int dtype, void* stream);
 
 /* Static text for a status code (never NULL). */
 LA_API const char* la_strerror(int status);

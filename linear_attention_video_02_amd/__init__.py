@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.la_apply.restype = ci
         L.la_block_causal_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [ci, ci, vp]
         L.la_block_causal_step.restype = ci
+        L.la_token_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + [ci] * 8 + [cf, ci, vp]
+        L.la_token_causal.restype = ci
         L.la_strerror.argtypes = [ci]
         L.la_strerror.restype = ctypes.c_char_p
         L.la_last_hip_error.argtypes = []
@@ -214,6 +216,30 @@ def block_causal_step(q, k, v, S_carry, z_carry, N, grid, block_tokens, block_id
                                     int(block_idx), int(bool(commit)), _stream(q))
     if rc:
         raise LinAttnError(rc, "la_block_causal_step")
+    return out
+
+
+def token_causal(q, k, v, grid=None, eps=1e-6, S_carry=None, z_carry=None, n_offset=0, out=None, ws=None):
+    """Token-causal linear attention (Eq. 3): token i sees tokens j <= i.
+
+    q, k, v: [B, H, N, d] bf16, d = 64; token i sits at global position
+    n_offset + i.  With S_carry/z_carry ([B, H, d, d] / [B, H, d] fp32) the
+    scan starts from that state and leaves the final state in them.
+    """
+    torch = _torch()
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, out)
+    if ws is None:
+        ws = workspace(B, H, max(N, 1), d, q.device)
+    gt, gh, gw = _grid(grid)
+    rc = lib().la_token_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_carry), _ptr(z_carry),
+                               _ptr(ws), ws.numel(), B, H, N, d, gt, gh, gw, int(n_offset), float(eps),
+                               _dtype_code(q), _stream(q))
+    if rc:
+        raise LinAttnError(rc, "la_token_causal")
     return out
 
 

@@ -10,6 +10,7 @@
 
 #include "la.h"
 #include "la_apply.h"
+#include "la_causal.h"
 #include "la_common.h"
 #include "la_state.h"
 
@@ -129,7 +130,16 @@ struct Plan {
 // State pass: about LA_STATE_WGS workgroups in all (default: one 512-thread
 // workgroup per CU for bf16),
 // chunks a multiple of the 64-token tile, at most kMaxPartials per head.
-int plan_state(const LaGeom& g, int d, int dtype, Plan* out) {
+int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0) {
+    if (force_chunk > 0) {  // chunking imposed by the caller (token-causal pass)
+        const int P = g.ntok > 0 ? (g.ntok + force_chunk - 1) / force_chunk : 1;
+        const size_t lds = (size_t)state_fixed_lds(d, dtype) + table_entries(g, force_chunk) * 8;
+        if (P > kMaxPartials || lds > kLdsLimit) return LA_E_UNSUPPORTED;
+        out->P = P;
+        out->chunk = force_chunk;
+        out->lds = lds;
+        return LA_OK;
+    }
     const int target = env_int("LA_STATE_WGS", dtype == LA_BF16 ? 256 : 1024);
     // chunks are whole tiles (the kernel's ring then runs on to a whole round
     // with zero tiles: a little compute, no memory traffic)
@@ -302,6 +312,80 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
     return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
 }
 
+// Token-causal pass: about LA_CAUSAL_WGS workgroups (default two 256-thread
+// workgroups per CU), chunks a multiple of 128 tokens (the state kernel's tile
+// at d = 64 and two causal steps), at most kMaxPartials per head.
+int plan_causal(const LaGeom& g, Plan* out) {
+    constexpr int unit = 128;
+    const int target = env_int("LA_CAUSAL_WGS", 512);
+    const int ntok = g.ntok;
+    int P = (target + g.BH - 1) / g.BH;
+    P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
+    const int max_p = (ntok + unit - 1) / unit;
+    if (P > max_p) P = max_p;
+    for (;;) {
+        const int chunk = (int)align_up((size_t)((ntok + P - 1) / P), unit);
+        const int Peff = (ntok + chunk - 1) / chunk;
+        const size_t lds = (size_t)CausalBf16Cfg<64>::SMEM_FIXED + table_entries(g, chunk) * 8;
+        Plan st;
+        if (Peff <= kMaxPartials && lds <= kLdsLimit && plan_state(g, 64, LA_BF16, &st, chunk) == LA_OK) {
+            out->P = Peff;
+            out->chunk = chunk;
+            out->lds = lds;
+            return LA_OK;
+        }
+        if (P >= kMaxPartials || P >= max_p) return LA_E_UNSUPPORTED;   // grid plane too large
+        ++P;
+    }
+}
+
+int run_token_causal(const void* Q, const void* K, const void* V, void* O, float* S_carry, float* z_carry,
+                     void* ws, int B, int H, int ntok, int n_offset, int d, int gt, int gh, int gw, float eps,
+                     hipStream_t st) {
+    const LaGeom g = make_geom(B, H, ntok, n_offset, d, gt, gh, gw);
+    Plan pc, ps;
+    int rc = plan_causal(g, &pc);
+    if (rc != LA_OK) return rc;
+    rc = plan_state(g, d, LA_BF16, &ps, pc.chunk);
+    if (rc != LA_OK) return rc;
+    const WsLayout L = ws_layout(g.BH, d);
+    float* partial = (float*)((char*)ws + L.partial);
+    // 1. one partial state per chunk
+    StateArgs sa;
+    sa.K = K;
+    sa.V = V;
+    sa.partial = partial;
+    sa.chunk = ps.chunk;
+    sa.P = ps.P;
+    sa.g = g;
+    rc = launch_kernel<StateArgs>(state_kernel(d, LA_BF16, g.rope), dim3(ps.P * g.BH), ps.lds, st, sa,
+                                  StateBf16Cfg<64>::THREADS);
+    if (rc != LA_OK) return rc;
+    // 2. exclusive prefixes in place (+ carry), total -> carry
+    PrefixArgs pa;
+    pa.partial = partial;
+    pa.S_carry = S_carry;
+    pa.z_carry = z_carry;
+    pa.S_out = S_carry;
+    pa.z_out = z_carry;
+    pa.P = ps.P;
+    rc = launch_kernel<PrefixArgs>(la_prefix_kernel<64>, dim3((d * d + d + 255) / 256, g.BH), 0, st, pa);
+    if (rc != LA_OK) return rc;
+    // 3. causal scan of every chunk from its prefix
+    CausalArgs ca;
+    ca.Q = Q;
+    ca.K = K;
+    ca.V = V;
+    ca.O = O;
+    ca.pre = partial;
+    ca.eps = eps;
+    ca.chunk = pc.chunk;
+    ca.P = pc.P;
+    ca.g = g;
+    auto fn = g.rope ? la_causal_bf16_kernel<64, true> : la_causal_bf16_kernel<64, false>;
+    return launch_kernel<CausalArgs>(fn, dim3(pc.P * g.BH), pc.lds, st, ca, CausalBf16Cfg<64>::THREADS);
+}
+
 size_t elem_bytes(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
 
 // Plans depend only on sizes, so a plan failure is reported before any launch.
@@ -404,6 +488,40 @@ int la_block_causal_step(const void* Q, const void* K, const void* V, void* O, f
                    H, Lb, (int)start, d, gt, gh, gw, dtype, st);
     if (rc != LA_OK) return rc;
     return run_apply(Q, O, Sb, zb, B, H, Lb, (int)start, d, gt, gh, gw, eps, dtype, st);
+}
+
+int la_token_causal(const void* Q, const void* K, const void* V, void* O, float* S_carry, float* z_carry,
+                    void* ws, size_t ws_bytes, int B, int H, int N, int d, int gt, int gh, int gw, int n_offset,
+                    float eps, int dtype, void* stream) {
+    if (n_offset < 0 || N < 0 || (long long)n_offset + N >= (1ll << 30)) return LA_E_SHAPE;
+    int rc = check_common(B, H, n_offset + N, d, gt, gh, gw, eps, dtype);
+    if (rc != LA_OK) return rc;
+    if (dtype != LA_BF16 || d != 64) return LA_E_UNSUPPORTED;
+    if ((S_carry == nullptr) != (z_carry == nullptr)) return LA_E_NULLPTR;
+    if (!ws || (N > 0 && (!Q || !K || !V || !O))) return LA_E_NULLPTR;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(ws) ||
+        !aligned16(S_carry) || !aligned16(z_carry))
+        return LA_E_ALIGN;
+    const WsLayout L = ws_layout(B * H, d);
+    if (ws_bytes < L.total) return LA_E_WORKSPACE;
+    if (N == 0) return LA_OK;  // no token: the carry stays as it is
+    const size_t nb = (size_t)B * H * N * d * elem_bytes(dtype);
+    const size_t nS = S_carry ? (size_t)B * H * d * d * 4 : 0, nz = z_carry ? (size_t)B * H * d * 4 : 0;
+    if (overlaps(O, nb, Q, nb) || overlaps(O, nb, K, nb) || overlaps(O, nb, V, nb) ||
+        overlaps(O, nb, S_carry, nS) || overlaps(O, nb, z_carry, nz) || overlaps(S_carry, nS, z_carry, nz) ||
+        overlaps(S_carry, nS, K, nb) || overlaps(S_carry, nS, V, nb) || overlaps(S_carry, nS, Q, nb) ||
+        overlaps(z_carry, nz, K, nb) || overlaps(z_carry, nz, V, nb) || overlaps(z_carry, nz, Q, nb) ||
+        overlaps(ws, ws_bytes, S_carry, nS) || overlaps(ws, ws_bytes, z_carry, nz) ||
+        overlaps(ws, ws_bytes, O, nb))
+        return LA_E_ALIAS;
+    {
+        const LaGeom g = make_geom(B, H, N, n_offset, d, gt, gh, gw);
+        Plan pc;
+        rc = plan_causal(g, &pc);
+        if (rc != LA_OK) return rc;
+    }
+    return run_token_causal(Q, K, V, O, S_carry, z_carry, ws, B, H, N, n_offset, d, gt, gh, gw, eps,
+                            (hipStream_t)stream);
 }
 
 const char* la_last_hip_error(void) { return g_hip_msg; }

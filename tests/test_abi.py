@@ -38,7 +38,8 @@ def header_enum(name):
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
-                          "la_block_causal_step", "la_strerror", "la_last_hip_error"}
+                          "la_block_causal_step", "la_token_causal", "la_strerror",
+                          "la_last_hip_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -154,6 +155,41 @@ def test_apply_rejects(L, kw, want):
 ])
 def test_block_step_rejects(L, kw, want):
     assert step_call(L, **kw) == E[want]
+
+
+def causal_call(L, **kw):
+    a = dict(Q=p(0), K=p(1 << 30), V=p(2 << 30), O=p(3 << 30), S=p(4 << 30), z=p(5 << 30),
+             ws=p(6 << 30), ws_bytes=1 << 40, B=1, H=2, N=1000, d=64, gt=10, gh=10, gw=10, n0=0,
+             eps=1e-6, dtype=la.LA_BF16)
+    a.update(kw)
+    return L.la_token_causal(a["Q"], a["K"], a["V"], a["O"], a["S"], a["z"], a["ws"], a["ws_bytes"],
+                             a["B"], a["H"], a["N"], a["d"], a["gt"], a["gh"], a["gw"], a["n0"],
+                             a["eps"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=la.LA_FP32), "LA_E_UNSUPPORTED"),
+    (dict(d=32), "LA_E_UNSUPPORTED"),
+    (dict(d=128), "LA_E_UNSUPPORTED"),
+    (dict(n0=-1), "LA_E_SHAPE"),
+    (dict(n0=1), "LA_E_SHAPE"),                    # grid holds 1000 tokens, needs 1001
+    (dict(N=-3), "LA_E_SHAPE"),
+    (dict(S=None), "LA_E_NULLPTR"),               # carry pointers: both or neither
+    (dict(ws=None), "LA_E_NULLPTR"),
+    (dict(K=None), "LA_E_NULLPTR"),
+    (dict(V=p((2 << 30) + 8)), "LA_E_ALIGN"),
+    (dict(ws_bytes=100), "LA_E_WORKSPACE"),
+    (dict(O=p(0)), "LA_E_ALIAS"),                  # O == Q
+    (dict(ws=p(3 << 30)), "LA_E_ALIAS"),           # workspace over O
+    (dict(gt=1, gh=1000, gw=3000), "LA_E_UNSUPPORTED"),  # RoPE table cannot fit LDS
+])
+def test_token_causal_rejects(L, kw, want):
+    assert causal_call(L, **kw) == E[want]
+
+
+def test_token_causal_empty_is_noop(L):
+    # N = 0: checks pass, nothing is launched, the (fake) carry is not touched
+    assert causal_call(L, N=0, Q=None, K=None, V=None, O=None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

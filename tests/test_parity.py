@@ -213,3 +213,67 @@ def test_cross720p(la):
     for (b, h) in ((0, 0), (1, 31), (0, 17)):
         ref = oracle.cross_attention_head(host(tq[b, h]), host(tk[b, h]), host(tv[b, h]), w["eps"])
         assert_close(host(out[b, h]), ref, "bf16", f"cross720p head ({b},{h})")
+
+
+TC_CASES = [
+    # B, H, N, d, grid, eps   (token-causal, Eq. 3 literally)
+    (1, 1, 1, 64, (1, 1, 1), 1e-6),
+    (1, 2, 1000, 64, (10, 10, 10), 1e-6),
+    (2, 3, 300, 64, None, 1e-6),
+    (1, 2, 129, 64, (2, 9, 10), 0.0),
+    (1, 1, 5000, 64, (3, 41, 41), 1e-6),
+    (1, 4, 4097, 64, (5, 23, 40), 1e-6),
+]
+
+
+@pytest.mark.parametrize("case", TC_CASES, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}" for c in TC_CASES])
+def test_token_causal(la, case):
+    import torch
+    B, H, N, d, grid, eps = case
+    say(f"[token-causal] {case}")
+    q, k, v = make_qkv(B, H, N, d, "bf16", seed=5000 + N)
+    out = la.token_causal(upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, eps)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.token_causal(q, k, v, grid, eps)
+    assert_close(host(out), ref, "bf16", f"token-causal {case}")
+
+
+def test_token_causal_720p5s(la):
+    """The 720p-5s workload in token-causal mode; sampled heads, every row."""
+    import torch
+    tq, tk, tv, w = make_workload_device("720p5s")
+    grid, eps = w["grid"], w["eps"]
+    out = la.token_causal(tq, tk, tv, grid, eps)
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 0), (1, 31), (0, 13)):
+        ref, _, _ = oracle.token_causal_head(host(tq[b, h]), host(tk[b, h]), host(tv[b, h]), grid, eps)
+        assert_close(host(out[b, h]), ref, "bf16", f"720p5s token-causal head ({b},{h})")
+
+
+def test_token_causal_carry_resume_and_determinism(la):
+    """Two segments with a carry and a position offset == one call; final carry == total state."""
+    import torch
+    B, H, N, d, grid, eps = 1, 2, 2000, 64, (5, 20, 20), 1e-6
+    q, k, v = make_qkv(B, H, N, d, "bf16", seed=5100)
+    tq, tk, tv = upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16")
+    S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda:0")
+    z = torch.zeros((B, H, d), dtype=torch.float32, device="cuda:0")
+    m = 777
+    o1 = la.token_causal(tq[:, :, :m].contiguous(), tk[:, :, :m].contiguous(), tv[:, :, :m].contiguous(),
+                         grid, eps, S, z, 0)
+    o2 = la.token_causal(tq[:, :, m:].contiguous(), tk[:, :, m:].contiguous(), tv[:, :, m:].contiguous(),
+                         grid, eps, S, z, m)
+    whole = la.token_causal(tq, tk, tv, grid, eps)
+    again = la.token_causal(tq, tk, tv, grid, eps)
+    torch.cuda.synchronize()
+    assert torch.equal(whole, again), "repeated calls differ"
+    ref, Sr, zr = oracle.token_causal(q, k, v, grid, eps)
+    assert_close(host(torch.cat([o1, o2], dim=2)), ref, "bf16", "two segments with carry")
+    assert state_err(host(S).reshape(-1, d), Sr.reshape(-1, d)) <= 1e-4
+    np.testing.assert_allclose(host(z), zr, rtol=1e-5)
+    # empty segment: carry unchanged
+    S0 = S.clone()
+    la.token_causal(tq[:, :, :0].contiguous(), tk[:, :, :0].contiguous(), tv[:, :, :0].contiguous(),
+                    grid, eps, S, z, N)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0)
