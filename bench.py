@@ -284,7 +284,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s"],
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b"],
                     help="default: the headline 720p-5s bidirectional step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel events on every n-th timed step (each event costs ~2 us)")
@@ -467,6 +467,37 @@ def setup_workload(name, la, dev):
             "groups": [("state", STATE_KERNELS, 2 * tb), ("apply", APPLY_KERNELS, 2 * tb)],
             "copy_pairs": [(s[0], s[3]) for s in sets],
             "cpu_baseline": lambda budget: cpu_baseline(q, k, v, spec, budget),
+        }
+
+    if name == "sana2b":
+        spec = WORKLOADS[name]
+        B, H, N, d, grid, eps = spec["B"], spec["H"], spec["N"], spec["d"], spec["grid"], spec["eps"]
+        q, k, v = make_qkv_device(B, H, N, d, "bf16", spec["seed"], dev)
+        tb = q.numel() * q.element_size()
+        base = rotating((q, k, v), n_sets_for(4 * tb))
+        sets = [(qi, ki, vi, torch.empty_like(q), torch.empty((B, H, d, d), dtype=torch.float32, device=dev),
+                 torch.empty((B, H, d), dtype=torch.float32, device=dev)) for (qi, ki, vi) in base]
+        ws = la.workspace(B, H, N, d, dev)
+
+        def step(i, ev, tev):
+            qi, ki, vi, oi, S, z = sets[i % len(sets)]
+            if ev is not None:
+                tev.record(ev[0])
+            la.state_reduce(ki, vi, grid, S=S, z=z, ws=ws)
+            if ev is not None:
+                tev.record(ev[1])
+            la.apply(qi, S, z, grid, eps, out=oi)
+            if ev is not None:
+                tev.record(ev[2])
+
+        return {
+            "metric": "linear-attn tokens/sec and achieved HBM GB/s (% peak), SANA-Video-2B heads "
+                      "(H=20, d=112) on the 720p-5s latent, 1 GPU",
+            "step": step, "tokens_per_step": B * N, "step_bytes": 4 * tb,
+            "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "eps": eps,
+                       "input_sets": len(sets)},
+            "groups": [("state", STATE_KERNELS, 2 * tb), ("apply", APPLY_KERNELS, 2 * tb)],
+            "copy_pairs": [(s_[0], s_[3]) for s_ in sets],
         }
 
     if name == "cross720p":

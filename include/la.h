@@ -26,7 +26,9 @@
  *  - S is a contiguous [B, H, d, d] float array, row index = key channel,
  *    column index = value channel.  z is a contiguous [B, H, d] float array.
  *    Both are always fp32 and always caller-owned device memory.
- *  - d must be 32, 64 or 128.  eps >= 0 is added to the denominator only.
+ *  - d must be 32, 64, 112 or 128 (112: SANA-Video-2B's head size, section
+ *    3.4 "Macro-architecture specifications (Table 6)").  eps >= 0 is added
+ *    to the denominator only.
  *    A row whose relu(Q_i) is all zero gets an all-zero output row.
  *  - (gt, gh, gw) is the latent grid.  Token n sits at
  *    t = n / (gh*gw), h = (n / gw) % gh, w = n % gw (0-based, t-major).
@@ -68,7 +70,7 @@ enum {
     LA_OK = 0,
     LA_E_NULLPTR = -1,     /* a required pointer is NULL */
     LA_E_SHAPE = -2,       /* bad B/H/N/grid/block arguments */
-    LA_E_UNSUPPORTED = -3, /* d not in {32,64,128}, bad dtype, grid too large */
+    LA_E_UNSUPPORTED = -3, /* d not in {32,64,112,128}, bad dtype, grid too large */
     LA_E_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     LA_E_WORKSPACE = -5,   /* ws_bytes < la_workspace_bytes(...) */
     LA_E_HIP = -6,         /* the HIP runtime rejected a launch */

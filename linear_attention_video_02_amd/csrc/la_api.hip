@@ -51,7 +51,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // Checks shared by every entry point.  N is the whole sequence length.
 int check_common(int B, int H, int N, int d, int gt, int gh, int gw, float eps, int dtype) {
     if (dtype != LA_FP32 && dtype != LA_BF16) return LA_E_UNSUPPORTED;
-    if (d != 32 && d != 64 && d != 128) return LA_E_UNSUPPORTED;
+    if (d != 32 && d != 64 && d != 112 && d != 128) return LA_E_UNSUPPORTED;
     if (B < 1 || H < 1 || N < 0) return LA_E_SHAPE;
     if (!(eps >= 0.0f) || eps != eps) return LA_E_SHAPE;
     const long long BH = (long long)B * H;
@@ -103,12 +103,14 @@ int state_fixed_lds(int d, int dtype) {
         switch (d) {
             case 32: return StateBf16Cfg<32>::SMEM_FIXED;
             case 64: return StateBf16Cfg<64>::SMEM_FIXED;
+            case 112: return StateBf16Cfg<112>::SMEM_FIXED;
             default: return StateBf16Cfg<128>::SMEM_FIXED;
         }
     }
     switch (d) {
         case 32: return StateF32Cfg<32>::SMEM_FIXED;
         case 64: return StateF32Cfg<64>::SMEM_FIXED;
+        case 112: return StateF32Cfg<112>::SMEM_FIXED;
         default: return StateF32Cfg<128>::SMEM_FIXED;
     }
 }
@@ -118,6 +120,7 @@ int apply_fixed_lds(int d, int dtype) {
     switch (d) {
         case 32: return ApplyF32Cfg<32>::SMEM_FIXED;
         case 64: return ApplyF32Cfg<64>::SMEM_FIXED;
+        case 112: return ApplyF32Cfg<112>::SMEM_FIXED;
         default: return ApplyF32Cfg<128>::SMEM_FIXED;
     }
 }
@@ -143,8 +146,10 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0
     const int target = env_int("LA_STATE_WGS", dtype == LA_BF16 ? 256 : 1024);
     // chunks are whole tiles (the kernel's ring then runs on to a whole round
     // with zero tiles: a little compute, no memory traffic)
-    const int tile = dtype == LA_BF16 ? (d == 32 ? StateBf16Cfg<32>::TT : d == 64 ? StateBf16Cfg<64>::TT
-                                                                              : StateBf16Cfg<128>::TT)
+    const int tile = dtype == LA_BF16 ? (d == 32   ? StateBf16Cfg<32>::TT
+                                         : d == 64  ? StateBf16Cfg<64>::TT
+                                         : d == 112 ? StateBf16Cfg<112>::TT
+                                                    : StateBf16Cfg<128>::TT)
                                       : 64;
     const int ntok = g.ntok;
     int P = (target + g.BH - 1) / g.BH;
@@ -224,6 +229,7 @@ int launch_kernel(KernelFn<Args> fn, dim3 grid, size_t lds, hipStream_t st, cons
 KernelFn<CombineArgs> combine_kernel(int d) {
     if (d == 32) return la_state_combine_kernel<32>;
     if (d == 64) return la_state_combine_kernel<64>;
+    if (d == 112) return la_state_combine_kernel<112>;
     return la_state_combine_kernel<128>;
 }
 
@@ -235,6 +241,7 @@ KernelFn<StateArgs> state_kernel(int d, int dtype, bool rope) {
     }
     LA_PICK(32)
     LA_PICK(64)
+    LA_PICK(112)
     LA_PICK(128)
 #undef LA_PICK
     return nullptr;
@@ -248,6 +255,7 @@ KernelFn<ApplyArgs> apply_kernel(int d, int dtype, bool rope) {
     }
     LA_PICK(32)
     LA_PICK(64)
+    LA_PICK(112)
     LA_PICK(128)
 #undef LA_PICK
     return nullptr;
@@ -272,6 +280,7 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     const int threads = dtype != LA_BF16 ? 256
                         : d == 32        ? StateBf16Cfg<32>::THREADS
                         : d == 64        ? StateBf16Cfg<64>::THREADS
+                        : d == 112       ? StateBf16Cfg<112>::THREADS
                                          : StateBf16Cfg<128>::THREADS;
     rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
     if (rc != LA_OK) return rc;
@@ -308,6 +317,7 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
     const int threads = dtype != LA_BF16 ? 256
                         : d == 32        ? ApplyBf16Cfg<32>::THREADS
                         : d == 64        ? ApplyBf16Cfg<64>::THREADS
+                        : d == 112       ? ApplyBf16Cfg<112>::THREADS
                                          : ApplyBf16Cfg<128>::THREADS;
     return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
 }

@@ -42,12 +42,13 @@ struct ApplyArgs {
 // ---------------------------------------------------------------------------
 template <int D>
 struct ApplyBf16Cfg {
+    static constexpr int DP = Pad<D>::P;  // channels on chip (zero above D)
     // 8 waves per CU; at d = 128 a lane needs ~350 registers, which only fits
     // with 4 waves per workgroup (one per SIMD)
     static constexpr int THREADS = D <= 64 ? 512 : 256;
     static constexpr int NW = THREADS / 64;
-    static constexpr int KS = D / 32;   // 32-channel k-steps
-    static constexpr int NT = D / 16;   // 16-channel output tiles
+    static constexpr int KS = DP / 32;  // 32-channel k-steps
+    static constexpr int NT = DP / 16;  // 16-channel output tiles
     static constexpr int GR = D <= 64 ? 2 : 1;   // 16-token groups per unit of work
     static constexpr int UNIT = 16 * GR;         // tokens a wave takes from the queue at a time
     static constexpr int DEPTH = D <= 64 ? 3 : 2;  // units of Q in flight per wave
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float sv = Sh[(32 * ks + 8 * g + e) * D + co];
+                const int ci = 32 * ks + 8 * g + e;
+                const float sv = (C::DP == D || (ci < D && co < D)) ? Sh[ci * D + co] : 0.0f;
                 const __bf16 hi = (__bf16)sv;
                 Ahi[T][ks][e] = hi;
                 if (C::SLO) Alo[C::SLO ? T : 0][ks][e] = (__bf16)(sv - (float)hi);
@@ -137,7 +139,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zr[ks][e] = a.z[(size_t)bh * D + 32 * ks + 8 * g + e];
+        for (int e = 0; e < 8; ++e)
+            zr[ks][e] = (C::DP == D || 32 * ks + 8 * g + e < D) ? a.z[(size_t)bh * D + 32 * ks + 8 * g + e] : 0.0f;
 
     int t_lo = 0, nt = 1;
     PairRef pr[C::KS][4];
@@ -149,7 +152,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pr[ks][i] = pair_ref(16 * ks + 4 * g + i, nt, a.g);
+            for (int i = 0; i < 4; ++i)
+                pr[ks][i] = pair_ref((C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g + i : 0, nt, a.g);
     }
     lds_barrier();  // RoPE table and queue head visible
 
@@ -180,9 +184,11 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
                     float x[8];
+                    // channels past d (d = 112) were loaded from the next row: zero them
+                    const bool live = C::DP == D || 32 * ks + 8 * g < D;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t w = relu_bf16x2(qc[r][ks][i]);
+                        const uint32_t w = live ? relu_bf16x2(qc[r][ks][i]) : 0u;
                         x[2 * i] = bf_lo(w);
                         x[2 * i + 1] = bf_hi(w);
                     }
@@ -228,7 +234,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     o[1] = pack_bf16(acc[2 * sp][2] * inv, acc[2 * sp][3] * inv);
                     o[2] = pack_bf16(acc[2 * sp + 1][0] * inv, acc[2 * sp + 1][1] * inv);
                     o[3] = pack_bf16(acc[2 * sp + 1][2] * inv, acc[2 * sp + 1][3] * inv);
-                    buf_store16(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
+                    if (C::DP == D || 32 * sp + 8 * g < D)
+                        buf_store16(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
                 }
             }
         }

@@ -40,6 +40,14 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
     return f.one ? n : (__umulhi(n, f.m) >> f.shift);
 }
 
+// Channels a kernel works on for head dim d: d itself for 32, 64 and 128;
+// d = 112 runs as 128 with channels 112..127 held at zero on chip (HBM rows
+// keep their 112 channels).
+template <int D>
+struct Pad {
+    static constexpr int P = D == 112 ? 128 : D;
+};
+
 // ---------------------------------------------------------------------------
 // geometry of one call: tokens, grid and RoPE pair split
 // ---------------------------------------------------------------------------

@@ -130,18 +130,19 @@ __device__ __forceinline__ void item_of_block(int P, int BH, int& bh, int& p) {
 // ---------------------------------------------------------------------------
 template <int D>
 struct StateBf16Cfg {
+    static constexpr int DP = Pad<D>::P;      // channels on chip (zero above D)
     static constexpr int THREADS = D <= 64 ? 1024 : 512;
     static constexpr int NW = THREADS / 64;
-    static constexpr int CH = D / 8;          // 16-byte pieces per token row
+    static constexpr int CH = DP / 8;         // 16-byte pieces per token row
     static constexpr int ROWS = THREADS / CH; // token rows per load pass
     static constexpr int LP = D <= 64 ? 1 : 2;  // load passes per tile
     static constexpr int TT = ROWS * LP;      // tokens per tile: 256, 128, 64
     static constexpr int DEPTH = 2;           // tiles of K/V in flight per workgroup
-    static constexpr int TILE = TT * D;       // elements per LDS tile (unpadded)
+    static constexpr int TILE = TT * DP;      // elements per LDS tile
     static constexpr int BUF = 3 * TILE;      // K hi, K lo, V
-    static constexpr int NCI = D / 32;        // key-channel tiles = wave groups
+    static constexpr int NCI = DP / 32;       // key-channel tiles = wave groups
     static constexpr int NTG = NW / NCI;      // token groups
-    static constexpr int NJ = D / 32;         // value-channel tiles per wave
+    static constexpr int NJ = DP / 32;        // value-channel tiles per wave
     static constexpr int KSTEPS = TT / (16 * NTG);  // 16-token steps per wave per tile
     static constexpr int NACC = NJ * 16;      // accumulators per lane
     static constexpr int STAGE_BYTES = 2 * BUF * 2;
@@ -158,7 +159,7 @@ struct StateBf16Cfg {
 // r0..r0+3 (r0 % 4 == 0) start in different 16-bank groups.
 template <int D>
 __device__ __forceinline__ int swz(int row, int ch) {
-    const int s = D == 32 ? 0 : (D == 64 ? ((row >> 1) & 1) : (row & 3));
+    const int s = D == 32 ? 0 : (D == 64 ? ((row >> 1) & 1) : (row & 3));  // D = on-chip width
     return row * D + (((ch >> 5) ^ s) << 5) + (ch & 31);
 }
 
@@ -182,6 +183,9 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
     const BufRsrc Kr = make_rsrc((const uint16_t*)a.K + chunk_off, chunk_bytes);
     const BufRsrc Vr = make_rsrc((const uint16_t*)a.V + chunk_off, chunk_bytes);
     const int cc = tid % C::CH, trow = tid / C::CH;
+    // lanes past the real channels (d = 112 only) load a neighbour's bytes
+    // unconditionally (keeps the load count uniform) and stage zeros
+    const bool live = C::DP == D || 8 * cc < D;
 
     // ring of DEPTH tiles in registers: tile i lives in slot i % DEPTH
     u32x4 kr[C::DEPTH][C::LP], vr[C::DEPTH][C::LP];
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
         int nt = (int)fdiv((uint32_t)(a.g.n_offset + cl), a.g.div_hw) - t_lo + 1;
         build_rope_table(tab, t_lo, nt, a.g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = pair_ref(4 * cc + i, nt, a.g);
+        for (int i = 0; i < 4; ++i) pr[i] = pair_ref(live ? 4 * cc + i : 0, nt, a.g);
     }
 
     float zp[8];
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
             float x[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t w = relu_bf16x2(kr[s][j][i]);
+                const uint32_t w = live ? relu_bf16x2(kr[s][j][i]) : 0u;
                 x[2 * i] = bf_lo(w);
                 x[2 * i + 1] = bf_hi(w);
             }
@@ -242,10 +246,10 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
                 hw[i] = h;
                 lw[i] = l;
             }
-            const int o = swz<D>(tl, 8 * cc);
+            const int o = swz<C::DP>(tl, 8 * cc);
             *(u32x4*)(khi + o) = hw;
             *(u32x4*)(klo + o) = lw;
-            *(u32x4*)(vt + o) = vr[s][j];
+            *(u32x4*)(vt + o) = live ? vr[s][j] : u32x4{0u, 0u, 0u, 0u};
         }
     };
 
@@ -287,12 +291,12 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
                 const int kb0 = 16 * (tgrp * C::KSTEPS + st);
                 const int r0 = kb0 + rd_row, r1 = r0 + 4;
                 const int col = 32 * ctile + rd_col;
-                Ah[st] = lds_read_tr8(khi + swz<D>(r0, col), khi + swz<D>(r1, col));
-                Al[st] = lds_read_tr8(klo + swz<D>(r0, col), klo + swz<D>(r1, col));
+                Ah[st] = lds_read_tr8(khi + swz<C::DP>(r0, col), khi + swz<C::DP>(r1, col));
+                Al[st] = lds_read_tr8(klo + swz<C::DP>(r0, col), klo + swz<C::DP>(r1, col));
 #pragma unroll
                 for (int j = 0; j < C::NJ; ++j) {
                     const int vcol = 32 * j + rd_col;
-                    Bv[st][j] = lds_read_tr8(vt + swz<D>(r0, vcol), vt + swz<D>(r1, vcol));
+                    Bv[st][j] = lds_read_tr8(vt + swz<C::DP>(r0, vcol), vt + swz<C::DP>(r1, vcol));
                 }
             }
             // stage the next tile into the other buffer while these MFMAs run
@@ -347,7 +351,7 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
             for (int r = 0; r < 16; ++r) {
                 const int row = 32 * ctile + 8 * (r >> 2) + 4 * gq + (r & 3);
                 const int col = 32 * j + m;
-                part[row * D + col] = acc[j][r];
+                if (C::DP == D || (row < D && col < D)) part[row * D + col] = acc[j][r];
             }
     }
     // ---- z partial: threads sharing a channel block, summed in thread order ----

@@ -12,6 +12,8 @@ Workloads (latent token grids of the pages' video shapes; DCAE-V compresses
   720p5s  B2 H32 N19320  d64  bf16, grid 21x23x40
   720p60s B1 H32 N220800 d64  bf16, grid 240x23x40, 10 blocks of 22080 tokens
   sweep   B1 H32 d in {32,64,128}, N in {4096,16384,65536,220800}, grid ceil(N/920)x23x40
+  sana2b  B1 H20 N19320  d112 bf16, grid 21x23x40: SANA-Video-2B's real heads (20 x 112,
+          width 2240) on the 720p-5s latent
   cross720p  B2 H32, 19320 video queries over 300 text keys/values, d64 bf16, no RoPE
              (the pages give no text length; 300 is a parameter)
 """
@@ -42,6 +44,7 @@ WORKLOADS = {
     "720p60s": _workload("720p60s", 1, 32, 220800, 64, "bf16", (240, 23, 40), 1004,
                          block=22080),
 }
+WORKLOADS["sana2b"] = _workload("sana2b", 1, 20, 19320, 112, "bf16", (21, 23, 40), 1007)
 for _d in SWEEP_D:
     for _n in SWEEP_N:
         WORKLOADS[f"sweep_d{_d}_n{_n}"] = _workload(

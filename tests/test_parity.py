@@ -81,6 +81,11 @@ def test_720p5s(la):
     _check_bidirectional(la, "720p5s")
 
 
+def test_sana2b_d112(la):
+    """SANA-Video-2B's heads (H = 20, d = 112) on the 720p-5s latent, every head."""
+    _check_bidirectional(la, "sana2b")
+
+
 @pytest.mark.parametrize("d", SWEEP_D)
 @pytest.mark.parametrize("N", SWEEP_N)
 def test_sweep(la, d, N):
@@ -121,6 +126,9 @@ FUZZ = [
     (2, 2, 513, 32, "fp32", None, 0.0),
     (1, 3, 130, 128, "bf16", (130, 1, 1), 1e-6),
     (1, 1, 5000, 64, "bf16", (3, 41, 41), 1e-6),
+    (1, 2, 1000, 112, "bf16", (4, 17, 19), 1e-6),
+    (2, 1, 333, 112, "fp32", (3, 11, 11), 1e-6),
+    (1, 3, 64, 112, "bf16", None, 0.0),
 ]
 
 
@@ -143,6 +151,7 @@ BC_FUZZ = [
     (1, 1, 500, 128, "bf16", (5, 10, 10), 100, 0.0),
     (1, 2, 100, 64, "fp32", (4, 5, 5), 1, 1e-6),
     (1, 1, 640, 64, "bf16", None, 128, 1e-6),
+    (1, 2, 900, 112, "bf16", (9, 10, 10), 250, 1e-6),
 ]
 
 
@@ -176,6 +185,7 @@ CROSS_CASES = [
     (2, 3, 1000, 77, 64, "bf16", 0.0),
     (1, 1, 1, 7, 64, "fp32", 1e-6),
     (1, 2, 64, 0, 64, "bf16", 1e-6),
+    (1, 20, 2000, 300, 112, "bf16", 1e-6),
 ]
 
 
