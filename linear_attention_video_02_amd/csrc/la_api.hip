@@ -116,7 +116,14 @@ int state_fixed_lds(int d, int dtype) {
 }
 
 int apply_fixed_lds(int d, int dtype) {
-    if (dtype == LA_BF16) return 0;
+    if (dtype == LA_BF16) {
+        switch (d) {
+            case 32: return ApplyBf16Cfg<32>::FIXED;
+            case 64: return ApplyBf16Cfg<64>::FIXED;
+            case 112: return ApplyBf16Cfg<112>::FIXED;
+            default: return ApplyBf16Cfg<128>::FIXED;
+        }
+    }
     switch (d) {
         case 32: return ApplyF32Cfg<32>::SMEM_FIXED;
         case 64: return ApplyF32Cfg<64>::SMEM_FIXED;
@@ -152,7 +159,9 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0
                                                     : StateBf16Cfg<128>::TT)
                                       : 64;
     const int ntok = g.ntok;
-    int P = (target + g.BH - 1) / g.BH;
+    // at most `target` workgroups: one more than the CUs would run a second
+    // wave of workgroups after the first and double the pass
+    int P = target / g.BH;
     P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
     const int max_p = ntok > 0 ? (ntok + tile - 1) / tile : 1;
     if (P > max_p) P = max_p;
@@ -178,7 +187,7 @@ int plan_apply(const LaGeom& g, int d, int dtype, Plan* out) {
     const int target = env_int("LA_APPLY_WGS", dtype == LA_BF16 ? 256 : 1024);
     const int tile = 128;
     const int ntok = g.ntok;
-    int P = (target + g.BH - 1) / g.BH;
+    int P = target / g.BH;  // at most `target` workgroups (see plan_state)
     if (P < 1) P = 1;
     const int max_p = ntok > 0 ? (ntok + tile - 1) / tile : 1;
     if (P > max_p) P = max_p;
@@ -329,7 +338,7 @@ int plan_causal(const LaGeom& g, Plan* out) {
     constexpr int unit = 128;
     const int target = env_int("LA_CAUSAL_WGS", 512);
     const int ntok = g.ntok;
-    int P = (target + g.BH - 1) / g.BH;
+    int P = target / g.BH;  // at most `target` workgroups (see plan_state)
     P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
     const int max_p = (ntok + unit - 1) / unit;
     if (P > max_p) P = max_p;

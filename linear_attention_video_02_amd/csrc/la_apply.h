@@ -43,9 +43,9 @@ struct ApplyArgs {
 template <int D>
 struct ApplyBf16Cfg {
     static constexpr int DP = Pad<D>::P;  // channels on chip (zero above D)
-    // 8 waves per CU; at d = 128 a lane needs ~350 registers, which only fits
-    // with 4 waves per workgroup (one per SIMD)
-    static constexpr int THREADS = D <= 64 ? 512 : 256;
+    // d <= 64: 8 waves per CU (2 per SIMD: S^T hi + lo in registers);
+    // d >= 112: 12 waves (S^T in LDS, <= 168 registers a lane)
+    static constexpr int THREADS = D <= 64 ? 512 : 768;
     static constexpr int NW = THREADS / 64;
     static constexpr int KS = DP / 32;  // 32-channel k-steps
     static constexpr int NT = DP / 16;  // 16-channel output tiles
@@ -56,7 +56,21 @@ struct ApplyBf16Cfg {
     // d = 64, 512 at d = 128.  At d = 128 only the hi part is held (S rounded to
     // bf16, relative error 2^-9 per entry).
     static constexpr bool SLO = D <= 64;
+    // d >= 112: S^T (bf16 hi) lives in LDS instead of registers (128 x 128
+    // bf16 would take 128 registers a lane); MFMA A fragments are read from it
+    static constexpr bool SLDS = DP > 64;
+    static constexpr int ZBYTES = DP * 4;                  // z, then S^T, then the RoPE table
+    static constexpr int SBYTES = SLDS ? DP * DP * 2 : 0;
+    static constexpr int FIXED = ZBYTES + SBYTES;
 };
+
+// Element offset of S^T row pr (= 16 T + m, see below), 16-byte chunk c, in
+// the LDS copy used at d >= 112: chunks are XOR-swizzled by row so that 16
+// consecutive rows read at one chunk hit 16 distinct bank groups.
+template <int DP>
+__device__ __forceinline__ int st_off(int pr, int c) {
+    return pr * DP + ((c ^ (pr & 15)) << 3);
+}
 
 // Work item mapping shared with the state pass (whole heads per XCD).
 __device__ __forceinline__ void apply_item_of_block(int P, int BH, int& bh, int& p) {
@@ -71,7 +85,9 @@ template <int D, bool ROPE>
 __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel(ApplyArgs a) {
     using C = ApplyBf16Cfg<D>;
     extern __shared__ __align__(16) unsigned char smem[];
-    float2* tab = (float2*)smem;
+    float* zs = (float*)smem;                        // [DP] z (zero above d)
+    uint16_t* st = (uint16_t*)(smem + C::ZBYTES);    // [DP][DP] S^T hi (d >= 112)
+    float2* tab = (float2*)(smem + C::FIXED);
     __shared__ int q_next;  // next unit of this workgroup's chunk, in tokens
 
     const int lane = threadIdx.x & 63;
@@ -118,10 +134,21 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     }
 
     // S^T fragments (hi/lo bf16) and this lane's z entries
-    bf16x8 Ahi[C::NT][C::KS], Alo[C::SLO ? C::NT : 1][C::KS];
+    bf16x8 Ahi[C::SLDS ? 1 : C::NT][C::KS], Alo[C::SLO ? C::NT : 1][C::KS];
     const float* Sh = a.S + (size_t)bh * D * D;
+    if (C::SLDS) {
+        // row pr = 16 T + m of the copy holds value channel co(T, m), the MFMA
+        // row order used below; element k is S[k][co] (zero past d)
+        for (int e = threadIdx.x; e < C::DP * C::DP; e += C::THREADS) {
+            const int k = e / C::DP, co = e % C::DP;   // coalesced over co
+            const float sv = (k < D && co < D) ? Sh[k * D + co] : 0.0f;
+            const int T = 2 * (co >> 5) + ((co >> 2) & 1);
+            const int m = (((co >> 3) & 3) << 2) | (co & 3);
+            st[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] = __builtin_bit_cast(uint16_t, (__bf16)sv);
+        }
+    }
 #pragma unroll
-    for (int T = 0; T < C::NT; ++T) {
+    for (int T = 0; T < (C::SLDS ? 0 : C::NT); ++T) {
         const int co = 32 * (T >> 1) + 8 * (n >> 2) + 4 * (T & 1) + (n & 3);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
@@ -135,12 +162,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             }
         }
     }
-    float zr[C::KS][8];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            zr[ks][e] = (C::DP == D || 32 * ks + 8 * g + e < D) ? a.z[(size_t)bh * D + 32 * ks + 8 * g + e] : 0.0f;
+    for (int c = threadIdx.x; c < C::DP; c += C::THREADS) zs[c] = c < D ? a.z[(size_t)bh * D + c] : 0.0f;
 
     int t_lo = 0, nt = 1;
     PairRef pr[C::KS][4];
@@ -180,7 +202,10 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 Pos3 ps;
                 if (ROPE) ps = token_pos((uint32_t)(a.g.n_offset + c0 + min(tl, len - 1)), t_lo, a.g);
                 float den = 0.0f;
-                bf16x8 Bq[C::KS], Bl[C::KS];
+                f32x4 acc[C::NT];
+#pragma unroll
+                for (int T = 0; T < C::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // one 32-channel k-step at a time: its B fragments, then its MFMAs
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
                     float x[8];
@@ -192,8 +217,12 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                         x[2 * i] = bf_lo(w);
                         x[2 * i + 1] = bf_hi(w);
                     }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) den = fmaf(x[e], zr[ks][e], den);
+                    const float4 za = *(const float4*)(zs + 32 * ks + 8 * g);
+                    const float4 zb = *(const float4*)(zs + 32 * ks + 8 * g + 4);
+                    den = fmaf(x[0], za.x, den); den = fmaf(x[1], za.y, den);
+                    den = fmaf(x[2], za.z, den); den = fmaf(x[3], za.w, den);
+                    den = fmaf(x[4], zb.x, den); den = fmaf(x[5], zb.y, den);
+                    den = fmaf(x[6], zb.z, den); den = fmaf(x[7], zb.w, den);
                     if (ROPE) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[ks][i], ps)]);
@@ -206,23 +235,23 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                         hw[i] = h;
                         lw[i] = l;
                     }
-                    Bq[ks] = __builtin_bit_cast(bf16x8, hw);
-                    Bl[ks] = __builtin_bit_cast(bf16x8, lw);
-                }
-                f32x4 acc[C::NT];
-#pragma unroll
-                for (int T = 0; T < C::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks)
+                    const bf16x8 Bq = __builtin_bit_cast(bf16x8, hw);
+                    const bf16x8 Bl = __builtin_bit_cast(bf16x8, lw);
 #pragma unroll
                     for (int T = 0; T < C::NT; ++T) {
                         // S q = S_hi q_hi + S_lo q_hi + S_hi q_lo  (S_lo q_lo ~ 2^-18 dropped)
-                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi[T][ks], Bq[ks], acc[T], 0, 0, 0);
+                        const bf16x8 A = C::SLDS ? *(const bf16x8*)(st + st_off<C::DP>(16 * T + n, 4 * ks + g))
+                                                 : Ahi[C::SLDS ? 0 : T][ks];
+                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bq, acc[T], 0, 0, 0);
                         if (C::SLO)
-                            acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo[C::SLO ? T : 0][ks], Bq[ks],
+                            acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo[C::SLO ? T : 0][ks], Bq,
                                                                              acc[T], 0, 0, 0);
-                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi[T][ks], Bl[ks], acc[T], 0, 0, 0);
+                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, acc[T], 0, 0, 0);
                     }
+                    // keep each k-step's LDS reads next to its MFMAs (hoisting
+                    // all of them would need 128 more registers a lane)
+                    if (C::SLDS) __builtin_amdgcn_sched_barrier(0);
+                }
                 den += __shfl_xor(den, 16);
                 den += __shfl_xor(den, 32);
                 den += a.eps;
