@@ -59,10 +59,26 @@ struct ApplyBf16Cfg {
     // d >= 112: S^T (bf16 hi) lives in LDS instead of registers (128 x 128
     // bf16 would take 128 registers a lane); MFMA A fragments are read from it
     static constexpr bool SLDS = DP > 64;
-    static constexpr int ZBYTES = DP * 4;                  // z, then S^T, then the RoPE table
+    // d = 64: Q and O pass through a per-wave LDS tile so that every global
+    // load / store instruction moves 8 whole 128-byte rows (the MFMA operand
+    // layout would touch 16 rows per instruction, half of each line).
+    static constexpr bool STG = D == 64;
+    static constexpr int RPI = 8;                          // rows per staged load / store
+    static constexpr int NI = UNIT / RPI;                  // staged loads per unit (= GR * KS)
+    static constexpr int ZBYTES = DP * 4;                  // z, S^T, staging, then the RoPE table
     static constexpr int SBYTES = SLDS ? DP * DP * 2 : 0;
-    static constexpr int FIXED = ZBYTES + SBYTES;
+    static constexpr int STGBYTES = STG ? NW * 2 * UNIT * D * 2 : 0;
+    static constexpr int FIXED = ZBYTES + SBYTES + STGBYTES;
+    static_assert(!STG || NI == GR * KS, "staged unit = register ring slot");
 };
+
+// Element offset of row r, 16-byte chunk c of a wave's staging tile
+// ([UNIT][64] bf16): chunk c of row r sits at c ^ f(r), which keeps both the
+// row-major 8-rows-per-instruction accesses and the MFMA-layout accesses
+// (16 consecutive rows at one chunk) free of bank conflicts.
+__device__ __forceinline__ int stg_off(int r, int c) {
+    return r * 64 + ((c ^ ((r ^ (r >> 3)) & 7)) << 3);
+}
 
 // Element offset of S^T row pr (= 16 T + m, see below), 16-byte chunk c, in
 // the LDS copy used at d >= 112: chunks are XOR-swizzled by row so that 16
@@ -87,6 +103,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     extern __shared__ __align__(16) unsigned char smem[];
     float* zs = (float*)smem;                        // [DP] z (zero above d)
     uint16_t* st = (uint16_t*)(smem + C::ZBYTES);    // [DP][DP] S^T hi (d >= 112)
+    uint16_t* stg = (uint16_t*)(smem + C::ZBYTES + C::SBYTES);  // [NW][Q, O][UNIT][D] (d = 64)
     float2* tab = (float2*)(smem + C::FIXED);
     __shared__ int q_next;  // next unit of this workgroup's chunk, in tokens
 
@@ -115,6 +132,13 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     };
     u32x4 qr[C::DEPTH][C::GR][C::KS];
     auto load_unit = [&](u32x4 (&q)[C::GR][C::KS], int u0) {
+        if (C::STG) {  // whole rows: lane -> row RPI*i + lane/8, 16-byte chunk lane%8
+#pragma unroll
+            for (int i = 0; i < C::NI; ++i)
+                q[i / C::KS][i % C::KS] =
+                    buf_load16(Qr, (uint32_t)((u0 + C::RPI * i + (lane >> 3)) * D + 8 * (lane & 7)) * 2u);
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < C::GR; ++r) {
             const int tl = u0 + 16 * r + n;
@@ -189,10 +213,26 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 break;
             }
             u32x4 qc[C::GR][C::KS];
+            uint16_t* wq = stg + wave * (2 * C::UNIT * D);  // this wave's Q tile, then its O tile
+            uint16_t* wo = wq + C::UNIT * D;
+            if (C::STG) {
+                // rows into LDS, then each lane reads its MFMA operand (token n, 8 channels)
 #pragma unroll
-            for (int r = 0; r < C::GR; ++r)
+                for (int i = 0; i < C::NI; ++i)
+                    *(u32x4*)(wq + stg_off(C::RPI * i + (lane >> 3), lane & 7)) = qr[s][i / C::KS][i % C::KS];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-                for (int ks = 0; ks < C::KS; ++ks) qc[r][ks] = qr[s][r][ks];
+                for (int r = 0; r < C::GR; ++r)
+#pragma unroll
+                    for (int ks = 0; ks < C::KS; ++ks) qc[r][ks] = *(const u32x4*)(wq + stg_off(16 * r + n, 4 * ks + g));
+            } else {
+#pragma unroll
+                for (int r = 0; r < C::GR; ++r)
+#pragma unroll
+                    for (int ks = 0; ks < C::KS; ++ks) qc[r][ks] = qr[s][r][ks];
+            }
             us[s] = grab();
             load_unit(qr[s], us[s]);
 
@@ -263,8 +303,21 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     o[1] = pack_bf16(acc[2 * sp][2] * inv, acc[2 * sp][3] * inv);
                     o[2] = pack_bf16(acc[2 * sp + 1][0] * inv, acc[2 * sp + 1][1] * inv);
                     o[3] = pack_bf16(acc[2 * sp + 1][2] * inv, acc[2 * sp + 1][3] * inv);
-                    if (C::DP == D || 32 * sp + 8 * g < D)
+                    if (C::STG)
+                        *(u32x4*)(wo + stg_off(16 * r + n, 4 * sp + g)) = o;
+                    else if (C::DP == D || 32 * sp + 8 * g < D)
                         buf_store16(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
+                }
+            }
+            if (C::STG) {  // whole rows out of LDS, one store per 8 rows
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int i = 0; i < C::NI; ++i) {
+                    const int row = C::RPI * i + (lane >> 3);
+                    buf_store16(*(const u32x4*)(wo + stg_off(row, lane & 7)), Or,
+                                (uint32_t)((u0 + row) * D + 8 * (lane & 7)) * 2u);
                 }
             }
         }
