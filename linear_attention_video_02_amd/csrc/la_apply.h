@@ -187,6 +187,21 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         }
     }
     for (int c = threadIdx.x; c < C::DP; c += C::THREADS) zs[c] = c < D ? a.z[(size_t)bh * D + c] : 0.0f;
+    // d <= 64: the denominator relu(q).z runs on the MFMA too, with z as an A
+    // tile of 16 identical rows (bf16 hi + lo) and the un-rotated relu(q) --
+    // exact in bf16 -- as B: every accumulator of a token's lanes is its sum.
+    bf16x8 Azh[C::SLDS ? 1 : C::KS], Azl[C::SLDS ? 1 : C::KS];
+    if (!C::SLDS) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float zv = a.z[(size_t)bh * D + 32 * ks + 8 * g + e];
+                const __bf16 hi = (__bf16)zv;
+                Azh[ks][e] = hi;
+                Azl[ks][e] = (__bf16)(zv - (float)hi);
+            }
+    }
 
     int t_lo = 0, nt = 1;
     PairRef pr[C::KS][4];
@@ -242,6 +257,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 Pos3 ps;
                 if (ROPE) ps = token_pos((uint32_t)(a.g.n_offset + c0 + min(tl, len - 1)), t_lo, a.g);
                 float den = 0.0f;
+                f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
                 f32x4 acc[C::NT];
 #pragma unroll
                 for (int T = 0; T < C::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -251,18 +267,26 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     float x[8];
                     // channels past d (d = 112) were loaded from the next row: zero them
                     const bool live = C::DP == D || 32 * ks + 8 * g < D;
+                    u32x4 u4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const uint32_t w = live ? relu_bf16x2(qc[r][ks][i]) : 0u;
+                        u4[i] = w;
                         x[2 * i] = bf_lo(w);
                         x[2 * i + 1] = bf_hi(w);
                     }
-                    const float4 za = *(const float4*)(zs + 32 * ks + 8 * g);
-                    const float4 zb = *(const float4*)(zs + 32 * ks + 8 * g + 4);
-                    den = fmaf(x[0], za.x, den); den = fmaf(x[1], za.y, den);
-                    den = fmaf(x[2], za.z, den); den = fmaf(x[3], za.w, den);
-                    den = fmaf(x[4], zb.x, den); den = fmaf(x[5], zb.y, den);
-                    den = fmaf(x[6], zb.z, den); den = fmaf(x[7], zb.w, den);
+                    if (C::SLDS) {
+                        const float4 za = *(const float4*)(zs + 32 * ks + 8 * g);
+                        const float4 zb = *(const float4*)(zs + 32 * ks + 8 * g + 4);
+                        den = fmaf(x[0], za.x, den); den = fmaf(x[1], za.y, den);
+                        den = fmaf(x[2], za.z, den); den = fmaf(x[3], za.w, den);
+                        den = fmaf(x[4], zb.x, den); den = fmaf(x[5], zb.y, den);
+                        den = fmaf(x[6], zb.z, den); den = fmaf(x[7], zb.w, den);
+                    } else {
+                        const bf16x8 Bu = __builtin_bit_cast(bf16x8, u4);
+                        dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Azh[C::SLDS ? 0 : ks], Bu, dacc, 0, 0, 0);
+                        dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Azl[C::SLDS ? 0 : ks], Bu, dacc, 0, 0, 0);
+                    }
                     if (ROPE) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[ks][i], ps)]);
@@ -292,8 +316,12 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     // all of them would need 128 more registers a lane)
                     if (C::SLDS) __builtin_amdgcn_sched_barrier(0);
                 }
-                den += __shfl_xor(den, 16);
-                den += __shfl_xor(den, 32);
+                if (C::SLDS) {
+                    den += __shfl_xor(den, 16);
+                    den += __shfl_xor(den, 32);
+                } else {
+                    den = dacc[0];
+                }
                 den += a.eps;
                 const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll

@@ -208,14 +208,16 @@ struct Pos3 {
     int t, h, w;
 };
 
+// All products here fit 24 bits (a grid whose RoPE table fits LDS has
+// gh * gw < 2^24), so they use the full-rate 24-bit multiplier.
 __device__ __forceinline__ Pos3 token_pos(uint32_t n, int t_lo, const LaGeom& g) {
     uint32_t t = fdiv(n, g.div_hw);
-    uint32_t r = n - t * (uint32_t)(g.gh * g.gw);
+    uint32_t r = n - __umul24(t, (uint32_t)(g.gh * g.gw));
     uint32_t h = fdiv(r, g.div_w);
     Pos3 p;
-    p.t = ((int)t - t_lo) * g.pt;
-    p.h = (int)h * g.ph;
-    p.w = (int)(r - h * (uint32_t)g.gw) * g.pw;
+    p.t = __mul24((int)t - t_lo, g.pt);
+    p.h = __mul24((int)h, g.ph);
+    p.w = __mul24((int)(r - __umul24(h, (uint32_t)g.gw)), g.pw);
     return p;
 }
 
