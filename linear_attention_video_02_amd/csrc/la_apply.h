@@ -333,18 +333,18 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     o[3] = pack_bf16(acc[2 * sp + 1][2] * inv, acc[2 * sp + 1][3] * inv);
                     if (C::STG)
                         *(u32x4*)(wo + stg_off(16 * r + n, 4 * sp + g)) = o;
-                    else if (C::DP == D || 32 * sp + 8 * g < D)
+                    else if (C::DP == D || 32 * sp + 8 * g < D)  // part-lines: let L2 merge them
                         buf_store16(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
                 }
             }
-            if (C::STG) {  // whole rows out of LDS, one store per 8 rows
+            if (C::STG) {  // whole rows out of LDS, one streaming store per 8 rows
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
                 for (int i = 0; i < C::NI; ++i) {
                     const int row = C::RPI * i + (lane >> 3);
-                    buf_store16(*(const u32x4*)(wo + stg_off(row, lane & 7)), Or,
+                    buf_store16_stream(*(const u32x4*)(wo + stg_off(row, lane & 7)), Or,
                                 (uint32_t)((u0 + row) * D + 8 * (lane & 7)) * 2u);
                 }
             }

@@ -385,7 +385,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
                 o[1] = pack_bf16(acc[2 * sp][2] * inv, acc[2 * sp][3] * inv);
                 o[2] = pack_bf16(acc[2 * sp + 1][0] * inv, acc[2 * sp + 1][1] * inv);
                 o[3] = pack_bf16(acc[2 * sp + 1][2] * inv, acc[2 * sp + 1][3] * inv);
-                buf_store16(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
+                buf_store16_stream(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
             }
         }
 

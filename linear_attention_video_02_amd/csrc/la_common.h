@@ -82,6 +82,18 @@ __device__ __forceinline__ void buf_store16(u32x4 v, BufRsrc r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
+// Streaming store for outputs nobody reads back soon (cache policy sc1 nt).
+// A default store leaves the line dirty in the memory-side Infinity Cache; it
+// is written to HBM later, while the next kernel streams its own inputs, and
+// slows that kernel down (a K/V read kernel after a copy: 83 us with default
+// stores, 47 us with these).  "nt" alone is pathological here: never use it
+// without sc1.  Only for stores that cover whole 128-byte lines: partial lines
+// written this way are not merged in L2 first (a d = 112 apply, whose rows
+// straddle lines, ran 75% slower).
+__device__ __forceinline__ void buf_store16_stream(u32x4 v, BufRsrc r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16 | 2);
+}
+
 // Workgroup barrier for an LDS hand-off only.  __syncthreads() also orders
 // global memory, which on gfx9 (loads and stores share vmcnt) drains every
 // prefetched load before each barrier; this one waits for LDS operations only.
