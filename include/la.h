@@ -37,9 +37,13 @@
  *    into t, h, w ranges of d/2 - 2*floor(d/6), floor(d/6), floor(d/6) pairs;
  *    pair k of an axis with P_a pairs turns by pos_a * 10000^(-k/P_a).
  *  - ws is a device workspace of at least la_workspace_bytes(B, H, N, d)
- *    bytes (scratch for per-workgroup partial states; no initialisation
- *    needed).  One workspace must not be used by two calls that may overlap
- *    in time (two streams): they would race on it.
+ *    bytes: per-workgroup partial states and one completion counter per
+ *    (batch, head).  Zero-fill it ONCE before its first use (e.g. right after
+ *    allocating it); every call that completes leaves the counters at zero
+ *    again, so no later call needs a fill.  A workspace with non-zero
+ *    counters gives wrong S/z (not a fault).  One workspace must not be used
+ *    by two calls that may overlap in time (two streams): they would race on
+ *    it.
  *  - All pointers must be 16-byte aligned.  O must not overlap Q, K, V, S or z.
  *  - stream is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues kernels: it never allocates, never synchronises, and returns as
@@ -129,8 +133,9 @@ LA_API int la_block_causal_step(const void* Q, const void* K, const void* V, voi
  * final state is not returned) or both non-NULL: the state before token 0 on
  * entry, the state after token N-1 on return.  bf16 and d = 64 only
  * (otherwise LA_E_UNSUPPORTED).  N = 0 returns LA_OK and leaves the carry as
- * it is.  ws: at least la_workspace_bytes(B, H, N, d) bytes, no
- * initialisation needed; it must not overlap O or the carry.  Every piece of
+ * it is.  ws: at least la_workspace_bytes(B, H, N, d) bytes (this call
+ * neither needs nor disturbs the zero counters); it must not overlap O or
+ * the carry.  Every piece of
  * the computation has a fixed order, so repeated calls give bitwise equal
  * results. */
 LA_API int la_token_causal(const void* Q, const void* K, const void* V, void* O,

@@ -126,7 +126,7 @@ _ws_cache: dict = {}
 
 
 def workspace(B: int, H: int, N: int, d: int, device):
-    """A workspace buffer, cached per (device, size); reusable on one stream."""
+    """A zero-filled workspace, cached per (device, size); reusable on one stream."""
     torch = _torch()
     nbytes = workspace_bytes(B, H, N, d)
     if nbytes == 0:
@@ -135,7 +135,7 @@ def workspace(B: int, H: int, N: int, d: int, device):
     key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device(), nbytes)
     ws = _ws_cache.get(key)
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 

@@ -21,6 +21,11 @@ constexpr size_t kLdsLimit = 160 * 1024; // gfx950 LDS per workgroup
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+int env_flag(const char* name, int dflt) {
+    const char* s = getenv(name);
+    return (s && *s) ? atoi(s) : dflt;
+}
+
 int env_int(const char* name, int dflt) {
     const char* s = getenv(name);
     if (!s || !*s) return dflt;
@@ -29,12 +34,13 @@ int env_int(const char* name, int dflt) {
 }
 
 struct WsLayout {
-    size_t partial, state, total;
+    size_t ticket, partial, state, total;
 };
 
 WsLayout ws_layout(int BH, int d) {
     WsLayout L;
-    L.partial = 0;
+    L.ticket = 0;
+    L.partial = align_up((size_t)BH * 4, 256);
     L.state = L.partial + align_up((size_t)BH * kMaxPartials * (d * d + d) * 4, 256);
     L.total = L.state + align_up((size_t)BH * (d * d + d) * 4, 256);
     return L;
@@ -279,22 +285,8 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     int rc = plan_state(g, d, dtype, &pl);
     if (rc != LA_OK) return rc;
     const WsLayout L = ws_layout(g.BH, d);
-    StateArgs a;
-    a.K = K;
-    a.V = V;
-    a.partial = (float*)((char*)ws + L.partial);
-    a.chunk = pl.chunk;
-    a.P = pl.P;
-    a.g = g;
-    const int threads = dtype != LA_BF16 ? 256
-                        : d == 32        ? StateBf16Cfg<32>::THREADS
-                        : d == 64        ? StateBf16Cfg<64>::THREADS
-                        : d == 112       ? StateBf16Cfg<112>::THREADS
-                                         : StateBf16Cfg<128>::THREADS;
-    rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
-    if (rc != LA_OK) return rc;
     CombineArgs c;
-    c.partial = a.partial;
+    c.partial = (float*)((char*)ws + L.partial);
     c.S_out = S_out;
     c.z_out = z_out;
     c.S_out2 = S_out2;
@@ -303,6 +295,23 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     c.z_carry = z_carry;
     c.P = pl.P;
     c.BH = g.BH;
+    const bool fused = dtype == LA_BF16 && env_flag("LA_STATE_FUSED", 1) != 0;
+    StateArgs a;
+    a.K = K;
+    a.V = V;
+    a.partial = (float*)((char*)ws + L.partial);
+    a.chunk = pl.chunk;
+    a.P = pl.P;
+    a.g = g;
+    a.ticket = fused ? (unsigned*)((char*)ws + L.ticket) : nullptr;
+    a.cmb = c;
+    const int threads = dtype != LA_BF16 ? 256
+                        : d == 32        ? StateBf16Cfg<32>::THREADS
+                        : d == 64        ? StateBf16Cfg<64>::THREADS
+                        : d == 112       ? StateBf16Cfg<112>::THREADS
+                                         : StateBf16Cfg<128>::THREADS;
+    rc = launch_kernel<StateArgs>(state_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
+    if (rc != LA_OK || fused) return rc;
     const int e4 = (d * d + d) / 4;
     return launch_kernel<CombineArgs>(combine_kernel(d), dim3((e4 + 255) / 256, g.BH), 0, st, c);
 }
@@ -377,6 +386,7 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     sa.chunk = ps.chunk;
     sa.P = ps.P;
     sa.g = g;
+    sa.ticket = nullptr;  // partials only: the prefix kernel reads them
     rc = launch_kernel<StateArgs>(state_kernel(d, LA_BF16, g.rope), dim3(ps.P * g.BH), ps.lds, st, sa,
                                   StateBf16Cfg<64>::THREADS);
     if (rc != LA_OK) return rc;

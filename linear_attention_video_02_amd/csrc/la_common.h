@@ -82,6 +82,13 @@ __device__ __forceinline__ void buf_store16(u32x4 v, BufRsrc r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
+// Device-coherent load (cache policy sc1, device scope): served from the
+// coherence point, never from a line another XCD's L2 may hold stale.  For
+// data other workgroups of the same kernel wrote with device-scope stores.
+__device__ __forceinline__ u32x4 buf_load16_dev(BufRsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+}
+
 // Streaming store for outputs nobody reads back soon (cache policy sc1 nt).
 // A default store leaves the line dirty in the memory-side Infinity Cache; it
 // is written to HBM later, while the next kernel streams its own inputs, and

@@ -3,27 +3,22 @@
 //
 //   S = sum_j RoPE(relu(K_j))^T V_j   (d x d, fp32)      z = sum_j relu(K_j)   (d, fp32)
 //
-// Work split: grid (P, B*H).  Workgroup p of head bh reduces the token chunk
-// [p*chunk, (p+1)*chunk) to a partial (S_p, z_p) in the workspace.  A second,
-// small kernel (la_state_combine_kernel) sums the P partials of each head in
-// the fixed order p = 0..P-1, adds the carried state when there is one
-// (block-causal mode, Eq. 3 / Algorithm 1) and writes S and z.  No atomics
-// and no in-kernel cross-workgroup signalling: the kernel boundary makes the
-// partials visible (an in-kernel device-scope fence per workgroup would write
-// back and invalidate a whole XCD L2 each time).  Results are bitwise
-// reproducible for a given shape.
+// Work split: P workgroups per (batch, head).  Workgroup p of head bh reduces
+// the token chunk [p*chunk, (p+1)*chunk) to a partial (S_p, z_p) in the
+// workspace.  Stage 2 sums the P partials of each head in the fixed order
+// p = 0..P-1, adds the carried state when there is one (block-causal mode,
+// Eq. 3 / Algorithm 1) and writes S and z.  Results are bitwise reproducible
+// for a given shape.  Stage 2 runs in one of two ways, with identical sums:
+//  - bf16 kernel, fused: the partials are written with device-scope stores
+//    and the last workgroup of a head to finish (a per-head counter in the
+//    workspace) does the sum.  No release fence: a device-scope fence per
+//    workgroup would write back a whole XCD L2 each time.
+//  - separate launch (la_state_combine_kernel): the kernel boundary makes
+//    the partials visible.  Used by the fp32 kernel, by the token-causal
+//    pass (its prefix kernel reads the partials) and when LA_STATE_FUSED=0.
 #pragma once
 
 #include "la_common.h"
-
-struct StateArgs {
-    const void* K;
-    const void* V;
-    float* partial;        // [BH][P][D*D + D]
-    int chunk;             // tokens per workgroup
-    int P;                 // workgroups per (batch, head)
-    LaGeom g;
-};
 
 struct CombineArgs {
     const float* partial;  // [BH][P][D*D + D]
@@ -35,6 +30,19 @@ struct CombineArgs {
     const float* z_carry;
     int P;
     int BH;
+};
+
+struct StateArgs {
+    const void* K;
+    const void* V;
+    float* partial;        // [BH][P][D*D + D]
+    int chunk;             // tokens per workgroup
+    int P;                 // workgroups per (batch, head)
+    LaGeom g;
+    // Stage 2 inside the bf16 kernel (ticket != null): the last workgroup of
+    // a head to finish sums that head's partials (see the kernel's end).
+    unsigned* ticket;      // [BH] counters, zero between calls
+    CombineArgs cmb;
 };
 
 // Stage 2: grid (ceil(E4 / 256), B*H), one float4 of (S, z) per thread.  Sums
@@ -342,6 +350,15 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
     }
 
     // ---- write this workgroup's partial (token group 0 holds the sums) ----
+    // In the fused mode the partials are device-coherent stores (sc1: written
+    // through to the agent-wide coherence point, not left in this XCD's L2).
+    const bool fused = a.ticket != nullptr;
+    auto put = [&](float* dst, float v) {
+        if (fused)
+            __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            *dst = v;
+    };
     constexpr int E = D * D + D;
     float* part = a.partial + ((size_t)bh * a.P + p) * E;
     if (tgrp == 0) {
@@ -351,7 +368,7 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
             for (int r = 0; r < 16; ++r) {
                 const int row = 32 * ctile + 8 * (r >> 2) + 4 * gq + (r & 3);
                 const int col = 32 * j + m;
-                if (C::DP == D || (row < D && col < D)) part[row * D + col] = acc[j][r];
+                if (C::DP == D || (row < D && col < D)) put(&part[row * D + col], acc[j][r]);
             }
     }
     // ---- z partial: threads sharing a channel block, summed in thread order ----
@@ -362,7 +379,55 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
     if (tid < D) {
         float sum = 0.0f;
         for (int r = 0; r < C::ROWS; ++r) sum += zr[((tid >> 3) + C::CH * r) * 8 + (tid & 7)];
-        part[D * D + tid] = sum;
+        put(&part[D * D + tid], sum);
+    }
+    if (!fused) return;
+
+    // ---- fused stage 2.  Every thread waits until its partial stores have
+    // completed (sc1 stores complete at the device coherence point), then one
+    // device-scope atomic per workgroup counts the finished partials of the
+    // head.  The workgroup that brings the count to P reads all P partials
+    // with device-coherent loads (sc1) and sums them in the fixed order
+    // p = 0..P-1 -- the same sums as the separate combine kernel.  No L2
+    // write-back or invalidate is needed: the partials never live in L2. ----
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unconstrained
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    lds_barrier();  // every thread's stores done; zr reads done (flag reuses zr[0])
+    int* flag = (int*)smem;
+    if (tid == 0)
+        *flag = __hip_atomic_fetch_add(&a.ticket[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (unsigned)(a.P - 1);
+    lds_barrier();
+    if (*flag) {
+        const CombineArgs& c = a.cmb;
+        constexpr int E4 = E / 4;  // S and z regions both hold whole float4s
+        const BufRsrc hp = make_rsrc(c.partial + (size_t)bh * c.P * E, (uint32_t)c.P * E * 4u);
+        for (int f = tid; f < E4; f += C::THREADS) {
+            f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int q0 = 0; q0 < c.P; q0 += 8) {
+                u32x4 v[8];  // eight partials' loads in flight, then added in order
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = buf_load16_dev(hp, (uint32_t)((q0 + u) * E4 + f) * 16u);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (q0 + u < c.P) s += __builtin_bit_cast(f32x4, v[u]);
+            }
+            const int e = 4 * f;
+            if (e < D * D) {
+                const size_t o = (size_t)bh * D * D + e;
+                if (c.S_carry) s = *(const f32x4*)(c.S_carry + o) + s;
+                *(f32x4*)(c.S_out + o) = s;
+                if (c.S_out2) *(f32x4*)(c.S_out2 + o) = s;
+            } else {
+                const size_t o = (size_t)bh * D + (e - D * D);
+                if (c.z_carry) s = *(const f32x4*)(c.z_carry + o) + s;
+                *(f32x4*)(c.z_out + o) = s;
+                if (c.z_out2) *(f32x4*)(c.z_out2 + o) = s;
+            }
+        }
+        // back to zero for the next call (kernels of one stream do not overlap)
+        if (tid == 0) __hip_atomic_store(&a.ticket[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -47,6 +47,33 @@ def test_determinism_bidirectional(la):
         assert torch.equal(S, S0) and torch.equal(z, z0), i
 
 
+@pytest.mark.parametrize("d", [32, 64, 112, 128])
+def test_fused_combine_matches_separate_launch(la, d, monkeypatch):
+    """The bf16 state kernel's in-kernel stage 2 (last workgroup of a head sums
+    the partials) and the separate combine launch give bitwise equal S and z,
+    also with a carry (block-causal), over repeated calls on one workspace."""
+    import torch
+    _, (tq, tk, tv) = _inputs(2, 6, 5000, d, "bf16", 17)
+    grid = (6, 23, 40)
+    qb, kb, vb = (t[:, :, 1000:2000].contiguous() for t in (tq, tk, tv))
+    res = {}
+    for fused in ("0", "1"):
+        monkeypatch.setenv("LA_STATE_FUSED", fused)
+        runs = []
+        for _ in range(3):
+            S, z = la.state_reduce(tk, tv, grid)
+            Sc = S.clone() * 0.5
+            zc = z.clone() * 0.5
+            la.block_causal_step(qb, kb, vb, Sc, zc, 5000, grid, 1000, 1, commit=True)
+            runs.append((S, z, Sc, zc))
+        torch.cuda.synchronize()
+        for r in runs[1:]:
+            assert all(torch.equal(x, y) for x, y in zip(r, runs[0])), fused
+        res[fused] = runs[0]
+    say(f"  d={d}: fused and separate stage 2 bitwise equal")
+    assert all(torch.equal(x, y) for x, y in zip(res["0"], res["1"]))
+
+
 def test_determinism_d128_fp32(la):
     import torch
     _, (tq, tk, tv) = _inputs(1, 4, 3000, 128, "fp32", 12)
