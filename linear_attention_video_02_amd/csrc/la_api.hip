@@ -88,20 +88,25 @@ LaGeom make_geom(int B, int H, int ntok, int n_offset, int d, int gt, int gh, in
         g.gw = gw;
         g.div_hw = make_fastdiv((uint32_t)gh * (uint32_t)gw);
         g.div_w = make_fastdiv((uint32_t)gw);
+        g.div_pt = make_fastdiv((uint32_t)g.pt);
+        g.div_ph = make_fastdiv((uint32_t)g.ph);
+        g.div_pw = make_fastdiv((uint32_t)g.pw);
     } else {
         g.gh = g.gw = 1;
         g.div_hw = make_fastdiv(1);
         g.div_w = make_fastdiv(1);
+        g.div_pt = g.div_ph = g.div_pw = make_fastdiv(1);
     }
     return g;
 }
 
-// Entries of the per-workgroup RoPE table for a chunk of `chunk` tokens.
+// 8-byte LDS slots of the per-workgroup RoPE table for a chunk of `chunk`
+// tokens, plus the d/2 frequencies stored after it while it is built.
 size_t table_entries(const LaGeom& g, int chunk) {
     if (!g.rope) return 0;
     const long long hw = (long long)g.gh * g.gw;
     const long long nt = (chunk + hw - 1) / hw + 1;   // frames one chunk can touch
-    return (size_t)(nt * g.pt + (long long)g.gh * g.ph + (long long)g.gw * g.pw);
+    return (size_t)(nt * g.pt + (long long)g.gh * g.ph + (long long)g.gw * g.pw + g.pt + g.ph + g.pw);
 }
 
 int state_fixed_lds(int d, int dtype) {

@@ -66,7 +66,9 @@ struct ApplyBf16Cfg {
     static constexpr int RPI = 8;                          // rows per staged load / store
     static constexpr int NI = UNIT / RPI;                  // staged loads per unit (= GR * KS)
     static constexpr int ZBYTES = DP * 4;                  // z, S^T, staging, then the RoPE table
-    static constexpr int SBYTES = SLDS ? DP * DP * 2 : 0;
+    // d <= 64: S^T in fp32 (row stride d + 4), read once into the fragments
+    static constexpr int SROW = D + 4;
+    static constexpr int SBYTES = SLDS ? DP * DP * 2 : D * SROW * 4;
     static constexpr int STGBYTES = STG ? NW * 2 * UNIT * D * 2 : 0;
     static constexpr int FIXED = ZBYTES + SBYTES + STGBYTES;
     static_assert(!STG || NI == GR * KS, "staged unit = register ring slot");
@@ -147,6 +149,30 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 q[r][ks] = buf_load16(Qr, (uint32_t)(tl * D + 32 * ks + 8 * g) * 2u);
         }
     };
+    // d <= 64: S and this lane's z entries are fetched before the first Q
+    // loads.  Loads return in order, so fetched after them the conversion
+    // below (and every wave's first MFMA) would wait until all of the first
+    // units of Q had arrived -- at kernel start, when every CU asks at once,
+    // that is several microseconds.  S comes in with coalesced 16-byte loads
+    // (a lane's fragment entries lie in 8 different rows of S, which as
+    // single-word global loads would be 64 per lane) and goes to LDS
+    // transposed, where each lane reads its fragments as 16-byte rows.
+    const float* Sh = a.S + (size_t)bh * D * D;
+    constexpr int S4 = C::SLDS ? 1 : (D * D / 4 + C::THREADS - 1) / C::THREADS;  // float4s a thread
+    f32x4 sraw[S4];
+    float zraw[C::SLDS ? 1 : C::KS][8];
+    if (!C::SLDS) {
+#pragma unroll
+        for (int i = 0; i < S4; ++i) {
+            const int f = threadIdx.x + i * C::THREADS;
+            if (f < D * D / 4) sraw[i] = *(const f32x4*)(Sh + 4 * f);
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zraw[ks][e] = a.z[(size_t)bh * D + 32 * ks + 8 * g + e];
+        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of Q's
+    }
     // first DEPTH units of each wave: fixed, so their loads go out before the
     // prologue work
     const int wave = threadIdx.x >> 6;
@@ -159,7 +185,18 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 
     // S^T fragments (hi/lo bf16) and this lane's z entries
     bf16x8 Ahi[C::SLDS ? 1 : C::NT][C::KS], Alo[C::SLO ? C::NT : 1][C::KS];
-    const float* Sh = a.S + (size_t)bh * D * D;
+    float* sT = (float*)st;  // d <= 64: [D][SROW] fp32, sT[co][ci] = S[ci][co]
+    if (!C::SLDS) {
+#pragma unroll
+        for (int i = 0; i < S4; ++i) {
+            const int f = threadIdx.x + i * C::THREADS;
+            if (f < D * D / 4) {
+                const int ci = f / (D / 4), co = 4 * (f % (D / 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sT[(co + j) * C::SROW + ci] = sraw[i][j];
+            }
+        }
+    }
     if (C::SLDS) {
         // row pr = 16 T + m of the copy holds value channel co(T, m), the MFMA
         // row order used below; element k is S[k][co] (zero past d)
@@ -171,22 +208,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             st[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] = __builtin_bit_cast(uint16_t, (__bf16)sv);
         }
     }
-#pragma unroll
-    for (int T = 0; T < (C::SLDS ? 0 : C::NT); ++T) {
-        const int co = 32 * (T >> 1) + 8 * (n >> 2) + 4 * (T & 1) + (n & 3);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int ci = 32 * ks + 8 * g + e;
-                const float sv = (C::DP == D || (ci < D && co < D)) ? Sh[ci * D + co] : 0.0f;
-                const __bf16 hi = (__bf16)sv;
-                Ahi[T][ks][e] = hi;
-                if (C::SLO) Alo[C::SLO ? T : 0][ks][e] = (__bf16)(sv - (float)hi);
-            }
-        }
-    }
-    for (int c = threadIdx.x; c < C::DP; c += C::THREADS) zs[c] = c < D ? a.z[(size_t)bh * D + c] : 0.0f;
+    if (C::SLDS)  // (d <= 64 sums the denominator on the MFMA from registers)
+        for (int c = threadIdx.x; c < C::DP; c += C::THREADS) zs[c] = c < D ? a.z[(size_t)bh * D + c] : 0.0f;
     // d <= 64: the denominator relu(q).z runs on the MFMA too, with z as an A
     // tile of 16 identical rows (bf16 hi + lo) and the un-rotated relu(q) --
     // exact in bf16 -- as B: every accumulator of a token's lanes is its sum.
@@ -196,7 +219,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float zv = a.z[(size_t)bh * D + 32 * ks + 8 * g + e];
+                const float zv = zraw[ks][e];
                 const __bf16 hi = (__bf16)zv;
                 Azh[ks][e] = hi;
                 Azl[ks][e] = (__bf16)(zv - (float)hi);
@@ -216,7 +239,25 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             for (int i = 0; i < 4; ++i)
                 pr[ks][i] = pair_ref((C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g + i : 0, nt, a.g);
     }
-    lds_barrier();  // RoPE table and queue head visible
+    lds_barrier();  // RoPE table, S^T copy and queue head visible
+    // this lane's S^T fragments: value channel co(T, n), key channels
+    // 32 ks + 8 g .. +7 -- two 16-byte LDS reads each
+#pragma unroll
+    for (int T = 0; T < (C::SLDS ? 0 : C::NT); ++T) {
+        const int co = 32 * (T >> 1) + 8 * (n >> 2) + 4 * (T & 1) + (n & 3);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const f32x4 v0 = *(const f32x4*)(sT + co * C::SROW + 32 * ks + 8 * g);
+            const f32x4 v1 = *(const f32x4*)(sT + co * C::SROW + 32 * ks + 8 * g + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sv = e < 4 ? v0[e] : v1[e - 4];
+                const __bf16 hi = (__bf16)sv;
+                Ahi[T][ks][e] = hi;
+                if (C::SLO) Alo[C::SLO ? T : 0][ks][e] = (__bf16)(sv - (float)hi);
+            }
+        }
+    }
 
     bool more = true;
     while (more) {

@@ -59,6 +59,7 @@ struct LaGeom {
     int gh, gw;    // grid plane (gt only matters for validation)
     int pt, ph, pw;  // rotation pairs per axis
     FastDiv div_hw, div_w;
+    FastDiv div_pt, div_ph, div_pw;  // by the pair counts (RoPE table build)
 };
 
 // ---------------------------------------------------------------------------
@@ -185,23 +186,44 @@ __device__ __forceinline__ int rope_table_entries(int nt, const LaGeom& g) {
     return nt * g.pt + g.gh * g.ph + g.gw * g.pw;
 }
 
+// The table is followed in LDS by d/2 doubles of scratch (the frequencies),
+// which the caller's LDS size must include.  Called by every thread of the
+// workgroup; contains a workgroup barrier on LDS.
 __device__ inline void build_rope_table(float2* tab, int t_lo, int nt, const LaGeom& g) {
     const double kLog2Base = 13.287712379549449;      // log2(10000)
     const double kInv2Pi = 0.15915494309189535;
     const double k2PiHi = 6.283185307179586;
     const double k2PiLo = 2.4492935982947064e-16;
     const int nT = nt * g.pt, nH = g.gh * g.ph, nW = g.gw * g.pw;
-    for (int i = threadIdx.x; i < nT + nH + nW; i += blockDim.x) {
-        int pos, k, np;
-        if (i < nT) {
-            pos = t_lo + i / g.pt; k = i % g.pt; np = g.pt;
-        } else if (i < nT + nH) {
-            int j = i - nT; pos = j / g.ph; k = j % g.ph; np = g.ph;
+    // the frequency of each pair, once: pairs [0, pt) of axis t, then h, then w
+    double* omg = (double*)(tab + nT + nH + nW);
+    for (int i = threadIdx.x; i < g.pt + g.ph + g.pw; i += blockDim.x) {
+        int k, np;
+        if (i < g.pt) {
+            k = i; np = g.pt;
+        } else if (i < g.pt + g.ph) {
+            k = i - g.pt; np = g.ph;
         } else {
-            int j = i - nT - nH; pos = j / g.pw; k = j % g.pw; np = g.pw;
+            k = i - g.pt - g.ph; np = g.pw;
         }
-        double omega = exp2(-((double)k / (double)np) * kLog2Base);
-        double ang = (double)pos * omega;
+        omg[i] = exp2(-((double)k / (double)np) * kLog2Base);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    for (int i = threadIdx.x; i < nT + nH + nW; i += blockDim.x) {
+        int pos, j;  // position on the entry's axis, index of its frequency
+        if (i < nT) {
+            const int r = (int)fdiv((uint32_t)i, g.div_pt);
+            pos = t_lo + r; j = i - r * g.pt;
+        } else if (i < nT + nH) {
+            const int r = i - nT;
+            pos = (int)fdiv((uint32_t)r, g.div_ph); j = g.pt + r - pos * g.ph;
+        } else {
+            const int r = i - nT - nH;
+            pos = (int)fdiv((uint32_t)r, g.div_pw); j = g.pt + g.ph + r - pos * g.pw;
+        }
+        double ang = (double)pos * omg[j];
         double q = rint(ang * kInv2Pi);
         double r = fma(-q, k2PiHi, ang);
         r = fma(-q, k2PiLo, r);
