@@ -21,14 +21,20 @@ struct ApplyArgs {
 };
 
 // ---------------------------------------------------------------------------
-// bf16: MFMA v_mfma_f32_16x16x32_bf16 with C = S^T . RoPE(relu Q)^T, so that
-// every accumulator a lane holds belongs to one token (column n = lane % 16)
-// and the B operand -- 8 consecutive channels of one token -- is a plain
-// 16-byte load of Q.  S^T is held in registers for the whole workgroup as
-// bf16 hi + lo parts (S = hi + lo to ~2^-17; hi only at d = 128), and
-// RoPE(relu Q) is split the same way (hi truncated, lo rounded), so the
-// product S q is formed to ~2^-16 (a single bf16 rounding of RoPE(relu Q) costs up to ~1% in rows
-// whose sum over channels cancels).
+// bf16: MFMA with C = S^T . RoPE(relu Q)^T, so that every accumulator a lane
+// holds belongs to one token (column n = lane % 16) and the B operand -- 8
+// consecutive channels of one token -- is a plain 16-byte load of Q.
+// Numerator: v_mfma_f32_16x16x32_f16 on fp16 operands.  S^T is scaled by a
+// power of two per head (its largest entry to [2^13, 2^14)) and rounded to
+// fp16; RoPE(relu Q) is rounded to fp16 as it is (fp16's 11-bit significand
+// makes one product per k-step as accurate as three bf16 hi/lo products --
+// a single bf16 rounding of either factor costs up to ~1% in rows whose sum
+// over channels cancels).  A group of 16 tokens whose relu(Q) values are
+// not all within [2^-6, 2^14) (or zero) -- where fp16 could overflow or lose
+// precision -- is scaled by a power of two per token first; powers of two
+// are exact and are undone after the sum.  Denominator: un-rotated relu(Q),
+// exact in bf16, against z (bf16 hi + lo on the MFMA at d <= 64, fp32 FMA
+// at d >= 112).
 //
 // Lane (n = lane % 16, g = lane / 16) handles token n of a 16-token group and
 // the key channels 32*ks + 8*g .. +7, ks = 0 .. d/32 - 1.  Output tile T (16
@@ -52,12 +58,8 @@ struct ApplyBf16Cfg {
     static constexpr int GR = D <= 64 ? 2 : 1;   // 16-token groups per unit of work
     static constexpr int UNIT = 16 * GR;         // tokens a wave takes from the queue at a time
     static constexpr int DEPTH = D <= 64 ? 3 : 2;  // units of Q in flight per wave
-    // S as bf16 hi + lo (to ~2^-17) needs d*d/32 registers per lane: 128 at
-    // d = 64, 512 at d = 128.  At d = 128 only the hi part is held (S rounded to
-    // bf16, relative error 2^-9 per entry).
-    static constexpr bool SLO = D <= 64;
-    // d >= 112: S^T (bf16 hi) lives in LDS instead of registers (128 x 128
-    // bf16 would take 128 registers a lane); MFMA A fragments are read from it
+    // d >= 112: S^T (fp16) lives in LDS instead of registers (128 x 128
+    // fp16 would take 128 registers a lane); MFMA A fragments are read from it
     static constexpr bool SLDS = DP > 64;
     // d = 64: Q and O pass through a per-wave LDS tile so that every global
     // load / store instruction moves 8 whole 128-byte rows (the MFMA operand
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     uint16_t* stg = (uint16_t*)(smem + C::ZBYTES + C::SBYTES);  // [NW][Q, O][UNIT][D] (d = 64)
     float2* tab = (float2*)(smem + C::FIXED);
     __shared__ int q_next;  // next unit of this workgroup's chunk, in tokens
+    __shared__ float smax[C::NW];  // per-wave max |S|
 
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
@@ -183,9 +186,10 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         load_unit(qr[s], us[s]);
     }
 
-    // S^T fragments (hi/lo bf16) and this lane's z entries
-    bf16x8 Ahi[C::SLDS ? 1 : C::NT][C::KS], Alo[C::SLO ? C::NT : 1][C::KS];
+    // S^T fragments (fp16, scaled by 2^-eS) and this lane's z entries
+    f16x8 A16[C::SLDS ? 1 : C::NT][C::KS];
     float* sT = (float*)st;  // d <= 64: [D][SROW] fp32, sT[co][ci] = S[ci][co]
+    float amax = 0.0f;       // this thread's largest |S| entry
     if (!C::SLDS) {
 #pragma unroll
         for (int i = 0; i < S4; ++i) {
@@ -193,19 +197,43 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             if (f < D * D / 4) {
                 const int ci = f / (D / 4), co = 4 * (f % (D / 4));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sT[(co + j) * C::SROW + ci] = sraw[i][j];
+                for (int j = 0; j < 4; ++j) {
+                    sT[(co + j) * C::SROW + ci] = sraw[i][j];
+                    amax = fmaxf(amax, fabsf(sraw[i][j]));
+                }
             }
         }
+    } else {
+        for (int e = threadIdx.x; e < D * D; e += C::THREADS) amax = fmaxf(amax, fabsf(Sh[e]));
     }
+    amax = wave_max(amax);
+    if (lane == 0) smax[wave] = amax;
+    // eS: the head's largest |S| times 2^-eS lies in [2^13, 2^14) (read after
+    // a barrier that follows the smax writes)
+    auto head_scale = [&]() -> int {
+        float hmax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) hmax = fmaxf(hmax, smax[w]);
+        int e = 0;
+        if (hmax > 0.0f) {
+            (void)frexpf(hmax, &e);
+            e -= 14;
+        }
+        return e;
+    };
+    int eS = 0;
     if (C::SLDS) {
+        lds_barrier();
+        eS = head_scale();
         // row pr = 16 T + m of the copy holds value channel co(T, m), the MFMA
-        // row order used below; element k is S[k][co] (zero past d)
+        // row order used below; element k is S[k][co] 2^-eS (zero past d)
         for (int e = threadIdx.x; e < C::DP * C::DP; e += C::THREADS) {
             const int k = e / C::DP, co = e % C::DP;   // coalesced over co
             const float sv = (k < D && co < D) ? Sh[k * D + co] : 0.0f;
             const int T = 2 * (co >> 5) + ((co >> 2) & 1);
             const int m = (((co >> 3) & 3) << 2) | (co & 3);
-            st[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] = __builtin_bit_cast(uint16_t, (__bf16)sv);
+            st[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] =
+                __builtin_bit_cast(uint16_t, (_Float16)ldexpf(sv, -eS));
         }
     }
     if (C::SLDS)  // (d <= 64 sums the denominator on the MFMA from registers)
@@ -239,7 +267,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             for (int i = 0; i < 4; ++i)
                 pr[ks][i] = pair_ref((C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g + i : 0, nt, a.g);
     }
-    lds_barrier();  // RoPE table, S^T copy and queue head visible
+    lds_barrier();  // RoPE table, S^T copy, per-wave max |S| and queue head visible
+    if (!C::SLDS) eS = head_scale();
     // this lane's S^T fragments: value channel co(T, n), key channels
     // 32 ks + 8 g .. +7 -- two 16-byte LDS reads each
 #pragma unroll
@@ -250,12 +279,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             const f32x4 v0 = *(const f32x4*)(sT + co * C::SROW + 32 * ks + 8 * g);
             const f32x4 v1 = *(const f32x4*)(sT + co * C::SROW + 32 * ks + 8 * g + 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float sv = e < 4 ? v0[e] : v1[e - 4];
-                const __bf16 hi = (__bf16)sv;
-                Ahi[T][ks][e] = hi;
-                if (C::SLO) Alo[C::SLO ? T : 0][ks][e] = (__bf16)(sv - (float)hi);
-            }
+            for (int e = 0; e < 8; ++e) A16[T][ks][e] = (_Float16)ldexpf(e < 4 ? v0[e] : v1[e - 4], -eS);
         }
     }
 
@@ -302,19 +326,39 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 f32x4 acc[C::NT];
 #pragma unroll
                 for (int T = 0; T < C::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // relu(Q) of the group (channels past d, loaded from the next
+                // row at d = 112, are zeroed), and whether any lane holds a
+                // value fp16 cannot carry exactly enough: then every token of
+                // the group is scaled by 2^sc, sc = 13 - (exponent of its
+                // largest relu(Q) value)
+                u32x4 w4[C::KS];
+                uint32_t m16 = 0;
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    const bool live = C::DP == D || 32 * ks + 8 * g < D;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w4[ks][i] = live ? relu_bf16x2(qc[r][ks][i]) : 0u;
+                    const uint32_t mk = max_u16x8(w4[ks]);
+                    m16 = mk > m16 ? mk : m16;
+                }
+                // bf16 bit patterns of 2^-6 and 2^14
+                const bool odd = m16 != 0 && (m16 < 0x3C80u || m16 >= 0x4680u);
+                const bool scaled = __builtin_amdgcn_ballot_w64(odd) != 0;
+                int sc = 0;
+                if (scaled) {
+                    uint32_t tm = m16;
+                    tm = max(tm, (uint32_t)__shfl_xor((int)tm, 16));
+                    tm = max(tm, (uint32_t)__shfl_xor((int)tm, 32));
+                    sc = tm != 0 ? 13 - ((int)(tm >> 7) - 127) : 0;
+                }
                 // one 32-channel k-step at a time: its B fragments, then its MFMAs
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
                     float x[8];
-                    // channels past d (d = 112) were loaded from the next row: zero them
-                    const bool live = C::DP == D || 32 * ks + 8 * g < D;
-                    u32x4 u4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t w = live ? relu_bf16x2(qc[r][ks][i]) : 0u;
-                        u4[i] = w;
-                        x[2 * i] = bf_lo(w);
-                        x[2 * i + 1] = bf_hi(w);
+                        x[2 * i] = bf_lo(w4[ks][i]);
+                        x[2 * i + 1] = bf_hi(w4[ks][i]);
                     }
                     if (C::SLDS) {
                         const float4 za = *(const float4*)(zs + 32 * ks + 8 * g);
@@ -324,34 +368,27 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                         den = fmaf(x[4], zb.x, den); den = fmaf(x[5], zb.y, den);
                         den = fmaf(x[6], zb.z, den); den = fmaf(x[7], zb.w, den);
                     } else {
-                        const bf16x8 Bu = __builtin_bit_cast(bf16x8, u4);
+                        const bf16x8 Bu = __builtin_bit_cast(bf16x8, w4[ks]);
                         dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Azh[C::SLDS ? 0 : ks], Bu, dacc, 0, 0, 0);
                         dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Azl[C::SLDS ? 0 : ks], Bu, dacc, 0, 0, 0);
+                    }
+                    if (scaled) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] = ldexpf(x[e], sc);
                     }
                     if (ROPE) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[ks][i], ps)]);
                     }
-                    u32x4 hw, lw;
+                    u32x4 hw;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        uint32_t h, l;
-                        split_bf16x2(x[2 * i], x[2 * i + 1], h, l);
-                        hw[i] = h;
-                        lw[i] = l;
-                    }
-                    const bf16x8 Bq = __builtin_bit_cast(bf16x8, hw);
-                    const bf16x8 Bl = __builtin_bit_cast(bf16x8, lw);
+                    for (int i = 0; i < 4; ++i) hw[i] = pack_f16(x[2 * i], x[2 * i + 1]);
+                    const f16x8 Bq = __builtin_bit_cast(f16x8, hw);
 #pragma unroll
                     for (int T = 0; T < C::NT; ++T) {
-                        // S q = S_hi q_hi + S_lo q_hi + S_hi q_lo  (S_lo q_lo ~ 2^-18 dropped)
-                        const bf16x8 A = C::SLDS ? *(const bf16x8*)(st + st_off<C::DP>(16 * T + n, 4 * ks + g))
-                                                 : Ahi[C::SLDS ? 0 : T][ks];
-                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bq, acc[T], 0, 0, 0);
-                        if (C::SLO)
-                            acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo[C::SLO ? T : 0][ks], Bq,
-                                                                             acc[T], 0, 0, 0);
-                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bl, acc[T], 0, 0, 0);
+                        const f16x8 A = C::SLDS ? *(const f16x8*)(st + st_off<C::DP>(16 * T + n, 4 * ks + g))
+                                                : A16[C::SLDS ? 0 : T][ks];
+                        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq, acc[T], 0, 0, 0);
                     }
                     // keep each k-step's LDS reads next to its MFMAs (hoisting
                     // all of them would need 128 more registers a lane)
@@ -364,7 +401,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     den = dacc[0];
                 }
                 den += a.eps;
-                const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+                // undo the scalings: S by 2^-eS, the group's tokens by 2^sc
+                const float inv = den > 0.0f ? ldexpf(1.0f / den, eS - sc) : 0.0f;
 #pragma unroll
                 for (int sp = 0; sp < C::NT / 2; ++sp) {
                     u32x4 o;

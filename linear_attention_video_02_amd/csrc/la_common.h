@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
@@ -158,6 +159,37 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uin
     const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
     hi = __builtin_amdgcn_perm(ub, ua, 0x07060302u);  // high halves: a in bits 0-15, b in 16-31
     lo = pack_bf16(a - __uint_as_float(ua & 0xffff0000u), b - __uint_as_float(ub & 0xffff0000u));
+}
+
+// two floats -> packed fp16 pair, round to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+    f16x2 v;
+    v[0] = (_Float16)a;
+    v[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Largest of the 4 bf16 pairs (8 values) of a u32x4, compared as unsigned
+// 16-bit integers -- which orders non-negative bf16 values by magnitude.
+// The words are copied to scalars before the bit casts: this compiler turns
+// __builtin_bit_cast of a vector-element expression (w[1]) into a cast of
+// element 0.
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ __forceinline__ uint32_t max_u16x8(u32x4 w) {
+    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+    u16x2 m = __builtin_elementwise_max(as_u16x2(w0), as_u16x2(w1));
+    m = __builtin_elementwise_max(m, as_u16x2(w2));
+    m = __builtin_elementwise_max(m, as_u16x2(w3));
+    return m[0] > m[1] ? m[0] : m[1];
+}
+
+// wave-wide maximum of a float (every lane gets it)
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
 }
 
 __device__ __forceinline__ float bf16_round(float a) {

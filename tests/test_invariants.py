@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from _gpu import assert_close, host, say, upload
-from linear_attention_video_02_amd.inputs import make_qkv
+from linear_attention_video_02_amd.inputs import make_qkv, round_to_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,38 @@ def test_fused_combine_matches_separate_launch(la, d, monkeypatch):
         res[fused] = runs[0]
     say(f"  d={d}: fused and separate stage 2 bitwise equal")
     assert all(torch.equal(x, y) for x, y in zip(res["0"], res["1"]))
+
+
+def oracle_bf16(x):
+    """x rounded to bf16 values (float32 array), as the GPU receives it."""
+    return round_to_bf16(np.asarray(x, dtype=np.float32))
+
+
+@pytest.mark.parametrize("d", [32, 64, 112, 128])
+def test_query_magnitudes(la, d):
+    """The bf16 apply rounds RoPE(relu Q) to fp16 after scaling any 16-token
+    group that holds a relu(Q) value outside [2^-6, 2^14) by a power of two
+    per token.  Queries scaled by 1e-20 .. 1e20, and groups mixing tiny,
+    ordinary and huge tokens, must match the oracle like ordinary ones."""
+    import torch
+    N, grid = 700, (2, 20, 20)
+    q, k, v = make_qkv(1, 2, N, d, "bf16", seed=23)
+    ref_eps = 1e-6
+    for scale in (1e-20, 1e-5, 1e-2, 1.0, 3e4, 1e6, 1e20):
+        qs = oracle_bf16(q * scale)
+        out = la.bidirectional(upload(qs, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, ref_eps)
+        torch.cuda.synchronize()
+        o = host(out)
+        assert np.all(np.isfinite(o)), scale
+        assert_close(o, oracle.bidirectional(qs, k, v, grid, ref_eps), "bf16", f"d={d} Q x {scale:g}")
+    # every token of a group at its own magnitude
+    mags = np.array([1e-30, 1e-9, 1e-3, 0.5, 1.0, 7.0, 2e4, 1e9, 1e30], dtype=np.float64)
+    qm = oracle_bf16(q * mags[np.arange(N) % len(mags)][None, None, :, None])
+    out = la.bidirectional(upload(qm, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, ref_eps)
+    torch.cuda.synchronize()
+    o = host(out)
+    assert np.all(np.isfinite(o))
+    assert_close(o, oracle.bidirectional(qm, k, v, grid, ref_eps), "bf16", f"d={d} mixed token magnitudes")
 
 
 def test_determinism_d128_fp32(la):
