@@ -36,8 +36,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-STATE_KERNELS = ("la_state_bf16_kernel", "la_state_combine_kernel")
+# The bf16 state pass is one launch (its last workgroup per head sums the
+# partials); with LA_STATE_FUSED=0 a separate combine launch follows it.
+STATE_KERNELS = ("la_state_bf16_kernel",)
+COMBINE_KERNEL = "la_state_combine_kernel"
 APPLY_KERNELS = ("la_apply_bf16_kernel",)
+OUR_KERNELS = STATE_KERNELS + (COMBINE_KERNEL,) + APPLY_KERNELS
 CALIB_KERNEL = "MulFunctor"   # torch's elementwise o = q * 1: a plain copy of known size
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_720p5s.json")
 
@@ -170,7 +174,7 @@ def _find(path, suffix):
 
 
 def _short(name):
-    for k in STATE_KERNELS + APPLY_KERNELS:
+    for k in OUR_KERNELS:
         if k + "<" in name or name.startswith(k):
             return k
     if CALIB_KERNEL in name:
@@ -183,9 +187,8 @@ def summarize_trace(trace_dir, command, out_path):
     import csv
     rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    la = [r for r in rows if _short(r["Kernel_Name"]) in STATE_KERNELS + APPLY_KERNELS]
-    # the timed steps are the last `steps` state/combine/apply triples
-    steps = len(la) // 3
+    la = [r for r in rows if _short(r["Kernel_Name"]) in OUR_KERNELS]
+    steps = sum(1 for r in la if _short(r["Kernel_Name"]) in APPLY_KERNELS)
     dur = {}
     for r in la:
         dur.setdefault(_short(r["Kernel_Name"]), []).append(
@@ -197,26 +200,29 @@ def summarize_trace(trace_dir, command, out_path):
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for st in stats:
         k = _short(st["Name"])
-        if k in STATE_KERNELS + APPLY_KERNELS:
+        if k in OUR_KERNELS:
             lines.append(f"| {k} | {st['Calls']} | {float(st['AverageNs']) / 1e3:.1f} | "
                          f"{float(st['MinNs']) / 1e3:.1f} | {float(st['MaxNs']) / 1e3:.1f} |")
-    # gaps inside a step, from the trace: state end -> combine start -> apply start
-    gaps = []
-    for i in range(len(la) - 2):
-        a, b, c = (_short(la[j]["Kernel_Name"]) for j in (i, i + 1, i + 2))
-        if (a, b, c) == STATE_KERNELS + APPLY_KERNELS:
-            gaps.append(((int(la[i + 1]["Start_Timestamp"]) - int(la[i]["End_Timestamp"])) / 1e3,
-                         (int(la[i + 2]["Start_Timestamp"]) - int(la[i + 1]["End_Timestamp"])) / 1e3,
-                         (int(la[i + 2]["End_Timestamp"]) - int(la[i]["Start_Timestamp"])) / 1e3,
-                         (int(la[i + 1]["End_Timestamp"]) - int(la[i]["Start_Timestamp"])) / 1e3))
-    if gaps:
-        n = len(gaps)
+    # per step, from the trace: state kernel start .. (combine end) .. apply end
+    t = lambda r, k: int(r[k]) / 1e3
+    steps_ = []
+    for i, r in enumerate(la):
+        if _short(r["Kernel_Name"]) not in STATE_KERNELS:
+            continue
+        j = i + 1
+        while j < len(la) and _short(la[j]["Kernel_Name"]) == COMBINE_KERNEL:
+            j += 1
+        if j < len(la) and _short(la[j]["Kernel_Name"]) in APPLY_KERNELS:
+            pass_end = t(la[j - 1], "End_Timestamp")
+            steps_.append((pass_end - t(r, "Start_Timestamp"), t(la[j], "Start_Timestamp") - pass_end,
+                           t(la[j], "End_Timestamp") - t(r, "Start_Timestamp")))
+    if steps_:
+        n = len(steps_)
         lines += ["", f"From the trace, over {n} steps (state kernel start to apply kernel end):", "",
-                  f"- state pass (state kernel start to combine kernel end): "
-                  f"{sum(g[3] for g in gaps) / n:.1f} us",
-                  f"- gap state -> combine: {sum(g[0] for g in gaps) / n:.2f} us, "
-                  f"combine -> apply: {sum(g[1] for g in gaps) / n:.2f} us",
-                  f"- whole step: {sum(g[2] for g in gaps) / n:.1f} us"]
+                  f"- state pass (state kernel start to its last launch's end): "
+                  f"{sum(g[0] for g in steps_) / n:.1f} us",
+                  f"- gap state pass -> apply: {sum(g[1] for g in steps_) / n:.2f} us",
+                  f"- whole step: {sum(g[2] for g in steps_) / n:.1f} us"]
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -250,7 +256,7 @@ def summarize_pmc(fetch_dir, write_dir, commands, out_json, out_md, src_hash, te
     w_scale = tensor_bytes / write[cal]
     algo = {"la_state_bf16_kernel": 2 * tensor_bytes, "la_apply_bf16_kernel": 2 * tensor_bytes}
     kernels = {}
-    for k in STATE_KERNELS + APPLY_KERNELS:
+    for k in OUR_KERNELS:
         if k in fetch and k in write:
             rd, wr = fetch[k] * f_scale, write[k] * w_scale
             kernels[k] = {"fetch_bytes_raw": fetch[k], "write_bytes_raw": write[k],
@@ -463,7 +469,6 @@ def setup_workload(name, la, dev):
             "metric": METRIC, "step": step, "tokens_per_step": B * N, "step_bytes": 4 * tb,
             "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "eps": eps,
                        "input_sets": len(sets)},
-            # the state pass is two launches (partial states, fixed-order combine) timed together
             "groups": [("state", STATE_KERNELS, 2 * tb), ("apply", APPLY_KERNELS, 2 * tb)],
             "copy_pairs": [(s[0], s[3]) for s in sets],
             "cpu_baseline": lambda budget: cpu_baseline(q, k, v, spec, budget),
