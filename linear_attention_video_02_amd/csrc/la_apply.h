@@ -331,19 +331,18 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 // value fp16 cannot carry exactly enough: then every token of
                 // the group is scaled by 2^sc, sc = 13 - (exponent of its
                 // largest relu(Q) value)
-                u32x4 w4[C::KS];
                 uint32_t m16 = 0;
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
                     const bool live = C::DP == D || 32 * ks + 8 * g < D;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) w4[ks][i] = live ? relu_bf16x2(qc[r][ks][i]) : 0u;
-                    const uint32_t mk = max_u16x8(w4[ks]);
+                    const uint32_t mk = live ? max_relu_bits8(qc[r][ks]) : 0u;
                     m16 = mk > m16 ? mk : m16;
                 }
                 // bf16 bit patterns of 2^-6 and 2^14
                 const bool odd = m16 != 0 && (m16 < 0x3C80u || m16 >= 0x4680u);
-                const bool scaled = __builtin_amdgcn_ballot_w64(odd) != 0;
+                // (d >= 112: always, without a branch -- a branch inside the
+                // k-step loop makes the 768-thread kernel spill registers)
+                const bool scaled = C::SLDS || __builtin_amdgcn_ballot_w64(odd) != 0;
                 int sc = 0;
                 if (scaled) {
                     uint32_t tm = m16;
@@ -354,11 +353,14 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 // one 32-channel k-step at a time: its B fragments, then its MFMAs
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
+                    const bool live = C::DP == D || 32 * ks + 8 * g < D;
+                    u32x4 w4;
                     float x[8];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        x[2 * i] = bf_lo(w4[ks][i]);
-                        x[2 * i + 1] = bf_hi(w4[ks][i]);
+                        w4[i] = live ? relu_bf16x2(qc[r][ks][i]) : 0u;
+                        x[2 * i] = bf_lo(w4[i]);
+                        x[2 * i + 1] = bf_hi(w4[i]);
                     }
                     if (C::SLDS) {
                         const float4 za = *(const float4*)(zs + 32 * ks + 8 * g);
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                         den = fmaf(x[4], zb.x, den); den = fmaf(x[5], zb.y, den);
                         den = fmaf(x[6], zb.z, den); den = fmaf(x[7], zb.w, den);
                     } else {
-                        const bf16x8 Bu = __builtin_bit_cast(bf16x8, w4[ks]);
+                        const bf16x8 Bu = __builtin_bit_cast(bf16x8, w4);
                         dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Azh[C::SLDS ? 0 : ks], Bu, dacc, 0, 0, 0);
                         dacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Azl[C::SLDS ? 0 : ks], Bu, dacc, 0, 0, 0);
                     }

@@ -170,19 +170,21 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Largest of the 4 bf16 pairs (8 values) of a u32x4, compared as unsigned
-// 16-bit integers -- which orders non-negative bf16 values by magnitude.
-// The words are copied to scalars before the bit casts: this compiler turns
-// __builtin_bit_cast of a vector-element expression (w[1]) into a cast of
-// element 0.
-typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
-__device__ __forceinline__ u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
-__device__ __forceinline__ uint32_t max_u16x8(u32x4 w) {
+// Largest of the 8 bf16 values of a u32x4 as a non-negative 16-bit pattern:
+// the signed 16-bit maximum of the raw words, clamped at 0 -- which is the
+// largest relu'd value's bit pattern (non-negative bf16 values order like
+// their int16 patterns; negative ones lie below 0).  The words are copied to
+// scalars before the bit casts: this compiler turns __builtin_bit_cast of a
+// vector-element expression (w[1]) into a cast of element 0.
+typedef __attribute__((ext_vector_type(2))) short s16x2_t;
+__device__ __forceinline__ s16x2_t as_s16x2(uint32_t x) { return __builtin_bit_cast(s16x2_t, x); }
+__device__ __forceinline__ uint32_t max_relu_bits8(u32x4 w) {
     const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-    u16x2 m = __builtin_elementwise_max(as_u16x2(w0), as_u16x2(w1));
-    m = __builtin_elementwise_max(m, as_u16x2(w2));
-    m = __builtin_elementwise_max(m, as_u16x2(w3));
-    return m[0] > m[1] ? m[0] : m[1];
+    s16x2_t m = __builtin_elementwise_max(as_s16x2(w0), as_s16x2(w1));
+    m = __builtin_elementwise_max(m, as_s16x2(w2));
+    m = __builtin_elementwise_max(m, as_s16x2(w3));
+    const int v = m[0] > m[1] ? m[0] : m[1];
+    return v > 0 ? (uint32_t)v : 0u;
 }
 
 // wave-wide maximum of a float (every lane gets it)
