@@ -25,7 +25,8 @@ sys.path.insert(0, ROOT)
 METRIC = "linear-attn tokens/sec and achieved HBM GB/s (% peak), 720p-5s shape, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "720p5s"
-SRC_FILES = ["la_common.h", "la_state.h", "la_apply.h", "la_causal.h", "la_api.hip"]
+SRC_FILES = ["la_common.h", "la_state.h", "la_apply.h", "la_causal.h", "la_tconv.h", "la_api.hip"]
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 
 def kernel_source_hash():
@@ -111,6 +112,42 @@ def cpu_baseline(q, k, v, spec, budget_s=12.0):
         "sample": f"{slices} (batch, head) slices of the {WORKLOAD} workload in order "
                   f"({slices / len(order):.1f} passes over its {len(order)} slices), all {N} "
                   f"tokens each, fp64 numpy, {t_used:.1f} s of oracle time "
+                  f"({len(os.sched_getaffinity(0))} host cores visible)",
+    }
+
+
+def cpu_baseline_tconv(X, W, cache, bias, spec, budget_s=12.0):
+    """Time the fp64 oracle of the temporal convolution on the block's spatial
+    positions, a few at a time (all frames of each), until about budget_s."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    B, T, P = spec["B"], spec["T"], spec["P"]
+    Wh = W.float().cpu().numpy().astype(np.float64)
+    bh = bias.float().cpu().numpy().astype(np.float64)
+    per = 8
+    done, t_used = 0, 0.0
+    while t_used < budget_s and done < B * P:
+        b, p0 = divmod(done, P)
+        p1 = min(p0 + per, P)
+        Xs = X[b:b + 1, :, p0:p1].float().cpu().numpy().astype(np.float64)
+        cs = cache[b:b + 1, p0:p1].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.temporal_conv(Xs, Wh, cs, bh)
+        t_used += time.perf_counter() - t0
+        done += p1 - p0
+    return {
+        "value": done * T / t_used,
+        "unit": "tokens/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of the block's {B * P} spatial positions, all {T} frames each "
+                  f"({done * T} tokens), fp64 numpy, {t_used:.1f} s of oracle time "
                   f"({len(os.sched_getaffinity(0))} host cores visible)",
     }
 
@@ -290,7 +327,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b"],
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b", "tconv720p"],
                     help="default: the headline 720p-5s bidirectional step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel events on every n-th timed step (each event costs ~2 us)")
@@ -361,7 +398,8 @@ def main():
     g = max(range(ngroups), key=lambda i: group_ms[i])
     gname, kernels, nbytes = wl["groups"][g]
     dur_ms = group_ms[g]
-    achieved = nbytes / (dur_ms * 1e-3) / 1e9
+    rf = wl.get("roofline", {"bound": "hbm", "peak": HBM_PEAK_GBPS, "unit": "GB/s", "scale": 1e9})
+    achieved = nbytes / (dur_ms * 1e-3) / rf["scale"]
     src_hash = kernel_source_hash()
     traffic = load_traffic(kernels, src_hash) if args.workload == WORKLOAD else None
 
@@ -398,16 +436,16 @@ def main():
         "data": "synthetic",
         "config": wl["config"],
         "roofline": {
-            "bound": "hbm",
+            "bound": rf["bound"],
             "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
+            "peak": rf["peak"],
+            "unit": rf["unit"],
+            "frac": achieved / rf["peak"],
             "traffic": traffic,
             "kernel": "+".join(kernels),
-            "algorithmic_bytes": nbytes,
+            ("algorithmic_flops" if rf["bound"] == "mfma" else "algorithmic_bytes"): nbytes,
             "duration_us": dur_ms * 1e3,
-            "traffic_over_algorithmic": traffic / nbytes if traffic else None,
+            "traffic_over_algorithmic": traffic / nbytes if traffic and rf["bound"] == "hbm" else None,
         },
         "step_GBps": wl["step_bytes"] / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": wl["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -420,6 +458,8 @@ def main():
         "wall_s": wall,
         "src_hash": src_hash,
     }
+    if "extra" in wl:
+        out.update(wl["extra"](tev_factory=FenceFreeEvents))
     if not args.no_cpu_baseline and "cpu_baseline" in wl:
         out["cpu_baseline"] = wl["cpu_baseline"](args.cpu_budget)
     print(json.dumps(out), flush=True)
@@ -603,6 +643,64 @@ def setup_workload(name, la, dev):
             "groups": [("block_steps", STATE_KERNELS + APPLY_KERNELS, step_bytes)],
             "copy_pairs": [(blocks[0][b], outs[b]) for b in range(nb)],
             "block_bytes": blk_bytes,
+        }
+    if name == "tconv720p":
+        from linear_attention_video_02_amd.inputs import TCONV, make_tconv_device
+        w = TCONV[name]
+        B, T, P, D = w["B"], w["T"], w["P"], w["D"]
+        X, W, cache, bias = make_tconv_device(B, T, P, D, w["seed"], dev)
+        xb = X.numel() * X.element_size()
+        wb = W.numel() * W.element_size()
+        base = rotating((X, W, cache), n_sets_for(2 * xb + wb))
+        sets = [(Xi, Wi, ci, torch.empty_like(X)) for (Xi, Wi, ci) in base]
+        M = B * T * P
+        flops = 2 * M * D * 3 * D  # the GEMM: M tokens x D outputs x 3D inputs
+
+        def step(i, ev, tev):
+            Xi, Wi, ci, Yi = sets[i % len(sets)]
+            if ev is not None:
+                tev.record(ev[0])
+            # a denoising step of the block: reads the cache, leaves it (commit = 0)
+            la.temporal_conv_step(Xi, Wi, ci, bias, commit=False, out=Yi)
+            if ev is not None:
+                tev.record(ev[1])
+
+        def library_gemm(tev_factory):
+            # context only: hipBLASLt (torch.matmul) on a plain GEMM of the same
+            # shape, [M, 3D] x [3D, D], without the frame shifts, shortcut or bias
+            A = torch.randn((M, 3 * D), device=dev).to(torch.bfloat16)
+            Bm = torch.randn((3 * D, D), device=dev).to(torch.bfloat16)
+            Cm = torch.empty((M, D), device=dev, dtype=torch.bfloat16)
+            for _ in range(5):
+                torch.matmul(A, Bm, out=Cm)
+            torch.cuda.synchronize()
+            te = tev_factory()
+            e0, e1 = te.new(), te.new()
+            n = 20
+            te.record(e0)
+            for _ in range(n):
+                torch.matmul(A, Bm, out=Cm)
+            te.record(e1)
+            torch.cuda.synchronize()
+            us = te.ms(e0, e1) / n * 1e3
+            te.close()
+            return {"library_gemm_same_shape": {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
+                                                "what": "torch.matmul bf16 [M,3D]x[3D,D] (hipBLASLt)"}}
+
+        def cpu(budget):
+            return cpu_baseline_tconv(X, W, cache, bias, w, budget)
+
+        return {
+            "metric": "temporal-conv (Mix-FFN, block-causal) tokens/sec and achieved TFLOP/s (% of bf16 "
+                      "MFMA peak), one 720p-60s block at SANA-Video-2B width, 1 GPU",
+            "step": step, "tokens_per_step": M, "step_bytes": 2 * xb + wb,
+            "config": {"workload": name, "B": B, "T": T, "P": P, "D": D, "bias": True, "commit": 0,
+                       "input_sets": len(sets)},
+            "groups": [("tconv", ("la_tconv_bf16_kernel",), flops)],
+            "roofline": {"bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "scale": 1e12},
+            "copy_pairs": [(s_[0], s_[3]) for s_ in sets],
+            "extra": library_gemm,
+            "cpu_baseline": cpu,
         }
     raise SystemExit(f"unknown workload {name}")
 

@@ -143,6 +143,32 @@ LA_API int la_token_causal(const void* Q, const void* K, const void* V, void* O,
                     int B, int H, int N, int d, int gt, int gh, int gw, int n_offset,
                     float eps, int dtype, void* stream);
 
+/* One block of the block-causal temporal convolution of the Mix-FFN, with
+ * its shortcut (same page, section 3.4, "Spatial-Temporal Mix-FFN" and
+ * "Block Causal Mix-FFN", Figure 4(b)).  Per spatial position p:
+ *   Y[b,f,p] = X[b,f,p] + W[0] X[b,f-1,p] + W[1] X[b,f,p] + W[2] X[b,f+1,p] (+ bias)
+ * for the block's frames f = 0..T-1, where X[b,-1,p] = cache[b,p] (the last
+ * frame of the previous block: zero-fill the cache before the first block)
+ * and X[b,T,p] = 0 (zero padding: no block sees a later one).  W[k] x is the
+ * matrix-vector product with the D x D matrix W[k] (row = output channel).
+ *  - X, Y: contiguous [B, T, P, D] bf16 (frame-major tokens, P spatial
+ *    positions per frame, D channels).  W: contiguous [3, D, D] bf16,
+ *    W[k][out][in].  bias: [D] float or NULL.  cache: [B, P, D] bf16.
+ *    All device memory, caller-owned, 16-byte aligned.
+ *  - commit = 1 writes X[b, T-1] into cache[b] after Y is formed (the cache
+ *    update after the clean block); commit = 0 leaves the cache untouched.
+ *  - Products run in bf16 with fp32 accumulation; Y is rounded to nearest
+ *    even once, after the shortcut and bias are added.
+ *  - dtype must be LA_BF16, D a multiple of 64 and at most 16384, and X
+ *    under 2 GiB (otherwise LA_E_UNSUPPORTED: split a larger call by
+ *    batch).  B*T*P = 0 returns LA_OK with nothing written.  Y must not
+ *    overlap X, W, bias or cache, nor the cache X, W or bias (LA_E_ALIAS).
+ *  - No workspace; the call only enqueues kernels on stream.  Every output
+ *    element has one fixed order of summation, so repeated calls give
+ *    bitwise equal results. */
+LA_API int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bias, void* cache,
+                                 int B, int T, int P, int D, int commit, int dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 LA_API const char* la_strerror(int status);
 

@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.la_block_causal_step.restype = ci
         L.la_token_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + [ci] * 8 + [cf, ci, vp]
         L.la_token_causal.restype = ci
+        L.la_temporal_conv_step.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
+        L.la_temporal_conv_step.restype = ci
         L.la_strerror.argtypes = [ci]
         L.la_strerror.restype = ctypes.c_char_p
         L.la_last_hip_error.argtypes = []
@@ -267,3 +269,35 @@ def block_causal(q_blocks, k_blocks, v_blocks, N, grid, block_tokens, eps=1e-6,
         outs.append(block_causal_step(qb, kb, vb, S_carry, z_carry, N, grid, block_tokens,
                                       first_block + i, True, eps))
     return outs, S_carry, z_carry
+
+
+def temporal_conv_step(x, W, cache, bias=None, commit=True, out=None):
+    """One block of the block-causal temporal convolution with shortcut.
+
+    x: [B, T, P, D] bf16 (the block's frames; P spatial positions); W: [3, D, D]
+    bf16 with W[k][out][in] the weight at time offset k - 1; cache: [B, P, D]
+    bf16, the previous block's last frame (zeros before the first block);
+    bias: [D] float32 or None.  Returns out = x + conv(x) (+ bias); with commit
+    the cache then holds x[:, -1].
+    """
+    torch = _torch()
+    for t in (x, W, cache):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("x, W and cache must be contiguous bf16 GPU tensors")
+    if x.dim() != 4:
+        raise ValueError("x must be [B, T, P, D]")
+    B, T, P, D = x.shape
+    if tuple(W.shape) != (3, D, D) or tuple(cache.shape) != (B, P, D):
+        raise ValueError("W must be [3, D, D] and cache [B, P, D]")
+    if bias is not None and (not bias.is_cuda or bias.dtype != torch.float32 or
+                             tuple(bias.shape) != (D,) or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 [D] GPU tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    rc = lib().la_temporal_conv_step(_ptr(x), _ptr(out), _ptr(W), _ptr(bias), _ptr(cache),
+                                     B, T, P, D, int(bool(commit)), LA_BF16, _stream(x))
+    if rc:
+        raise LinAttnError(rc, "la_temporal_conv_step")
+    return out

@@ -13,6 +13,7 @@
 #include "la_causal.h"
 #include "la_common.h"
 #include "la_state.h"
+#include "la_tconv.h"
 
 namespace {
 
@@ -556,6 +557,52 @@ int la_token_causal(const void* Q, const void* K, const void* V, void* O, float*
     }
     return run_token_causal(Q, K, V, O, S_carry, z_carry, ws, B, H, N, n_offset, d, gt, gh, gw, eps,
                             (hipStream_t)stream);
+}
+
+int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bias, void* cache, int B, int T,
+                          int P, int D, int commit, int dtype, void* stream) {
+    if (dtype != LA_BF16) return LA_E_UNSUPPORTED;
+    if (B < 0 || T < 0 || P < 0 || D < 1 || (commit != 0 && commit != 1)) return LA_E_SHAPE;
+    if (D % 64 != 0 || D > 16384) return LA_E_UNSUPPORTED;  // W under 2 GiB
+    const long long M = (long long)B * T * P;
+    if (M * D * 2 >= (1ll << 31)) return LA_E_UNSUPPORTED;  // X under 2 GiB (32-bit buffer offsets)
+    if (M == 0) return LA_OK;  // an empty block: no output, the cache stays
+    if (!X || !Y || !W || !cache) return LA_E_NULLPTR;
+    if (!aligned16(X) || !aligned16(Y) || !aligned16(W) || !aligned16(cache) || !aligned16(bias))
+        return LA_E_ALIGN;
+    const size_t nx = (size_t)M * D * 2, nw = (size_t)3 * D * D * 2, nc = (size_t)B * P * D * 2;
+    const size_t nb = bias ? (size_t)D * 4 : 0;
+    if (overlaps(Y, nx, X, nx) || overlaps(Y, nx, W, nw) || overlaps(Y, nx, cache, nc) ||
+        overlaps(Y, nx, bias, nb) || overlaps(cache, nc, X, nx) || overlaps(cache, nc, W, nw) ||
+        overlaps(cache, nc, bias, nb))
+        return LA_E_ALIAS;
+    TconvArgs a;
+    a.X = (const uint16_t*)X;
+    a.Y = (uint16_t*)Y;
+    a.W = (const uint16_t*)W;
+    a.bias = bias;
+    a.cache = (const uint16_t*)cache;
+    a.T = T;
+    a.P = P;
+    a.D = D;
+    a.M = (int)M;
+    a.mtiles = (int)((M + TconvCfg::BM - 1) / TconvCfg::BM);
+    a.ntiles = (D + TconvCfg::BN - 1) / TconvCfg::BN;
+    a.group = env_int("LA_TCONV_GROUP", 8);
+    if ((long long)a.mtiles * a.ntiles >= (1ll << 31)) return LA_E_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    int rc = launch_kernel<TconvArgs>(la_tconv_bf16_kernel, dim3(a.mtiles * a.ntiles), 0, st, a,
+                                      TconvCfg::THREADS);
+    if (rc != LA_OK || !commit) return rc;
+    TconvCacheArgs c;
+    c.X = (const uint16_t*)X;
+    c.cache = (uint16_t*)cache;
+    c.T = T;
+    c.P = P;
+    c.D = D;
+    c.B = B;
+    const size_t pieces = (size_t)B * P * D / 8;
+    return launch_kernel<TconvCacheArgs>(la_tconv_cache_kernel, dim3((unsigned)((pieces + 255) / 256)), 0, st, c);
 }
 
 const char* la_last_hip_error(void) { return g_hip_msg; }

@@ -16,6 +16,8 @@ Workloads (latent token grids of the pages' video shapes; DCAE-V compresses
           width 2240) on the 720p-5s latent
   cross720p  B2 H32, 19320 video queries over 300 text keys/values, d64 bf16, no RoPE
              (the pages give no text length; 300 is a parameter)
+  tconv720p  the Mix-FFN temporal convolution on one block of the 720p-60s clip:
+             B1, 24 frames x 920 positions, width D = 2240 (SANA-Video-2B), bf16
 """
 from __future__ import annotations
 
@@ -145,3 +147,39 @@ def make_workload_device(name: str, device="cuda:0"):
         tdt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
         return tuple(torch.from_numpy(a).to(device=device, dtype=tdt) for a in (q, k, v)) + (w,)
     return make_qkv_device(w["B"], w["H"], w["N"], w["d"], w["dtype"], w["seed"], device) + (w,)
+
+
+TCONV = {"tconv720p": dict(name="tconv720p", B=1, T=24, P=920, D=2240, seed=1008)}
+
+
+def make_tconv(B: int, T: int, P: int, D: int, seed: int = 0, bias: bool = True):
+    """Inputs of one temporal-convolution block as float32 arrays.
+
+    Draw order from numpy's PCG64 stream of `seed`: X [B, T, P, D] ~ N(0, 1),
+    W [3, D, D] ~ N(0, 1/(3D)) (unit-variance output), cache [B, P, D] ~ N(0, 1),
+    then bias [D] ~ N(0, 0.01) if asked (else None).  X, W and the cache are
+    rounded to bf16; the bias stays float32.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = round_to_bf16(rng.standard_normal((B, T, P, D), dtype=np.float32))
+    W = round_to_bf16(rng.standard_normal((3, D, D), dtype=np.float32) * np.float32(1.0 / math.sqrt(3 * D)))
+    cache = round_to_bf16(rng.standard_normal((B, P, D), dtype=np.float32))
+    b = (rng.standard_normal(D, dtype=np.float32) * np.float32(0.1)) if bias else None
+    return X, W, cache, b
+
+
+def make_tconv_device(B: int, T: int, P: int, D: int, seed: int = 0, device="cuda:0"):
+    """X, W, cache and bias of the same distributions as make_tconv, drawn on a GPU.
+
+    torch's device generator seeded with `seed`, draw order X, W, cache, bias;
+    X, W and the cache in bf16 by torch's round-to-nearest-even cast, the bias
+    float32.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    X = torch.randn((B, T, P, D), generator=gen, device=device).to(torch.bfloat16)
+    W = (torch.randn((3, D, D), generator=gen, device=device) / math.sqrt(3 * D)).to(torch.bfloat16)
+    cache = torch.randn((B, P, D), generator=gen, device=device).to(torch.bfloat16)
+    bias = torch.randn(D, generator=gen, device=device) * 0.1
+    return X, W, cache, bias

@@ -38,8 +38,8 @@ def header_enum(name):
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
-                          "la_block_causal_step", "la_token_causal", "la_strerror",
-                          "la_last_hip_error"}
+                          "la_block_causal_step", "la_token_causal", "la_temporal_conv_step",
+                          "la_strerror", "la_last_hip_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -190,6 +190,40 @@ def test_token_causal_rejects(L, kw, want):
 def test_token_causal_empty_is_noop(L):
     # N = 0: checks pass, nothing is launched, the (fake) carry is not touched
     assert causal_call(L, N=0, Q=None, K=None, V=None, O=None) == 0
+
+
+def tconv_call(L, **kw):
+    a = dict(X=p(0), Y=p(1 << 30), W=p(2 << 30), bias=None, cache=p(3 << 30), B=1, T=4, P=920,
+             D=2240, commit=1, dtype=la.LA_BF16)
+    a.update(kw)
+    return L.la_temporal_conv_step(a["X"], a["Y"], a["W"], a["bias"], a["cache"], a["B"], a["T"],
+                                   a["P"], a["D"], a["commit"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=la.LA_FP32), "LA_E_UNSUPPORTED"),
+    (dict(D=100), "LA_E_UNSUPPORTED"),             # not a multiple of 64
+    (dict(D=16448), "LA_E_UNSUPPORTED"),           # W would pass 2 GiB
+    (dict(B=200, T=24, D=2240), "LA_E_UNSUPPORTED"),  # X would pass 2 GiB
+    (dict(D=0), "LA_E_SHAPE"),
+    (dict(T=-1), "LA_E_SHAPE"),
+    (dict(commit=2), "LA_E_SHAPE"),
+    (dict(X=None), "LA_E_NULLPTR"),
+    (dict(cache=None), "LA_E_NULLPTR"),
+    (dict(W=p((2 << 30) + 4)), "LA_E_ALIGN"),
+    (dict(bias=p((4 << 30) + 8)), "LA_E_ALIGN"),
+    (dict(Y=p(64)), "LA_E_ALIAS"),                 # Y inside X
+    (dict(cache=p(1 << 20)), "LA_E_ALIAS"),        # cache inside X
+    (dict(bias=p((3 << 30) + 32)), "LA_E_ALIAS"),  # bias inside the cache
+])
+def test_temporal_conv_rejects(L, kw, want):
+    assert tconv_call(L, **kw) == E[want]
+
+
+def test_temporal_conv_empty_is_noop(L):
+    # no token: checks pass, nothing is launched, the (null) buffers are not touched
+    assert tconv_call(L, T=0, X=None, Y=None, W=None, cache=None) == 0
+    assert tconv_call(L, P=0, X=None, Y=None, W=None, cache=None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,137 @@
+"""GPU parity of the block-causal temporal convolution (la_temporal_conv_step)
+against the fp64 oracle.
+
+Bound, element by element: |got - ref| <= 2^-8 |ref| + 1e-3 rms(ref).  The
+first term is the one rounding of Y to bf16 (half an ulp is at most 2^-8 of
+the value); the second covers fp32 accumulation over K = 3D products, whose
+error is orders of magnitude below it at these widths.  The row-normalised
+error of the linear-attention tests (2e-2) is checked as well.
+
+Inputs are bf16-exact (make_tconv / make_tconv_device), so the oracle sees
+exactly the values the kernel reads.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from _gpu import TOL, host, row_err, say
+from linear_attention_video_02_amd.inputs import TCONV, make_tconv, make_tconv_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def la():
+    import linear_attention_video_02_amd as m
+    m.lib()
+    return m
+
+
+def up(a, dtype="bf16"):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def check(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = float(np.sqrt(np.mean(ref * ref))) or 1.0
+    excess = np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)
+    worst = float(excess.max()) / scale
+    e = row_err(got.reshape(-1, got.shape[-1]), ref.reshape(-1, ref.shape[-1]))
+    say(f"  {what}: worst excess over bf16 rounding {worst:.2e} rms, row err {e:.2e}")
+    assert worst <= 1e-3, (what, worst)
+    assert e <= TOL["bf16"], (what, e)
+
+
+# (B, T, P, D, bias, seed): several 128-token and 128-channel tiles with ragged
+# tails, blocks of one frame (cache and zero padding meet), P below a tile.
+CASES = [
+    (1, 3, 37, 64, False, 11),
+    (2, 3, 37, 128, True, 12),
+    (1, 5, 300, 320, True, 13),
+    (2, 1, 200, 192, False, 14),
+    (3, 4, 45, 256, True, 15),
+    (1, 2, 1, 64, True, 16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}T{c[1]}P{c[2]}D{c[3]}{'b' if c[4] else ''}"
+                                             for c in CASES])
+def test_block_against_oracle(la, case):
+    import torch
+    B, T, P, D, use_bias, seed = case
+    say(f"[tconv] B={B} T={T} P={P} D={D} bias={use_bias}")
+    X, W, cache, bias = make_tconv(B, T, P, D, seed, bias=use_bias)
+    tX, tW, tc = up(X), up(W), up(cache)
+    tb = up(bias, "fp32") if use_bias else None
+    out = la.temporal_conv_step(tX, tW, tc, tb, commit=True)
+    torch.cuda.synchronize()
+    ref, new_cache = oracle.temporal_conv(X, W, cache, bias)
+    check(host(out), ref, f"B{B} T{T} P{P} D{D}")
+    # commit: the cache now holds the block's last frame, bit for bit
+    assert torch.equal(tc, tX[:, -1]), "cache after commit"
+    assert np.array_equal(host(tc), new_cache)
+
+
+def test_first_block_zero_cache_and_chain(la):
+    """A sequence of 7 frames in blocks of 3, 3, 1 from a zero cache, each block
+    committing, against the oracle's block loop; and the chain equals the
+    whole-sequence convolution with the block boundaries cut."""
+    import torch
+    P, D = 70, 192
+    X, W, _, bias = make_tconv(1, 7, P, D, 21)
+    tW, tb = up(W), up(bias, "fp32")
+    tc = torch.zeros((1, P, D), dtype=torch.bfloat16, device="cuda:0")
+    outs = []
+    for f0 in range(0, 7, 3):
+        xb = up(X[:, f0:f0 + 3])
+        outs.append(host(la.temporal_conv_step(xb, tW, tc, tb, commit=True)))
+    torch.cuda.synchronize()
+    got = np.concatenate(outs, axis=1)[0]
+    ref, last = oracle.temporal_conv_blocks(X[0], W, 3, bias)
+    check(got, ref, "chained blocks 3+3+1")
+    assert np.array_equal(host(tc)[0], last)
+
+
+def test_commit_zero_leaves_cache(la):
+    import torch
+    X, W, cache, bias = make_tconv(2, 3, 50, 128, 31)
+    tc = up(cache)
+    before = tc.clone()
+    out = la.temporal_conv_step(up(X), up(W), tc, up(bias, "fp32"), commit=False)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, before)
+    check(host(out), oracle.temporal_conv(X, W, cache, bias)[0], "commit=0")
+
+
+def test_repeatable(la):
+    import torch
+    X, W, cache, bias = make_tconv(1, 4, 130, 256, 41)
+    tX, tW, tc, tb = up(X), up(W), up(cache), up(bias, "fp32")
+    a = la.temporal_conv_step(tX, tW, tc, tb, commit=False)
+    b = la.temporal_conv_step(tX, tW, tc, tb, commit=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_tconv720p_sampled_positions(la):
+    """The benchmarked block (24 frames x 920 positions, D = 2240, with bias) in
+    the benchmark's launch configuration; the oracle on 12 sampled spatial
+    positions (every frame of each: the convolution never mixes positions)."""
+    import torch
+    w = TCONV["tconv720p"]
+    B, T, P, D = w["B"], w["T"], w["P"], w["D"]
+    say(f"[tconv720p] B={B} T={T} P={P} D={D}")
+    tX, tW, tc, tb = make_tconv_device(B, T, P, D, w["seed"])
+    out = la.temporal_conv_step(tX, tW, tc, tb, commit=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    pos = np.sort(np.concatenate([[0, P - 1], rng.choice(np.arange(1, P - 1), 10, replace=False)]))
+    idx = torch.from_numpy(pos).to("cuda:0")
+    Xs = host(tX.index_select(2, idx))
+    cs = host(make_tconv_device(B, T, P, D, w["seed"])[2].index_select(1, idx))
+    ref, _ = oracle.temporal_conv(Xs, host(tW), cs, host(tb))
+    check(host(out.index_select(2, idx)), ref, "tconv720p sampled positions")
+    assert torch.equal(tc, tX[:, -1])
