@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "linear-attn tokens/sec and achieved HBM GB/s (% peak), 720p-5s shape, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "720p5s"
-SRC_FILES = ["la_common.h", "la_state.h", "la_apply.h", "la_causal.h", "la_tconv.h", "la_api.hip"]
+SRC_FILES = ["la_common.h", "la_state.h", "la_apply.h", "la_causal.h", "la_tconv.h", "la_api.hip", "la_tconv.hip"]
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 

@@ -9,26 +9,42 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblinattn.so")
 
-SOURCES = ["la_api.hip"]
+# translation unit -> its own extra flags
+SOURCES = {
+    "la_api.hip": [],
+    # the temporal-convolution GEMM keeps its MFMA accumulators in VGPRs
+    "la_tconv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 (v_pk_*_f32) instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode})")
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every translation unit for gfx950 and link liblinattn.so."""
+    import tempfile
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    with tempfile.TemporaryDirectory(prefix="la_build_") as tmp:
+        objs = []
+        for src, flags in SOURCES.items():
+            obj = os.path.join(tmp, src + ".o")
+            _run([hipcc, *FLAGS, *flags, *extra, "-I", INCLUDE, "-I", CSRC, "-c",
+                  os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -588,12 +588,13 @@ int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bi
     a.M = (int)M;
     a.mtiles = (int)((M + TconvCfg::BM - 1) / TconvCfg::BM);
     a.ntiles = (D + TconvCfg::BN - 1) / TconvCfg::BN;
-    a.group = env_int("LA_TCONV_GROUP", 8);
+    a.group = env_int("LA_TCONV_GROUP", 4);
     if ((long long)a.mtiles * a.ntiles >= (1ll << 31)) return LA_E_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
-    int rc = launch_kernel<TconvArgs>(la_tconv_bf16_kernel, dim3(a.mtiles * a.ntiles), 0, st, a,
-                                      TconvCfg::THREADS);
-    if (rc != LA_OK || !commit) return rc;
+    (void)hipGetLastError();  // clear a stale error so it is not reported as ours
+    hipError_t e = la_tconv_launch(a, st);
+    if (e != hipSuccess) return hip_fail(e, "la_tconv_bf16_kernel launch");
+    if (!commit) return LA_OK;
     TconvCacheArgs c;
     c.X = (const uint16_t*)X;
     c.cache = (uint16_t*)cache;
@@ -601,8 +602,9 @@ int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bi
     c.P = P;
     c.D = D;
     c.B = B;
-    const size_t pieces = (size_t)B * P * D / 8;
-    return launch_kernel<TconvCacheArgs>(la_tconv_cache_kernel, dim3((unsigned)((pieces + 255) / 256)), 0, st, c);
+    e = la_tconv_cache_launch(c, st);
+    if (e != hipSuccess) return hip_fail(e, "la_tconv_cache_kernel launch");
+    return LA_OK;
 }
 
 const char* la_last_hip_error(void) { return g_hip_msg; }
