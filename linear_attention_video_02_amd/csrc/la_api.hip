@@ -586,9 +586,14 @@ int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bi
     a.P = P;
     a.D = D;
     a.M = (int)M;
-    a.mtiles = (int)((M + TconvCfg::BM - 1) / TconvCfg::BM);
+    a.F = T < TconvCfg::FMAX ? T : TconvCfg::FMAX;
+    a.nft = (T + a.F - 1) / a.F;
+    a.npt = (P + TconvCfg::S - 1) / TconvCfg::S;
+    if ((long long)B * a.nft * a.npt >= (1ll << 31) / 8) return LA_E_UNSUPPORTED;
+    a.mtiles = B * a.nft * a.npt;
     a.ntiles = (D + TconvCfg::BN - 1) / TconvCfg::BN;
-    a.group = env_int("LA_TCONV_GROUP", 4);
+    a.gm = env_int("LA_TCONV_GM", 4);
+    a.gn = env_int("LA_TCONV_GN", 7);
     if ((long long)a.mtiles * a.ntiles >= (1ll << 31)) return LA_E_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours

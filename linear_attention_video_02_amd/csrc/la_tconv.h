@@ -26,24 +26,31 @@ struct TconvArgs {
     const uint16_t* cache;  // [B][P][D] bf16: the previous block's last frame
     int T, P, D;
     int M;                  // B * T * P tokens
-    int mtiles, ntiles;     // ceil(M / BM), ceil(D / BN)
-    int group;              // token tiles per group of the tile order
+    int F;                  // frames per token tile: min(T, 8)
+    int nft, npt;           // ceil(T / F), ceil(P / 40)
+    int mtiles, ntiles;     // B * nft * npt token tiles, ceil(D / 160) channel tiles
+    int gm, gn;             // tile-order group: gm token tiles by gn channel tiles
 };
 
-// 320 output channels x 160 tokens per workgroup (the 720p block at width
-// 2240 is 7 x 138 such tiles, no ragged edge), K in stages of 64 channels,
-// double-buffered in LDS (120 KB, one workgroup per CU).  8 waves in a 4 x 2
-// grid, each 80 channels x 80 tokens = 5 x 5 tiles of v_mfma_f32_16x16x32_bf16
-// (100 accumulators in VGPRs): per 32-deep k step a wave reads 10 fragments
-// for 25 MFMAs; two waves share each SIMD and hide each other's LDS reads.
+// 160 output channels x 320 tokens per workgroup, the tokens being 8 frames x
+// 40 positions (the 720p block, 24 frames x 920 positions at width 2240, is
+// 14 x 69 such tiles with no ragged edge).  K runs over 64-channel chunks,
+// each taken at the three time offsets in turn (K = 3D).  Per chunk the
+// tile's 10-frame union (one frame before, one after) is staged in LDS once
+// and read by all three offsets at row shifts of 0, 40 and 80; W slices are
+// staged per offset.  Both are double-buffered: 140 KB of LDS, one
+// workgroup per CU.  8 waves in a 2 x 4 grid, each 80 channels x 80 tokens =
+// 5 x 5 tiles of v_mfma_f32_16x16x32_bf16 (100 accumulators in VGPRs): per
+// 32-deep k step a wave reads 10 fragments for 25 MFMAs.
 struct TconvCfg {
-    static constexpr int BN = 320, BM = 160, BK = 64;
+    static constexpr int BN = 160, BM = 320, BK = 64;
     static constexpr int THREADS = 512;
-    static constexpr int WN = 5, WM = 5;               // 16 x 16 tiles per wave
-    static constexpr int ROWS = BN + BM;               // LDS rows per stage (W, then X)
-    static constexpr int STAGE = ROWS * BK;            // bf16 elements per stage
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;    // two stages
-    static constexpr int XR = 3;                       // X rows per loader thread (last: tid < 256)
+    static constexpr int WN = 5, WM = 5;                 // 16 x 16 tiles per wave
+    static constexpr int S = 40, FMAX = 8;               // token tile: F <= 8 frames x 40 positions
+    static constexpr int UROWS = (FMAX + 2) * S;         // frame-union rows per chunk
+    static constexpr int WSTAGE = BN * BK;               // bf16 elements of a W slice
+    static constexpr int XSTAGE = UROWS * BK;            // bf16 elements of a union chunk
+    static constexpr int LDS_BYTES = 2 * (WSTAGE + XSTAGE) * 2;
 };
 
 // The cache after a block: its last input frame, X[b][T-1] -> cache[b].

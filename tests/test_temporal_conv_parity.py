@@ -45,9 +45,14 @@ def check(got, ref, what):
     assert e <= TOL["bf16"], (what, e)
 
 
-# (B, T, P, D, bias, seed): several 128-token and 128-channel tiles with ragged
-# tails, blocks of one frame (cache and zero padding meet), P below a tile.
+# (B, T, P, D, bias, seed): token tiles of F frames x 160/F positions (F = 8,
+# 4, 2 or 1 by the block's length) and 320-channel tiles, with ragged frame,
+# position and channel tails; blocks of one frame (cache and zero padding
+# meet); P below a tile.
 CASES = [
+    (1, 9, 45, 128, True, 17),
+    (2, 8, 21, 64, False, 18),
+    (1, 17, 33, 384, True, 19),
     (1, 3, 37, 64, False, 11),
     (2, 3, 37, 128, True, 12),
     (1, 5, 300, 320, True, 13),
