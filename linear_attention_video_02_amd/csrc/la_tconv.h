@@ -50,7 +50,7 @@ struct TconvCfg {
     static constexpr int UROWS = (FMAX + 2) * S;         // frame-union rows per chunk
     static constexpr int WSTAGE = BN * BK;               // bf16 elements of a W slice
     static constexpr int XSTAGE = UROWS * BK;            // bf16 elements of a union chunk
-    static constexpr int LDS_BYTES = 2 * (WSTAGE + XSTAGE) * 2;
+    static constexpr int LDS_BYTES = (3 * WSTAGE + 2 * XSTAGE) * 2;  // 160 KB, all of it
 };
 
 // The cache after a block: its last input frame, X[b][T-1] -> cache[b].

@@ -10,11 +10,49 @@
 // chunk) and the loaders' writes (8 whole rows) spread over all banks.
 __device__ __forceinline__ int tc_off(int row, int c) { return row * 64 + ((c ^ (row & 7)) << 3); }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 15] (expcnt and lgkmcnt
+// left unconstrained): vector-memory operations of this wave may stay in
+// flight, the oldest first to complete.  The LDS-DMA loads below are counted
+// by vmcnt but not tracked by the compiler, so their completion is awaited here.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+#define LA_VMCNT_CASE(k) case k: __builtin_amdgcn_s_waitcnt(0x0F70 | k); break;
+        LA_VMCNT_CASE(0) LA_VMCNT_CASE(1) LA_VMCNT_CASE(2) LA_VMCNT_CASE(3)
+        LA_VMCNT_CASE(4) LA_VMCNT_CASE(5) LA_VMCNT_CASE(6) LA_VMCNT_CASE(7)
+        LA_VMCNT_CASE(8) LA_VMCNT_CASE(9) LA_VMCNT_CASE(10) LA_VMCNT_CASE(11)
+        LA_VMCNT_CASE(12) LA_VMCNT_CASE(13) LA_VMCNT_CASE(14)
+#undef LA_VMCNT_CASE
+        default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15); break;
+    }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier without the memory model's fences.  A release fence on
+// LDS would drain vmcnt (it counts the LDS-DMA loads as LDS stores in flight)
+// and so every prefetch at each barrier.  Here LDS is written only by those
+// loads, whose completion each wave awaits itself (wait_vmcnt) before the
+// barrier, and every LDS read has returned before its value is used, ahead of
+// the barrier.  The empty asm statements keep the compiler from moving memory
+// operations across it.
+__device__ __forceinline__ void dma_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One wave-wide LDS-DMA load: lane i reads 16 bytes at byte offset off of
+// the buffer r and writes them to LDS at dst + 16 i (dst wave-uniform).
+// Offsets past the buffer's range write zeros.
+__device__ __forceinline__ void dma16(BufRsrc r, uint32_t off, uint16_t* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvArgs a) {
     using C = TconvCfg;
     extern __shared__ __align__(16) uint16_t lds[];
-    uint16_t* const wbuf0 = lds;                          // W slice of a stage, two buffers
-    uint16_t* const xbuf0 = lds + 2 * C::WSTAGE;          // frame union of a chunk, two buffers
+    uint16_t* const wbuf0 = lds;                          // W slice of a stage, three buffers
+    uint16_t* const xbuf0 = lds + 3 * C::WSTAGE;          // frame union of a chunk, two buffers
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -44,71 +82,56 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
     const int pt = mt % a.npt, ft = (mt / a.npt) % a.nft, bb = mt / (a.npt * a.nft);
     const int f0 = ft * F, p0 = pt * C::S, n0 = nt * C::BN;
 
-    // Loaders.  Thread (lr, lc) = (tid / 8, tid % 8) moves 16-byte chunk lc of
-    // W rows lr + 64 j (j < 2; j = 2 for waves 0-3) and of union rows
-    // 128 s + lr + 64 j in piece s (j < 2; j = 2 in piece 2 for waves 0-1,
-    // rows 384..399).  kOob (past every buffer's range) reads as zeros:
-    // channels past D, positions past P, frames past the block (its zero
-    // padding frame) and union rows past frame f0 + F.  Union frame f0 - 1 = -1
-    // (a block's first tile) reads the cache.
+    // Loads go straight from memory into LDS (LDS DMA), 8 rows of 128 bytes
+    // per wave instruction: lane i fills row 8 q + i / 8 at slot i % 8, which
+    // under the swizzle holds chunk c = (i % 8) ^ (i / 8).  W slice: 20
+    // instructions, q = wave + 8 j (3 per wave for waves 0-3, else 2).  Union:
+    // 50, q = wave + 8 j (7 for waves 0-1, else 6).  kOob (past every buffer's
+    // range) loads zeros: channels past D, positions past P, frames past the
+    // block (its zero padding frame) and union rows past frame f0 + F.  Union
+    // frame -1 (a block's first tiles, union rows 0..39 = instructions 0..4)
+    // comes from the cache.
     constexpr uint32_t kOob = 0x80000000u;
     const BufRsrc rX = make_rsrc(a.X, (uint32_t)((size_t)a.M * D * 2));
     const BufRsrc rC = make_rsrc(a.cache, (uint32_t)((size_t)(a.M / (T * P)) * P * D * 2));
     const BufRsrc rW = make_rsrc(a.W, (uint32_t)((size_t)3 * D * D * 2));
-    const int lr = tid >> 3, lc = tid & 7;
-    uint32_t wo[3], xo[7], co = kOob;
+    const uint32_t cb = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));  // byte offset of this lane's chunk
+    const int nw = wave < 4 ? 3 : 2, nx = wave < 2 ? 7 : 6;
+    uint32_t wo[3], xo[7];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-        const int n = n0 + lr + 64 * j;
-        wo[j] = (n < D && lr + 64 * j < C::BN) ? (uint32_t)n * (uint32_t)D * 2u + 16u * lc : kOob;
+        const int row = 8 * (wave + 8 * j) + (lane >> 3), n = n0 + row;
+        wo[j] = (j < nw && n < D) ? (uint32_t)n * (uint32_t)D * 2u + cb : kOob;
     }
+    const bool from_cache = f0 == 0 && wave < 5;  // instruction j = 0 of waves 0-4: union frame -1
 #pragma unroll
-    for (int k = 0; k < 7; ++k) {  // union rows of pieces 0 (k 0,1), 1 (k 2,3), 2 (k 4,5,6)
-        const int u = k < 2 ? lr + 64 * k : k < 4 ? 128 + lr + 64 * (k - 2) : 256 + lr + 64 * (k - 4);
+    for (int j = 0; j < 7; ++j) {
+        const int u = 8 * (wave + 8 * j) + (lane >> 3);
         const int ip = u / C::S, q = u - ip * C::S;
         const int f = f0 - 1 + ip, p = p0 + q;
-        const bool ok = u < C::UROWS && ip <= F + 1 && p < P;
-        xo[k] = (ok && f >= 0 && f < T) ? (uint32_t)((bb * T + f) * P + p) * (uint32_t)D * 2u + 16u * lc : kOob;
-        if (k == 0 && ok && f == -1) co = (uint32_t)(bb * P + p) * (uint32_t)D * 2u + 16u * lc;
+        const bool ok = j < nx && ip <= F + 1 && p < P;
+        if (j == 0 && from_cache)
+            xo[j] = p < P ? (uint32_t)(bb * P + p) * (uint32_t)D * 2u + cb : kOob;
+        else
+            xo[j] = (ok && f >= 0 && f < T) ? (uint32_t)((bb * T + f) * P + p) * (uint32_t)D * 2u + cb : kOob;
     }
-    const bool cache_rows = f0 == 0 && wave < 5;  // wave-uniform: union rows 0..39 of piece 0
     const int nkk = D / C::BK, KT = 3 * nkk;
-
-    u32x4 rw[3], rx[3];
-    auto load_w = [&](int t) {  // W slice of stage t = (chunk t / 3, offset t % 3)
+    auto dma_w = [&](int t, int buf) {  // W slice of stage t = (chunk t / 3, offset t % 3)
         const int kk = t / 3, seg = t - 3 * kk;
         const uint32_t wk = (uint32_t)seg * (uint32_t)D * (uint32_t)D * 2u + (uint32_t)kk * (C::BK * 2);
-        rw[0] = buf_load16(rW, wo[0] + wk);
-        rw[1] = buf_load16(rW, wo[1] + wk);
-        if (wave < 4) rw[2] = buf_load16(rW, wo[2] + wk);
+        uint16_t* dst = wbuf0 + buf * C::WSTAGE + 8 * 64 * wave;
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < nw) dma16(rW, wo[j] + wk, dst + j * 8 * 8 * 64);
     };
-    auto load_x = [&](int kk, int piece) {  // piece of the union of chunk kk
+    auto dma_x = [&](int kk, int buf) {  // frame union of chunk kk
         const uint32_t kb = (uint32_t)kk * (C::BK * 2);
-        if (piece == 0) {
-            rx[0] = buf_load16(rX, xo[0] + kb);
-            if (cache_rows) rx[0] |= buf_load16(rC, co + kb);
-            rx[1] = buf_load16(rX, xo[1] + kb);
-        } else if (piece == 1) {
-            rx[0] = buf_load16(rX, xo[2] + kb);
-            rx[1] = buf_load16(rX, xo[3] + kb);
-        } else {
-            rx[0] = buf_load16(rX, xo[4] + kb);
-            rx[1] = buf_load16(rX, xo[5] + kb);
-            if (wave < 2) rx[2] = buf_load16(rX, xo[6] + kb);
+        uint16_t* dst = xbuf0 + buf * C::XSTAGE + 8 * 64 * wave;
+#pragma unroll
+        for (int j = 0; j < 7; ++j) {
+            if (j >= nx) break;
+            dma16((j == 0 && from_cache) ? rC : rX, xo[j] + kb, dst + j * 8 * 8 * 64);
         }
-    };
-    auto store_w = [&](int buf) {
-        uint16_t* st = wbuf0 + buf * C::WSTAGE;
-        *(u32x4*)(st + tc_off(lr, lc)) = rw[0];
-        *(u32x4*)(st + tc_off(lr + 64, lc)) = rw[1];
-        if (wave < 4) *(u32x4*)(st + tc_off(lr + 128, lc)) = rw[2];
-    };
-    auto store_x = [&](int buf, int piece) {
-        uint16_t* st = xbuf0 + buf * C::XSTAGE;
-        const int u0 = 128 * piece + lr;
-        *(u32x4*)(st + tc_off(u0, lc)) = rx[0];
-        *(u32x4*)(st + tc_off(u0 + 64, lc)) = rx[1];
-        if (piece == 2 && wave < 2) *(u32x4*)(st + tc_off(u0 + 128, lc)) = rx[2];
     };
 
     // Compute role: wave (wn, wm) owns channels 80 wn .. +79 and tile rows
@@ -122,26 +145,33 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
 #pragma unroll
         for (int j = 0; j < C::WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Pipeline.  Stage t = (chunk kk, offset seg) computes from W buffer t & 1
-    // and union buffer kk & 1.  At its end it stores what the previous stage's
-    // loads brought (W of stage t + 1, piece seg of the union of chunk kk + 1;
-    // both buffers' readers passed the last barrier) and loads W of stage t + 2
-    // and the next piece.
-    load_w(0);
-    store_w(0);
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-        load_x(0, s);
-        store_x(0, s);
-    }
-    if (KT > 1) load_w(1);
-    if (nkk > 1) load_x(1, 0);
-    lds_barrier();
+    // Pipeline.  Stage t = (chunk kk, offset seg) computes from W buffer
+    // t % 3 = seg and union buffer kk & 1.  At its start it issues the loads
+    // of W for stage t + 2 (into buffer (t + 2) % 3, whose readers, stage
+    // t - 1, passed the last barrier) and, at seg 0, of the union of chunk
+    // kk + 1 (into buffer (kk + 1) & 1, free since chunk kk - 1 ended): two
+    // and three stages ahead of their use.  Before its closing barrier each
+    // wave waits for its own loads other than those just issued, which covers
+    // everything stage t + 1 reads.
+    dma_x(0, 0);
+    dma_w(0, 0);
+    if (KT > 1) dma_w(1, 1);
+    wait_vmcnt(KT > 1 ? nw : 0);
+    dma_barrier();
     for (int kk = 0; kk < nkk; ++kk) {
 #pragma unroll
-        for (int seg = 0; seg < 3; ++seg) {  // unrolled: the union piece is a constant
+        for (int seg = 0; seg < 3; ++seg) {  // unrolled: buffer indices are constants
             const int t = 3 * kk + seg;
-            const uint16_t* wb = wbuf0 + (t & 1) * C::WSTAGE;
+            int issued = 0;
+            if (seg == 0 && kk + 1 < nkk) {
+                dma_x(kk + 1, (kk + 1) & 1);
+                issued += nx;
+            }
+            if (t + 2 < KT) {
+                dma_w(t + 2, (seg + 2) % 3);
+                issued += nw;
+            }
+            const uint16_t* wb = wbuf0 + seg * C::WSTAGE;
             const uint16_t* xb = xbuf0 + (kk & 1) * C::XSTAGE;
 #pragma unroll
             for (int ks = 0; ks < C::BK / 32; ++ks) {
@@ -157,17 +187,8 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[j], acc[i][j], 0, 0, 0);
                 }
             }
-            if (t + 1 < KT) store_w((t + 1) & 1);
-            if (kk + 1 < nkk) store_x((kk + 1) & 1, seg);
-            if (t + 2 < KT) load_w(t + 2);
-            // the piece the next stage stores: piece seg + 1 of chunk kk + 1, or
-            // piece 0 of chunk kk + 2
-            if (seg < 2) {
-                if (kk + 1 < nkk) load_x(kk + 1, seg + 1);
-            } else {
-                if (kk + 2 < nkk) load_x(kk + 2, 0);
-            }
-            lds_barrier();
+            wait_vmcnt(issued);
+            dma_barrier();
         }
     }
 
