@@ -42,30 +42,38 @@ def kernel_source_hash():
 STATE_KERNELS = ("la_state_bf16_kernel",)
 COMBINE_KERNEL = "la_state_combine_kernel"
 APPLY_KERNELS = ("la_apply_bf16_kernel",)
-OUR_KERNELS = STATE_KERNELS + (COMBINE_KERNEL,) + APPLY_KERNELS
+TCONV_KERNELS = ("la_tconv_bf16_kernel",)
+OUR_KERNELS = STATE_KERNELS + (COMBINE_KERNEL,) + APPLY_KERNELS + TCONV_KERNELS
 CALIB_KERNEL = "MulFunctor"   # torch's elementwise o = q * 1: a plain copy of known size
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_720p5s.json")
-
-# The profiler runs whose summaries are committed (run from /tmp, with the
-# repository at $REPO); the summaries are then written by --summarize-*.
-PROFILE_COMMANDS = {
-    "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/la_prof/trace -o trace "
-             "-- python3 $REPO/bench.py --steps 50 --warmup 5 --no-cpu-baseline",
-    "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/la_prof/fetch -o fetch "
-             "-- python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
-    "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/la_prof/write -o write "
-             "-- python3 $REPO/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
-}
+LIBGEMM_KERNEL = "Cijk_"      # hipBLASLt's GEMM kernels (context for the temporal convolution)
 
 
-def load_traffic(kernels, src_hash):
+def traffic_json(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def profile_commands(workload):
+    """The profiler runs whose summaries are committed (run from /tmp, with the
+    repository at $REPO); the summaries are then written by --summarize-*."""
+    wl = "" if workload == WORKLOAD else f" --workload {workload}"
+    return {
+        "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/la_prof/trace -o trace "
+                 f"-- python3 $REPO/bench.py{wl} --steps 50 --warmup 5 --no-cpu-baseline",
+        "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/la_prof/fetch -o fetch "
+                 f"-- python3 $REPO/bench.py{wl} --steps 10 --warmup 2 --no-cpu-baseline",
+        "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/la_prof/write -o write "
+                 f"-- python3 $REPO/bench.py{wl} --steps 10 --warmup 2 --no-cpu-baseline",
+    }
+
+
+def load_traffic(kernels, src_hash, workload=WORKLOAD):
     """HBM bytes per launch of a pass from the committed counter summary, or None.
 
     The summary records the kernel-source hash it was taken with; if the
     kernels changed since, the counters no longer describe them.
     """
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(traffic_json(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -216,10 +224,19 @@ def _short(name):
             return k
     if CALIB_KERNEL in name:
         return "calibration copy (torch mul by 1)"
+    if name.startswith(LIBGEMM_KERNEL):
+        return "hipBLASLt GEMM (torch.matmul, context)"
     return None
 
 
-def summarize_trace(trace_dir, command, out_path):
+WORKLOAD_TITLES = {
+    WORKLOAD: "720p5s workload (bf16, B=2 H=32 N=19320 d=64, RoPE)",
+    "tconv720p": "tconv720p workload (temporal convolution, bf16, one block of 24 frames x 920 "
+                 "positions, D=2240, bias)",
+}
+
+
+def summarize_trace(trace_dir, command, out_path, workload=WORKLOAD):
     """Per-kernel durations of the timed steps from a rocprofv3 --kernel-trace run."""
     import csv
     rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
@@ -231,13 +248,13 @@ def summarize_trace(trace_dir, command, out_path):
         dur.setdefault(_short(r["Kernel_Name"]), []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     stats = list(csv.DictReader(open(_find(trace_dir, "kernel_stats.csv"))))
-    lines = [f"# Kernel durations, {WORKLOAD} workload (bf16, B=2 H=32 N=19320 d=64, RoPE)", "",
+    lines = [f"# Kernel durations, {WORKLOAD_TITLES[workload]}", "",
              "Command (from the repository root, one MI355X):", "", "```", command, "```", "",
              "rocprofv3 --stats summary, this library's kernels (all launches, warm-up included):", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for st in stats:
         k = _short(st["Name"])
-        if k in OUR_KERNELS:
+        if k in OUR_KERNELS or (k or "").startswith("hipBLASLt"):
             lines.append(f"| {k} | {st['Calls']} | {float(st['AverageNs']) / 1e3:.1f} | "
                          f"{float(st['MinNs']) / 1e3:.1f} | {float(st['MaxNs']) / 1e3:.1f} |")
     # per step, from the trace: state kernel start .. (combine end) .. apply end
@@ -266,7 +283,8 @@ def summarize_trace(trace_dir, command, out_path):
     return steps
 
 
-def summarize_pmc(fetch_dir, write_dir, commands, out_json, out_md, src_hash, tensor_bytes):
+def summarize_pmc(fetch_dir, write_dir, commands, out_json, out_md, src_hash, tensor_bytes, algo=None,
+                  workload=WORKLOAD):
     """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs, scaled by a copy kernel.
 
     Both counters are in KiB per dispatch.  The calibration kernel reads
@@ -291,7 +309,8 @@ def summarize_pmc(fetch_dir, write_dir, commands, out_json, out_md, src_hash, te
         raise SystemExit("calibration copy kernel missing from the counter runs")
     f_scale = tensor_bytes / fetch[cal]
     w_scale = tensor_bytes / write[cal]
-    algo = {"la_state_bf16_kernel": 2 * tensor_bytes, "la_apply_bf16_kernel": 2 * tensor_bytes}
+    if algo is None:
+        algo = {"la_state_bf16_kernel": 2 * tensor_bytes, "la_apply_bf16_kernel": 2 * tensor_bytes}
     kernels = {}
     for k in OUR_KERNELS:
         if k in fetch and k in write:
@@ -299,12 +318,12 @@ def summarize_pmc(fetch_dir, write_dir, commands, out_json, out_md, src_hash, te
             kernels[k] = {"fetch_bytes_raw": fetch[k], "write_bytes_raw": write[k],
                           "read_bytes": rd, "write_bytes": wr, "hbm_bytes_per_launch": rd + wr,
                           "algorithmic_bytes": algo.get(k)}
-    out = {"workload": WORKLOAD, "src_hash": src_hash, "fetch_scale": f_scale, "write_scale": w_scale,
+    out = {"workload": workload, "src_hash": src_hash, "fetch_scale": f_scale, "write_scale": w_scale,
            "calibration": f"{cal}: reads {tensor_bytes} B and writes {tensor_bytes} B per launch",
            "commands": commands, "kernels": kernels}
     with open(out_json, "w") as f:
         json.dump(out, f, indent=1)
-    lines = [f"# HBM traffic per launch, {WORKLOAD} workload", "", "Commands (repository root, one MI355X):",
+    lines = [f"# HBM traffic per launch, {workload} workload", "", "Commands (repository root, one MI355X):",
              "", "```", *commands, "```", "",
              f"Scale factors from the calibration copy (reads and writes {tensor_bytes / 1e6:.1f} MB): "
              f"FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.", "",
@@ -338,20 +357,34 @@ def main():
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"), help="where summaries go")
     args = ap.parse_args()
     if args.summarize_trace or args.summarize_pmc:
-        from linear_attention_video_02_amd.inputs import WORKLOADS
-        w = WORKLOADS[WORKLOAD]
-        tensor_bytes = w["B"] * w["H"] * w["N"] * w["d"] * 2
+        wlname = args.workload
+        if wlname not in WORKLOAD_TITLES:
+            raise SystemExit(f"no profile summary for workload {wlname}")
+        wlflag = "" if wlname == WORKLOAD else f" --workload {wlname}"
+        algo = None
+        if wlname == "tconv720p":
+            from linear_attention_video_02_amd.inputs import TCONV
+            w = TCONV[wlname]
+            tensor_bytes = w["B"] * w["T"] * w["P"] * w["D"] * 2  # the calibration copy moves X
+            # minimum HBM bytes of one launch: X and W read once, Y written once
+            algo = {"la_tconv_bf16_kernel": 2 * tensor_bytes + 3 * w["D"] * w["D"] * 2}
+        else:
+            from linear_attention_video_02_amd.inputs import WORKLOADS
+            w = WORKLOADS[wlname]
+            tensor_bytes = w["B"] * w["H"] * w["N"] * w["d"] * 2
+        cmds_ = profile_commands(wlname)
         os.makedirs(args.out, exist_ok=True)
         if args.summarize_trace:
             summarize_trace(args.summarize_trace,
-                            PROFILE_COMMANDS["trace"] + "\npython3 bench.py --summarize-trace /tmp/la_prof/trace",
-                            os.path.join(args.out, f"kernels_{WORKLOAD}.md"))
+                            cmds_["trace"] + f"\npython3 bench.py{wlflag} --summarize-trace /tmp/la_prof/trace",
+                            os.path.join(args.out, f"kernels_{wlname}.md"), wlname)
         if args.summarize_pmc:
-            cmds = [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"],
-                    "python3 bench.py --summarize-pmc /tmp/la_prof/fetch /tmp/la_prof/write"]
+            cmds = [cmds_["fetch"], cmds_["write"],
+                    f"python3 bench.py{wlflag} --summarize-pmc /tmp/la_prof/fetch /tmp/la_prof/write"]
             summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], cmds,
-                          os.path.join(args.out, f"traffic_{WORKLOAD}.json"),
-                          os.path.join(args.out, f"traffic_{WORKLOAD}.md"), kernel_source_hash(), tensor_bytes)
+                          os.path.join(args.out, f"traffic_{wlname}.json"),
+                          os.path.join(args.out, f"traffic_{wlname}.md"), kernel_source_hash(), tensor_bytes,
+                          algo, wlname)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
@@ -401,7 +434,7 @@ def main():
     rf = wl.get("roofline", {"bound": "hbm", "peak": HBM_PEAK_GBPS, "unit": "GB/s", "scale": 1e9})
     achieved = nbytes / (dur_ms * 1e-3) / rf["scale"]
     src_hash = kernel_source_hash()
-    traffic = load_traffic(kernels, src_hash) if args.workload == WORKLOAD else None
+    traffic = load_traffic(kernels, src_hash, args.workload)
 
     # Calibration copy o = q * 1 over rotating buffers: a plain elementwise
     # copy of known size (reads and writes copy_bytes), timed as the practical
