@@ -139,11 +139,17 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
     // l % 16 of a 16-row block at k chunk l / 16 (8 consecutive k).
     const int wn = wave & 1, wm = wave >> 1;
     const int fr = lane & 15, fc = lane >> 4;
+    // Accumulators start at the bias (4 consecutive channels per lane); the
+    // shortcut X is added from LDS at the stage that holds it (below).
     f32x4 acc[C::WN][C::WM];
 #pragma unroll
-    for (int i = 0; i < C::WN; ++i)
+    for (int i = 0; i < C::WN; ++i) {
+        const int n = n0 + 80 * wn + 16 * i + 4 * fc;
+        f32x4 b0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.bias && n < D) b0 = *(const f32x4*)(a.bias + n);
 #pragma unroll
-        for (int j = 0; j < C::WM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < C::WM; ++j) acc[i][j] = b0;
+    }
 
     // Pipeline.  Stage t = (chunk kk, offset seg) computes from W buffer
     // t % 3 = seg and union buffer kk & 1.  At its start it issues the loads
@@ -187,33 +193,54 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[j], acc[i][j], 0, 0, 0);
                 }
             }
+            if (seg == 1) {
+                // The shortcut: the union's own-frame rows of chunk kk hold X for the
+                // 16-channel blocks of this wave that fall in the chunk (a block never
+                // straddles two chunks).  Each lane adds its token's 4 channels.
+#pragma unroll
+                for (int i = 0; i < C::WN; ++i) {
+                    const int nb = n0 + 80 * wn + 16 * i;  // wave-uniform
+                    if ((nb >> 6) != kk) continue;
+                    const int e = (nb & 63) + 4 * fc;      // element within the chunk's 64
+#pragma unroll
+                    for (int j = 0; j < C::WM; ++j) {
+                        const uint2 xv =
+                            *(const uint2*)(xb + tc_off(80 * wm + 16 * j + fr + C::S, e >> 3) + (e & 7));
+                        acc[i][j] += f32x4{bf_lo(xv.x), bf_hi(xv.x), bf_lo(xv.y), bf_hi(xv.y)};
+                    }
+                }
+            }
             wait_vmcnt(issued);
             dma_barrier();
         }
     }
 
-    // Epilogue: lane holds C[n][m] for the token of tile row .. + lane % 16 and
-    // channels n = .. + 4 (lane / 16) + (0..3): 4 consecutive channels of one token.
+    // Epilogue.  Lane holds Y[m][n .. n + 3] (bias and shortcut already in)
+    // for the token of tile row .. + lane % 16 and channels n = .. + 4 (lane /
+    // 16).  The tile is rounded to bf16 into LDS (free now: every wave passed
+    // the last barrier, and no load is in flight), rows of 168 elements so the
+    // 16 rows of one write land in distinct banks, then written out as 16-byte
+    // pieces, 20 per token row of 160 channels, so that every store
+    // instruction moves whole row segments.
+    constexpr int YROW = 168;
+    uint16_t* const ys = lds;
 #pragma unroll
-    for (int j = 0; j < C::WM; ++j) {
-        const int r = 80 * wm + 16 * j + fr, i = r / C::S, q = r - i * C::S;
-        const int f = f0 + i, p = p0 + q;
-        if (i >= F || f >= T || p >= P) continue;
-        const int m = (bb * T + f) * P + p;
+    for (int j = 0; j < C::WM; ++j)
 #pragma unroll
         for (int i2 = 0; i2 < C::WN; ++i2) {
-            const int n = n0 + 80 * wn + 16 * i2 + 4 * fc;
-            if (n >= D) continue;
-            const size_t o = (size_t)m * D + n;
-            const uint2 xv = *(const uint2*)(a.X + o);
-            float4 bv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (a.bias) bv = *(const float4*)(a.bias + n);
-            const float y0 = bf_lo(xv.x) + acc[i2][j][0] + bv.x;
-            const float y1 = bf_hi(xv.x) + acc[i2][j][1] + bv.y;
-            const float y2 = bf_lo(xv.y) + acc[i2][j][2] + bv.z;
-            const float y3 = bf_hi(xv.y) + acc[i2][j][3] + bv.w;
-            *(uint2*)(a.Y + o) = make_uint2(pack_bf16(y0, y1), pack_bf16(y2, y3));
+            const f32x4 y = acc[i2][j];
+            *(uint2*)(ys + (80 * wm + 16 * j + fr) * YROW + 80 * wn + 16 * i2 + 4 * fc) =
+                make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
         }
+    lds_barrier();
+    constexpr int PIECES = C::BM * (C::BN / 8);
+#pragma unroll 4
+    for (int c = tid; c < PIECES; c += C::THREADS) {
+        const int r = c / (C::BN / 8), k = c - r * (C::BN / 8);
+        const int i = r / C::S, q = r - i * C::S;
+        const int f = f0 + i, p = p0 + q, n = n0 + 8 * k;
+        if (i >= F || f >= T || p >= P || n >= D) continue;
+        *(u32x4*)(a.Y + (size_t)((bb * T + f) * P + p) * D + n) = *(const u32x4*)(ys + r * YROW + 8 * k);
     }
 }
 
