@@ -25,13 +25,18 @@ sys.path.insert(0, ROOT)
 METRIC = "linear-attn tokens/sec and achieved HBM GB/s (% peak), 720p-5s shape, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "720p5s"
-SRC_FILES = ["la_common.h", "la_state.h", "la_apply.h", "la_causal.h", "la_tconv.h", "la_api.hip", "la_tconv.hip"]
+# The sources each workload's kernels are built from (their hash tags the
+# committed counter summaries).
+SRC_FILES = {
+    "attention": ["la_common.h", "la_state.h", "la_apply.h", "la_causal.h", "la_api.hip"],
+    "tconv": ["la_common.h", "la_tconv.h", "la_tconv.hip", "la_api.hip"],
+}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 
 
-def kernel_source_hash():
+def kernel_source_hash(workload=None):
     h = hashlib.sha256()
-    for f in SRC_FILES:
+    for f in SRC_FILES["tconv" if workload == "tconv720p" else "attention"]:
         with open(os.path.join(ROOT, "linear_attention_video_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -383,7 +388,7 @@ def main():
                     f"python3 bench.py{wlflag} --summarize-pmc /tmp/la_prof/fetch /tmp/la_prof/write"]
             summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], cmds,
                           os.path.join(args.out, f"traffic_{wlname}.json"),
-                          os.path.join(args.out, f"traffic_{wlname}.md"), kernel_source_hash(), tensor_bytes,
+                          os.path.join(args.out, f"traffic_{wlname}.md"), kernel_source_hash(wlname), tensor_bytes,
                           algo, wlname)
         return
     if args.gpus != 1:
@@ -433,7 +438,7 @@ def main():
     dur_ms = group_ms[g]
     rf = wl.get("roofline", {"bound": "hbm", "peak": HBM_PEAK_GBPS, "unit": "GB/s", "scale": 1e9})
     achieved = nbytes / (dur_ms * 1e-3) / rf["scale"]
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(args.workload)
     traffic = load_traffic(kernels, src_hash, args.workload)
 
     # Calibration copy o = q * 1 over rotating buffers: a plain elementwise
