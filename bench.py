@@ -117,16 +117,48 @@ def cpu_baseline(q, k, v, spec, budget_s=12.0):
         t_used += time.perf_counter() - t0
         slices += 1
     tokens = slices * N / H  # a token is one grid position across all H heads
+    one = _one_thread(lambda qh, kh, vh: oracle.apply(qh, *oracle.state(kh, vh, grid), grid, eps),
+                      [host[o] for o in order if o in host], N / H, budget_s / 4)
     return {
         "value": tokens / t_used,
         "unit": "tokens/s",
         "cores": int(blas_threads),
         "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "one_thread": one,
         "sample": f"{slices} (batch, head) slices of the {WORKLOAD} workload in order "
                   f"({slices / len(order):.1f} passes over its {len(order)} slices), all {N} "
                   f"tokens each, fp64 numpy, {t_used:.1f} s of oracle time "
                   f"({len(os.sched_getaffinity(0))} host cores visible)",
     }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _one_thread(fn, samples, tokens_per_sample, budget_s):
+    """The same oracle work with BLAS limited to one thread, over the first
+    samples again, until about budget_s: tokens/s and what was run."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        return None
+    done, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s and samples:
+            t0 = time.perf_counter()
+            fn(*samples[done % len(samples)])
+            t_used += time.perf_counter() - t0
+            done += 1
+    return {"value": done * tokens_per_sample / t_used, "unit": "tokens/s", "cores": 1,
+            "sample": f"{done} of the same samples, {t_used:.1f} s, BLAS limited to 1 thread"}
 
 
 def cpu_baseline_tconv(X, W, cache, bias, spec, budget_s=12.0):
@@ -154,11 +186,16 @@ def cpu_baseline_tconv(X, W, cache, bias, spec, budget_s=12.0):
         oracle.temporal_conv(Xs, Wh, cs, bh)
         t_used += time.perf_counter() - t0
         done += p1 - p0
+    samp = [(X[0:1, :, q0:q0 + per].float().cpu().numpy().astype(np.float64),
+             cache[0:1, q0:q0 + per].float().cpu().numpy().astype(np.float64)) for q0 in range(0, min(P, 4 * per), per)]
+    one = _one_thread(lambda xs, cs: oracle.temporal_conv(xs, Wh, cs, bh), samp, per * T, budget_s / 4)
     return {
         "value": done * T / t_used,
         "unit": "tokens/s",
         "cores": int(blas_threads),
         "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "one_thread": one,
         "sample": f"{done} of the block's {B * P} spatial positions, all {T} frames each "
                   f"({done * T} tokens), fp64 numpy, {t_used:.1f} s of oracle time "
                   f"({len(os.sched_getaffinity(0))} host cores visible)",
@@ -344,6 +381,45 @@ def summarize_pmc(fetch_dir, write_dir, commands, out_json, out_md, src_hash, te
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA GRBM_GUI_ACTIVE"
+
+
+def summarize_counters(dirs, out_path):
+    """MFMA utilisation per kernel from rocprofv3 --pmc runs of MFMA_COUNTERS.
+
+    SQ_VALU_MFMA_BUSY_CYCLES sums over the 4 SIMDs of every CU and
+    SQ_BUSY_CU_CYCLES over the CUs, so utilisation = busy / (4 * CU cycles).
+    """
+    import csv
+    lines = ["# MFMA utilisation of this library's kernels", "", "Commands (repository root, one MI355X):", "",
+             "```"]
+    for wl in dirs:
+        flag = "" if wl == WORKLOAD else f" --workload {wl}"
+        lines.append(f"cd /tmp && rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d /tmp/la_prof/mfma_{wl} "
+                     f"-o p -- python3 $REPO/bench.py{flag} --steps 10 --warmup 2 --no-cpu-baseline")
+    lines += ["python3 bench.py --summarize-counters " + " ".join(f"{w}=/tmp/la_prof/mfma_{w}" for w in dirs),
+              "```", "", "utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), mean over the dispatches "
+              "of each kernel (warm-up included).", "",
+              "| workload | kernel | dispatches | MFMA instructions | MFMA busy (SIMD cycles) | CU busy cycles | "
+              "utilisation |", "|---|---|---|---|---|---|---|"]
+    for wl, d in dirs.items():
+        acc = {}
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            k = _short(r["Kernel_Name"])
+            if k is None or k not in OUR_KERNELS:
+                continue
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for k, c in acc.items():
+            mean = {n: sum(v) / len(v) for n, v in c.items()}
+            busy, cu = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), mean.get("SQ_BUSY_CU_CYCLES", 0.0)
+            util = busy / (4 * cu) if cu else 0.0
+            lines.append(f"| {wl} | {k} | {len(c.get('SQ_BUSY_CU_CYCLES', []))} | {mean.get('SQ_INSTS_MFMA', 0):.0f} | "
+                         f"{busy:.3e} | {cu:.3e} | {100 * util:.1f}% |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,8 +435,15 @@ def main():
                     help="write the kernel-duration summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the HBM-traffic summary of rocprofv3 FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="WORKLOAD=DIR",
+                    help="write the MFMA-utilisation summary of rocprofv3 --pmc runs of " + MFMA_COUNTERS)
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"), help="where summaries go")
     args = ap.parse_args()
+    if args.summarize_counters:
+        os.makedirs(args.out, exist_ok=True)
+        summarize_counters(dict(x.split("=", 1) for x in args.summarize_counters),
+                           os.path.join(args.out, "mfma_utilisation.md"))
+        return
     if args.summarize_trace or args.summarize_pmc:
         wlname = args.workload
         if wlname not in WORKLOAD_TITLES:
@@ -457,6 +540,17 @@ def main():
     tev.record(c1)
     torch.cuda.synchronize()
     copy_gbps = 2 * copy_bytes / (tev.ms(c0, c1) / n_copy * 1e-3) / 1e9
+    # the same copy through this library's plain copy kernel (la_stream_copy)
+    for i in range(3):
+        la.stream_copy(pairs[i % len(pairs)][0], pairs[i % len(pairs)][1])
+    torch.cuda.synchronize()
+    c2, c3 = tev.new(), tev.new()
+    tev.record(c2)
+    for i in range(n_copy):
+        la.stream_copy(pairs[i % len(pairs)][0], pairs[i % len(pairs)][1])
+    tev.record(c3)
+    torch.cuda.synchronize()
+    copy_repo_gbps = 2 * copy_bytes / (tev.ms(c2, c3) / n_copy * 1e-3) / 1e9
     tev.close()
 
     out = {
@@ -493,6 +587,8 @@ def main():
                   f"on every {every}th timed step ({len(evs)} samples)",
         "copy_GBps": copy_gbps,
         "copy_kind": "torch mul by 1 (read + write, rotating buffers)",
+        "copy_repo_GBps": copy_repo_gbps,
+        "copy_repo_kind": "la_stream_copy: this library's plain 16-byte-per-lane copy, same buffers",
         "wall_s": wall,
         "src_hash": src_hash,
     }

@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.la_token_causal.restype = ci
         L.la_temporal_conv_step.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
         L.la_temporal_conv_step.restype = ci
+        L.la_stream_copy.argtypes = [vp, vp, cs, vp]
+        L.la_stream_copy.restype = ci
         L.la_strerror.argtypes = [ci]
         L.la_strerror.restype = ctypes.c_char_p
         L.la_last_hip_error.argtypes = []
@@ -301,3 +303,17 @@ def temporal_conv_step(x, W, cache, bias=None, commit=True, out=None):
     if rc:
         raise LinAttnError(rc, "la_temporal_conv_step")
     return out
+
+
+def stream_copy(src, dst):
+    """Plain device copy src -> dst (same size, contiguous): the library's
+    reference stream for the practical HBM ceiling (a measurement utility)."""
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous GPU tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    rc = lib().la_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src))
+    if rc:
+        raise LinAttnError(rc, "la_stream_copy")
+    return dst

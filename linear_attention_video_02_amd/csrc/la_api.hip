@@ -15,6 +15,16 @@
 #include "la_state.h"
 #include "la_tconv.h"
 
+// A plain copy, one 16-byte piece per lane and one workgroup per 4 KB (the
+// fastest of the simple forms measured: grid-stride loops with 1 or 4 pieces
+// per iteration, with or without streaming stores, were 3-17% slower): the
+// reference for the practical HBM ceiling of a read + write stream
+// (la_stream_copy).
+__global__ __launch_bounds__(256) void la_copy_kernel(const u32x4* src, u32x4* dst, size_t n16) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) dst[i] = src[i];
+}
+
 namespace {
 
 constexpr int kMaxPartials = 64;         // state workgroups per (batch, head), upper bound
@@ -610,6 +620,22 @@ int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bi
     e = la_tconv_cache_launch(c, st);
     if (e != hipSuccess) return hip_fail(e, "la_tconv_cache_kernel launch");
     return LA_OK;
+}
+
+int la_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    if (bytes == 0) return LA_OK;
+    if (!src || !dst) return LA_E_NULLPTR;
+    if (!aligned16(src) || !aligned16(dst) || bytes % 16 != 0) return LA_E_ALIGN;
+    if (overlaps(src, bytes, dst, bytes)) return LA_E_ALIAS;
+    const size_t n16 = bytes / 16;
+    const size_t blocks = (n16 + 255) / 256;
+    if (blocks >= (1ull << 31)) return LA_E_UNSUPPORTED;
+    const unsigned grid = (unsigned)blocks;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(la_copy_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
+                       (u32x4*)dst, n16);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? LA_OK : hip_fail(e, "la_copy_kernel launch");
 }
 
 const char* la_last_hip_error(void) { return g_hip_msg; }

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
                           "la_block_causal_step", "la_token_causal", "la_temporal_conv_step",
-                          "la_strerror", "la_last_hip_error"}
+                          "la_stream_copy", "la_strerror", "la_last_hip_error"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -224,6 +224,14 @@ def test_temporal_conv_empty_is_noop(L):
     # no token: checks pass, nothing is launched, the (null) buffers are not touched
     assert tconv_call(L, T=0, X=None, Y=None, W=None, cache=None) == 0
     assert tconv_call(L, P=0, X=None, Y=None, W=None, cache=None) == 0
+
+
+def test_stream_copy_rejects(L):
+    assert L.la_stream_copy(p(0), p(1 << 30), 0, None) == 0          # nothing to copy
+    assert L.la_stream_copy(None, p(1 << 30), 64, None) == E["LA_E_NULLPTR"]
+    assert L.la_stream_copy(p(8), p(1 << 30), 64, None) == E["LA_E_ALIGN"]
+    assert L.la_stream_copy(p(0), p(1 << 30), 60, None) == E["LA_E_ALIGN"]
+    assert L.la_stream_copy(p(0), p(32), 64, None) == E["LA_E_ALIAS"]
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

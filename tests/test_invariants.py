@@ -225,3 +225,14 @@ def test_canaries_untouched(la):
     for buf, val in ((canary, -7.0), (Sbuf, 3.5), (zbuf, 3.5)):
         assert torch.all(buf[:pad] == val) and torch.all(buf[-pad:] == val)
     say("  canaries intact")
+
+
+def test_stream_copy_is_exact(la):
+    """The measurement copy (la_stream_copy) moves every byte, at a size that
+    is not a multiple of one sweep of the grid."""
+    import torch
+    src = torch.randint(0, 2**31 - 1, (5 * 1048576 + 20,), dtype=torch.int32, device="cuda:0")  # > one sweep (16 MB)
+    dst = torch.zeros_like(src)
+    la.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
