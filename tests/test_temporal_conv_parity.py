@@ -10,6 +10,8 @@ error of the linear-attention tests (2e-2) is checked as well.
 Inputs are bf16-exact (make_tconv / make_tconv_device), so the oracle sees
 exactly the values the kernel reads.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -140,3 +142,43 @@ def test_tconv720p_sampled_positions(la):
     ref, _ = oracle.temporal_conv(Xs, host(tW), cs, host(tb))
     check(host(out.index_select(2, idx)), ref, "tconv720p sampled positions")
     assert torch.equal(tc, tX[:, -1])
+
+
+def test_x_near_the_2gib_limit(la):
+    """Maximum size: X of 1.98 GB (20 blocks of 24 x 920 at D = 2240, just under
+    the 2 GiB the 32-bit buffer offsets allow), checked on sampled positions of
+    the first and the last batch element (offsets near 2^31 bytes)."""
+    import torch
+    B, T, P, D = 20, 24, 920, 2240
+    assert B * T * P * D * 2 < 2**31
+    say(f"[tconv max] B={B} T={T} P={P} D={D}: X {B * T * P * D * 2 / 1e9:.2f} GB")
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(77)
+    X = torch.empty((B, T, P, D), dtype=torch.bfloat16, device="cuda:0")
+    for b in range(B):  # draw per batch element to keep the fp32 temporaries small
+        X[b] = torch.randn((T, P, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    W = (torch.randn((3, D, D), generator=gen, device="cuda:0") / math.sqrt(3 * D)).to(torch.bfloat16)
+    cache = torch.randn((B, P, D), generator=gen, device="cuda:0").to(torch.bfloat16)
+    cache0 = cache.clone()
+    out = la.temporal_conv_step(X, W, cache, None, commit=True)
+    torch.cuda.synchronize()
+    pos = torch.tensor([0, 457, P - 1], device="cuda:0")
+    Wh = host(W)
+    for b in (0, B - 1):
+        ref, _ = oracle.temporal_conv(host(X[b:b + 1].index_select(2, pos)), Wh,
+                                      host(cache0[b:b + 1].index_select(1, pos)))
+        check(host(out[b:b + 1].index_select(2, pos)), ref, f"batch element {b}")
+    assert torch.equal(cache, X[:, -1])
+    del X, out, cache, cache0
+    torch.cuda.empty_cache()
+
+
+def test_wide_channels(la):
+    """D = 8192 (26 channel tiles, W of 402 MB): every output against the oracle."""
+    import torch
+    B, T, P, D = 1, 3, 2, 8192
+    X, W, cache, bias = make_tconv(B, T, P, D, 91)
+    out = la.temporal_conv_step(up(X), up(W), up(cache), up(bias, "fp32"), commit=False)
+    torch.cuda.synchronize()
+    ref, _ = oracle.temporal_conv(X, W, cache, bias)
+    check(host(out), ref, f"D={D}")
