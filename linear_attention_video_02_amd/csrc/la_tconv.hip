@@ -254,13 +254,11 @@ __global__ __launch_bounds__(256) void la_tconv_cache_kernel(TconvCacheArgs a) {
 }
 
 hipError_t la_tconv_launch(const TconvArgs& a, hipStream_t st) {
-    static bool attr_set = false;  // the attribute is per function; setting it twice is harmless
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)la_tconv_bf16_kernel,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, TconvCfg::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // set on every call (a host-side attribute, cheap): it must hold on the
+    // device current at this launch
+    const hipError_t e = hipFuncSetAttribute((const void*)la_tconv_bf16_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, TconvCfg::LDS_BYTES);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(la_tconv_bf16_kernel, dim3(a.mtiles * a.ntiles), dim3(TconvCfg::THREADS),
                        TconvCfg::LDS_BYTES, st, a);
     return hipGetLastError();
