@@ -179,20 +179,34 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
             }
             const uint16_t* wb = wbuf0 + seg * C::WSTAGE;
             const uint16_t* xb = xbuf0 + (kk & 1) * C::XSTAGE;
+            // The stage's fragments, both k steps: the second step's LDS reads
+            // are issued among the first step's MFMAs (scheduling groups below)
+            bf16x8 xf[2][C::WM], wfr[2][C::WN];
 #pragma unroll
             for (int ks = 0; ks < C::BK / 32; ++ks) {
-                bf16x8 xf[C::WM];
 #pragma unroll
                 for (int j = 0; j < C::WM; ++j)
-                    xf[j] = *(const bf16x8*)(xb + tc_off(80 * wm + 16 * j + fr + C::S * seg, 4 * ks + fc));
+                    xf[ks][j] = *(const bf16x8*)(xb + tc_off(80 * wm + 16 * j + fr + C::S * seg, 4 * ks + fc));
 #pragma unroll
-                for (int i = 0; i < C::WN; ++i) {
-                    const bf16x8 wf = *(const bf16x8*)(wb + tc_off(80 * wn + 16 * i + fr, 4 * ks + fc));
+                for (int i = 0; i < C::WN; ++i)
+                    wfr[ks][i] = *(const bf16x8*)(wb + tc_off(80 * wn + 16 * i + fr, 4 * ks + fc));
+            }
+#pragma unroll
+            for (int ks = 0; ks < C::BK / 32; ++ks)
+#pragma unroll
+                for (int i = 0; i < C::WN; ++i)
 #pragma unroll
                     for (int j = 0; j < C::WM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[j], acc[i][j], 0, 0, 0);
-                }
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfr[ks][i], xf[ks][j], acc[i][j], 0, 0, 0);
+            // order: step 0's 10 reads; its 25 MFMAs with step 1's 10 reads, two
+            // after every five; step 1's 25 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);  // DS reads
+#pragma unroll
+            for (int g5 = 0; g5 < 5; ++g5) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);  // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 25, 0);
             if (seg == 1) {
                 // The shortcut: the union's own-frame rows of chunk kk hold X for the
                 // 16-channel blocks of this wave that fall in the chunk (a block never
