@@ -10,6 +10,13 @@ the 256 MB Infinity Cache or in L2.
 Prints one JSON line: tokens/s (value), the roofline of the dominant kernel
 (algorithmic bytes per launch / HIP-event duration on the launch stream) and
 the fp64 oracle's throughput on the host cores over a bounded sample.
+
+Other workloads (--workload): sana2b (20 heads x d = 112), 720p60s (ten
+block-causal steps), tc720p5s (token-causal), cross720p (cross-attention), and
+tconv720p -- the Mix-FFN temporal convolution on one 720p-60s block at width
+2240, whose roofline is the bf16 MFMA peak (algorithmic flops per launch / its
+duration).  --summarize-trace / --summarize-pmc / --summarize-counters turn
+rocprofv3 runs into the summaries under profiles/.
 """
 import argparse
 import hashlib

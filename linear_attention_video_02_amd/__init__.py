@@ -7,7 +7,10 @@ is no fallback: if the library is not built, every call raises.
 
 The method is the ReLU linear attention of the SANA-Video analysis page
 (section 3.4: the linear-attention equation, Eq. 2 for RoPE, Eq. 3 and
-Algorithm 1 for the block-causal cache).
+Algorithm 1 for the block-causal cache), and beside it the block-causal
+temporal convolution of the Mix-FFN (section 3.4, "Spatial-Temporal Mix-FFN"
+and "Block Causal Mix-FFN": a kernel-3 convolution along time with a shortcut,
+last-frame caching and zero padding) -- temporal_conv_step.
 """
 from __future__ import annotations
 
