@@ -434,7 +434,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b", "tconv720p"],
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b", "tconv720p", "sweep"],
                     help="default: the headline 720p-5s bidirectional step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel events on every n-th timed step (each event costs ~2 us)")
@@ -486,6 +486,10 @@ def main():
               "across GPUs the bidirectional path would shard by (batch, head), with no "
               "communication", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "sweep":
+        run_sweep(args)
+        return
 
     import torch
 
@@ -603,6 +607,78 @@ def main():
         out.update(wl["extra"](tev_factory=FenceFreeEvents))
     if not args.no_cpu_baseline and "cpu_baseline" in wl:
         out["cpu_baseline"] = wl["cpu_baseline"](args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def run_sweep(args):
+    """Time the bidirectional step (la_state_reduce + la_apply) over the d x N
+    sweep (B1 H32, d in {32, 64, 128}, N in {4096 .. 220800}, grid ceil(N/920)
+    x 23 x 40) and check that time grows linearly in N at fixed d (Table 1's
+    O(N) claim): a least-squares fit t = a + b N per d, and the time per token
+    at the two largest N.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import linear_attention_video_02_amd as la
+    from linear_attention_video_02_amd.inputs import SWEEP_D, SWEEP_N, WORKLOADS, make_qkv_device
+    dev = torch.device("cuda:0")
+    tev = FenceFreeEvents()
+    points = []
+    for d in SWEEP_D:
+        for N in SWEEP_N:
+            w = WORKLOADS[f"sweep_d{d}_n{N}"]
+            B, H, grid, eps = w["B"], w["H"], w["grid"], w["eps"]
+            q, k, v = make_qkv_device(B, H, N, d, "bf16", w["seed"], dev)
+            tb = q.numel() * q.element_size()
+            nsets = max(2, math.ceil(2 * 2**30 / (4 * tb)))
+            sets = [(q, k, v)] + [tuple(t.clone() for t in (q, k, v)) for _ in range(nsets - 1)]
+            outs = [torch.empty_like(q) for _ in range(nsets)]
+            S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+            z = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+            ws = la.workspace(B, H, N, d, dev)
+
+            def step(i):
+                qi, ki, vi = sets[i % nsets]
+                la.state_reduce(ki, vi, grid, S=S, z=z, ws=ws)
+                la.apply(qi, S, z, grid, eps, out=outs[i % nsets])
+            for i in range(3):
+                step(i)
+            torch.cuda.synchronize()
+            iters = max(10, min(200, int(50e-3 / max(4 * tb / 5e12, 1e-6))))
+            e0, e1 = tev.new(), tev.new()
+            tev.record(e0)
+            for i in range(iters):
+                step(i)
+            tev.record(e1)
+            torch.cuda.synchronize()
+            us = tev.ms(e0, e1) / iters * 1e3
+            points.append({"d": d, "N": N, "us": us, "tokens_per_s": B * N / (us * 1e-6),
+                           "GBps": 4 * tb / (us * 1e-6) / 1e9, "iters": iters, "input_sets": nsets})
+            print(f"sweep d={d} N={N}: {us:.1f} us, {4 * tb / (us * 1e-6) / 1e9:.0f} GB/s", file=sys.stderr,
+                  flush=True)
+            del sets, outs, q, k, v
+            torch.cuda.empty_cache()
+    tev.close()
+    linear = {}
+    for d in SWEEP_D:
+        pts = [p_ for p_ in points if p_["d"] == d]
+        Ns = np.array([p_["N"] for p_ in pts], dtype=np.float64)
+        ts = np.array([p_["us"] for p_ in pts], dtype=np.float64)
+        b_, a_ = np.polyfit(Ns, ts, 1)
+        pred = a_ + b_ * Ns
+        r2 = 1.0 - float(((ts - pred) ** 2).sum() / ((ts - ts.mean()) ** 2).sum())
+        per_tok = ts / Ns
+        linear[str(d)] = {"fit_us": [float(a_), float(b_) * 1e6], "fit_units": "us = a + b * (N / 1e6)",
+                          "r2": r2, "us_per_Mtoken_largest_two": [float(per_tok[-2] * 1e6), float(per_tok[-1] * 1e6)]}
+    top = [p_ for p_ in points if p_["d"] == 64][-1]
+    out = {
+        "metric": "linear-attn tokens/sec over the d x N sweep (B1 H32, bidirectional, RoPE), 1 GPU",
+        "value": top["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": None, "warmup": 3,
+        "ms_per_step": top["us"] / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "sweep", "value_point": {"d": 64, "N": top["N"]}},
+        "sweep": points, "linearity": linear,
+    }
     print(json.dumps(out), flush=True)
 
 
