@@ -40,10 +40,17 @@ __global__ __launch_bounds__(256) void la_prefix_kernel(PrefixArgs a) {
     } else if (a.z_carry) {
         s = a.z_carry[(size_t)bh * D + f - D * D];
     }
-    for (int p = 0; p < a.P; ++p) {
-        const float t = part[(size_t)p * E];
-        part[(size_t)p * E] = s;
-        s = s + t;
+    // eight partials at a time: all loads issued before any store (the
+    // compiler cannot tell that a store does not alias the next loads)
+    for (int p0 = 0; p0 < a.P; p0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = p0 + i < a.P ? part[(size_t)(p0 + i) * E] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (p0 + i < a.P) part[(size_t)(p0 + i) * E] = s;
+            s = s + t[i];
+        }
     }
     if (f < D * D) {
         if (a.S_out) a.S_out[(size_t)bh * D * D + f] = s;
