@@ -72,9 +72,9 @@ def profile_commands(workload):
         "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/la_prof/trace -o trace "
                  f"-- python3 $REPO/bench.py{wl} --steps 50 --warmup 5 --no-cpu-baseline",
         "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/la_prof/fetch -o fetch "
-                 f"-- python3 $REPO/bench.py{wl} --steps 10 --warmup 2 --no-cpu-baseline",
+                 f"-- python3 $REPO/bench.py{wl} --steps 10 --warmup 2 --prewarm-ms 0 --no-cpu-baseline",
         "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/la_prof/write -o write "
-                 f"-- python3 $REPO/bench.py{wl} --steps 10 --warmup 2 --no-cpu-baseline",
+                 f"-- python3 $REPO/bench.py{wl} --steps 10 --warmup 2 --prewarm-ms 0 --no-cpu-baseline",
     }
 
 
@@ -403,7 +403,7 @@ def summarize_counters(dirs, out_path):
     for wl in dirs:
         flag = "" if wl == WORKLOAD else f" --workload {wl}"
         lines.append(f"cd /tmp && rocprofv3 --pmc {MFMA_COUNTERS} --output-format csv -d /tmp/la_prof/mfma_{wl} "
-                     f"-o p -- python3 $REPO/bench.py{flag} --steps 10 --warmup 2 --no-cpu-baseline")
+                     f"-o p -- python3 $REPO/bench.py{flag} --steps 10 --warmup 2 --prewarm-ms 0 --no-cpu-baseline")
     lines += ["python3 bench.py --summarize-counters " + " ".join(f"{w}=/tmp/la_prof/mfma_{w}" for w in dirs),
               "```", "", "utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), mean over the dispatches "
               "of each kernel (warm-up included).", "",
@@ -432,6 +432,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-ms", type=float, default=200.0,
+                    help="before the warm-up steps, run untimed steps for this long so that the GPU "
+                         "reaches its steady clock (from idle it needs tens of ms)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b", "tconv720p", "sweep"],
@@ -503,6 +506,13 @@ def main():
     tev = FenceFreeEvents()
     step = wl["step"]
 
+    # clock ramp: untimed steps for about prewarm_ms, then the W warm-up steps
+    t_pre, n_pre = time.perf_counter(), 0
+    while (time.perf_counter() - t_pre) * 1e3 < args.prewarm_ms:
+        for _ in range(8):
+            step(n_pre, None, tev)
+            n_pre += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i, None, tev)
     torch.cuda.synchronize()
@@ -571,6 +581,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm": {"ms": args.prewarm_ms, "steps": n_pre,
+                    "what": "untimed steps before the warm-up steps, for the GPU clock to ramp up"},
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -641,8 +653,13 @@ def run_sweep(args):
                 qi, ki, vi = sets[i % nsets]
                 la.state_reduce(ki, vi, grid, S=S, z=z, ws=ws)
                 la.apply(qi, S, z, grid, eps, out=outs[i % nsets])
-            for i in range(3):
-                step(i)
+            # warm-up: at least 3 steps and about prewarm_ms / 4 (clock ramp)
+            t_w, i_w = time.perf_counter(), 0
+            while i_w < 3 or (time.perf_counter() - t_w) * 1e3 < args.prewarm_ms / 4:
+                step(i_w)
+                i_w += 1
+                if i_w % 8 == 0:
+                    torch.cuda.synchronize()
             torch.cuda.synchronize()
             iters = max(10, min(200, int(50e-3 / max(4 * tb / 5e12, 1e-6))))
             e0, e1 = tev.new(), tev.new()
