@@ -597,8 +597,9 @@ int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bi
     a.D = D;
     a.M = (int)M;
     a.F = T < TconvCfg::FMAX ? T : TconvCfg::FMAX;
+    a.S = tconv_positions(a.F);
     a.nft = (T + a.F - 1) / a.F;
-    a.npt = (P + TconvCfg::S - 1) / TconvCfg::S;
+    a.npt = (P + a.S - 1) / a.S;
     if ((long long)B * a.nft * a.npt >= (1ll << 31) / 8) return LA_E_UNSUPPORTED;
     a.mtiles = B * a.nft * a.npt;
     a.ntiles = (D + TconvCfg::BN - 1) / TconvCfg::BN;

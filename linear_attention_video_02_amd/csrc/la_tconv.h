@@ -26,8 +26,8 @@ struct TconvArgs {
     const uint16_t* cache;  // [B][P][D] bf16: the previous block's last frame
     int T, P, D;
     int M;                  // B * T * P tokens
-    int F;                  // frames per token tile: min(T, 8)
-    int nft, npt;           // ceil(T / F), ceil(P / 40)
+    int F, S;               // token tile: F = min(T, 8) frames x S positions (tconv_positions)
+    int nft, npt;           // ceil(T / F), ceil(P / S)
     int mtiles, ntiles;     // B * nft * npt token tiles, ceil(D / 160) channel tiles
     int gm, gn;             // tile-order group: gm token tiles by gn channel tiles
 };
@@ -46,12 +46,22 @@ struct TconvCfg {
     static constexpr int BN = 160, BM = 320, BK = 64;
     static constexpr int THREADS = 512;
     static constexpr int WN = 5, WM = 5;                 // 16 x 16 tiles per wave
-    static constexpr int S = 40, FMAX = 8;               // token tile: F <= 8 frames x 40 positions
-    static constexpr int UROWS = (FMAX + 2) * S;         // frame-union rows per chunk
+    static constexpr int FMAX = 8;                       // token tile: F <= 8 frames x S positions
+    static constexpr int UROWS = 400;                    // frame-union rows per chunk: (F + 2) S <= 400
     static constexpr int WSTAGE = BN * BK;               // bf16 elements of a W slice
     static constexpr int XSTAGE = UROWS * BK;            // bf16 elements of a union chunk
     static constexpr int LDS_BYTES = (3 * WSTAGE + 2 * XSTAGE) * 2;  // 160 KB, all of it
 };
+
+// Positions per token tile for a tile of F frames: the largest multiple of 8
+// with F S <= 320 (the tile's rows) and (F + 2) S <= 400 (the frame union's
+// rows): 128, 96, 80, 64, 56, 48, 40, 40 for F = 1 .. 8.
+inline int tconv_positions(int F) {
+    int s = TconvCfg::BM / F;
+    const int u = TconvCfg::UROWS / (F + 2);
+    if (u < s) s = u;
+    return s & ~7;
+}
 
 // The cache after a block: its last input frame, X[b][T-1] -> cache[b].
 struct TconvCacheArgs {

@@ -48,6 +48,10 @@ __device__ __forceinline__ void dma16(BufRsrc r, uint32_t off, uint16_t* dst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
 }
 
+// FULL: tiles of 8 frames x 40 positions (blocks of 8 frames or more), with
+// the tile shape known at compile time; otherwise F and S come from the
+// arguments.
+template <bool FULL>
 __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvArgs a) {
     using C = TconvCfg;
     extern __shared__ __align__(16) uint16_t lds[];
@@ -73,14 +77,15 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
         mt = gi * a.gm + rem2 % gm;
         nt = sub * a.gn + rem2 / gm;
     }
-    // Token tile mt: frames f0 .. f0 + F - 1 by positions p0 .. p0 + 39 of batch
-    // element bb; tile row r = 40 i + q holds token (f0 + i, p0 + q).  Its
+    // Token tile mt: frames f0 .. f0 + F - 1 by positions p0 .. p0 + S - 1 of
+    // batch element bb (S = 40 for F = 8; more positions for shorter blocks, a
+    // multiple of 8); tile row r = S i + q holds token (f0 + i, p0 + q).  Its
     // frame union, frames f0 - 1 .. f0 + F, is staged per 64-channel chunk as
-    // union rows u = 40 i' + q (frame f0 - 1 + i'), so time offset o in {-1, 0, 1}
-    // of tile row r is union row r + 40 (o + 1).
-    const int F = a.F, D = a.D, P = a.P, T = a.T;
+    // union rows u = S i' + q (frame f0 - 1 + i'), so time offset o in {-1, 0, 1}
+    // of tile row r is union row r + S (o + 1).
+    const int F = FULL ? 8 : a.F, S = FULL ? 40 : a.S, D = a.D, P = a.P, T = a.T;
     const int pt = mt % a.npt, ft = (mt / a.npt) % a.nft, bb = mt / (a.npt * a.nft);
-    const int f0 = ft * F, p0 = pt * C::S, n0 = nt * C::BN;
+    const int f0 = ft * F, p0 = pt * S, n0 = nt * C::BN;
 
     // Loads go straight from memory into LDS (LDS DMA), 8 rows of 128 bytes
     // per wave instruction: lane i fills row 8 q + i / 8 at slot i % 8, which
@@ -89,8 +94,9 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
     // 50, q = wave + 8 j (7 for waves 0-1, else 6).  kOob (past every buffer's
     // range) loads zeros: channels past D, positions past P, frames past the
     // block (its zero padding frame) and union rows past frame f0 + F.  Union
-    // frame -1 (a block's first tiles, union rows 0..39 = instructions 0..4)
-    // comes from the cache.
+    // frame -1 (a block's first tiles, union rows 0 .. S - 1 = instructions
+    // 0 .. S/8 - 1, whole instructions since S is a multiple of 8) comes from
+    // the cache.
     constexpr uint32_t kOob = 0x80000000u;
     const BufRsrc rX = make_rsrc(a.X, (uint32_t)((size_t)a.M * D * 2));
     const BufRsrc rC = make_rsrc(a.cache, (uint32_t)((size_t)(a.M / (T * P)) * P * D * 2));
@@ -103,14 +109,16 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
         const int row = 8 * (wave + 8 * j) + (lane >> 3), n = n0 + row;
         wo[j] = (j < nw && n < D) ? (uint32_t)n * (uint32_t)D * 2u + cb : kOob;
     }
-    const bool from_cache = f0 == 0 && wave < 5;  // instruction j = 0 of waves 0-4: union frame -1
+    uint32_t cache_j = 0;  // bit j: instruction j of this wave loads union frame -1 (wave-uniform)
 #pragma unroll
     for (int j = 0; j < 7; ++j) {
         const int u = 8 * (wave + 8 * j) + (lane >> 3);
-        const int ip = u / C::S, q = u - ip * C::S;
+        const int ip = u / S, q = u - ip * S;
         const int f = f0 - 1 + ip, p = p0 + q;
         const bool ok = j < nx && ip <= F + 1 && p < P;
-        if (j == 0 && from_cache)
+        const bool from_cache = f0 == 0 && 8 * (wave + 8 * j) < S;
+        if (from_cache) cache_j |= 1u << j;
+        if (from_cache)
             xo[j] = p < P ? (uint32_t)(bb * P + p) * (uint32_t)D * 2u + cb : kOob;
         else
             xo[j] = (ok && f >= 0 && f < T) ? (uint32_t)((bb * T + f) * P + p) * (uint32_t)D * 2u + cb : kOob;
@@ -130,7 +138,7 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
 #pragma unroll
         for (int j = 0; j < 7; ++j) {
             if (j >= nx) break;
-            dma16((j == 0 && from_cache) ? rC : rX, xo[j] + kb, dst + j * 8 * 8 * 64);
+            dma16((cache_j >> j) & 1u ? rC : rX, xo[j] + kb, dst + j * 8 * 8 * 64);
         }
     };
 
@@ -139,6 +147,14 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
     // l % 16 of a 16-row block at k chunk l / 16 (8 consecutive k).
     const int wn = wave & 1, wm = wave >> 1;
     const int fr = lane & 15, fc = lane >> 4;
+    // First tile row of fragment j of this wave, for reads of the frame union.
+    // A fragment holding a real token (tile row < F S) maps, shifted by up to
+    // 2 S, to union rows below (F + 2) S <= 400 (also when F S is not a
+    // multiple of 16).  In a short block (F S < 320) a fragment with no real
+    // token reads rows of fragment 0 instead (wave-uniform choice; its
+    // results are never stored), so no read leaves the buffer.
+    const int fs = F * S;
+    auto frow = [&](int j) { const int r0 = 80 * wm + 16 * j; return r0 < fs ? r0 : 0; };
     // Accumulators start at the bias (4 consecutive channels per lane); the
     // shortcut X is added from LDS at the stage that holds it (below).
     f32x4 acc[C::WN][C::WM];
@@ -179,6 +195,8 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
             }
             const uint16_t* wb = wbuf0 + seg * C::WSTAGE;
             const uint16_t* xb = xbuf0 + (kk & 1) * C::XSTAGE;
+            const uint16_t* xs = xb + S * seg * 64;  // union rows shifted by this offset (S % 8 == 0:
+                                                     // the swizzle of row u + S seg is that of row u)
             // The stage's fragments, both k steps: the second step's LDS reads
             // are issued among the first step's MFMAs (scheduling groups below)
             bf16x8 xf[2][C::WM], wfr[2][C::WN];
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
             for (int ks = 0; ks < C::BK / 32; ++ks) {
 #pragma unroll
                 for (int j = 0; j < C::WM; ++j)
-                    xf[ks][j] = *(const bf16x8*)(xb + tc_off(80 * wm + 16 * j + fr + C::S * seg, 4 * ks + fc));
+                    xf[ks][j] = *(const bf16x8*)(xs + tc_off(frow(j) + fr, 4 * ks + fc));
 #pragma unroll
                 for (int i = 0; i < C::WN; ++i)
                     wfr[ks][i] = *(const bf16x8*)(wb + tc_off(80 * wn + 16 * i + fr, 4 * ks + fc));
@@ -219,7 +237,7 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
 #pragma unroll
                     for (int j = 0; j < C::WM; ++j) {
                         const uint2 xv =
-                            *(const uint2*)(xb + tc_off(80 * wm + 16 * j + fr + C::S, e >> 3) + (e & 7));
+                            *(const uint2*)(xb + S * 64 + tc_off(frow(j) + fr, e >> 3) + (e & 7));
                         acc[i][j] += f32x4{bf_lo(xv.x), bf_hi(xv.x), bf_lo(xv.y), bf_hi(xv.y)};
                     }
                 }
@@ -251,7 +269,7 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
 #pragma unroll 4
     for (int c = tid; c < PIECES; c += C::THREADS) {
         const int r = c / (C::BN / 8), k = c - r * (C::BN / 8);
-        const int i = r / C::S, q = r - i * C::S;
+        const int i = r / S, q = r - i * S;
         const int f = f0 + i, p = p0 + q, n = n0 + 8 * k;
         if (i >= F || f >= T || p >= P || n >= D) continue;
         *(u32x4*)(a.Y + (size_t)((bb * T + f) * P + p) * D + n) = *(const u32x4*)(ys + r * YROW + 8 * k);
@@ -270,11 +288,12 @@ __global__ __launch_bounds__(256) void la_tconv_cache_kernel(TconvCacheArgs a) {
 hipError_t la_tconv_launch(const TconvArgs& a, hipStream_t st) {
     // set on every call (a host-side attribute, cheap): it must hold on the
     // device current at this launch
-    const hipError_t e = hipFuncSetAttribute((const void*)la_tconv_bf16_kernel,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, TconvCfg::LDS_BYTES);
+    const bool full = a.F == 8 && a.S == 40;
+    void (*k)(TconvArgs) = full ? la_tconv_bf16_kernel<true> : la_tconv_bf16_kernel<false>;
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, TconvCfg::LDS_BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(la_tconv_bf16_kernel, dim3(a.mtiles * a.ntiles), dim3(TconvCfg::THREADS),
-                       TconvCfg::LDS_BYTES, st, a);
+    hipLaunchKernelGGL(k, dim3(a.mtiles * a.ntiles), dim3(TconvCfg::THREADS), TconvCfg::LDS_BYTES, st, a);
     return hipGetLastError();
 }
 

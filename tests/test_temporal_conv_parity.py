@@ -52,6 +52,9 @@ def check(got, ref, what):
 # position and channel tails; blocks of one frame (cache and zero padding
 # meet); P below a tile.
 CASES = [
+    (1, 6, 100, 192, True, 22),     # F = 6: 48 positions per tile
+    (2, 7, 90, 128, False, 23),     # F = 7: 40 positions, frames 5-6 of an 8-frame union
+    (1, 1, 300, 128, True, 24),     # F = 1: 128 positions, tile rows 128..319 unused
     (1, 9, 45, 128, True, 17),
     (2, 8, 21, 64, False, 18),
     (1, 17, 33, 384, True, 19),
