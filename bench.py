@@ -49,8 +49,9 @@ def kernel_source_hash(workload=None):
     return h.hexdigest()[:16]
 
 
-# The bf16 state pass is one launch (its last workgroup per head sums the
-# partials); with LA_STATE_FUSED=0 a separate combine launch follows it.
+# The bf16 state pass is one launch when a head's partials are small (its last
+# workgroup per head sums them); otherwise, or with LA_STATE_FUSED=0, a
+# separate combine launch follows it.
 STATE_KERNELS = ("la_state_bf16_kernel",)
 COMBINE_KERNEL = "la_state_combine_kernel"
 APPLY_KERNELS = ("la_apply_bf16_kernel",)

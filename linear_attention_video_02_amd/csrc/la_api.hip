@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kMaxPartials = 64;         // state workgroups per (batch, head), upper bound
 constexpr size_t kLdsLimit = 160 * 1024; // gfx950 LDS per workgroup
+constexpr size_t kFusedCombineBytes = 256 * 1024;  // per-head partials summed in the state launch
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -311,7 +312,14 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     c.z_carry = z_carry;
     c.P = pl.P;
     c.BH = g.BH;
-    const bool fused = dtype == LA_BF16 && env_flag("LA_STATE_FUSED", 1) != 0;
+    // Stage 2 inside the state launch saves a launch but leaves each head's sum
+    // to one workgroup.  That pays while a head's partials are small (P = 4 at
+    // d = 64: 66 KB); with many large partials (P = 12 at d = 112: 607 KB per
+    // head) the separate combine launch, spread over many workgroups, is faster.
+    // LA_STATE_FUSED = 0 / 1 forces one of the two.
+    const size_t head_partials = (size_t)pl.P * (size_t)(d * d + d) * 4;
+    const int force = env_flag("LA_STATE_FUSED", -1);
+    const bool fused = dtype == LA_BF16 && (force >= 0 ? force != 0 : head_partials <= kFusedCombineBytes);
     StateArgs a;
     a.K = K;
     a.V = V;

@@ -12,10 +12,12 @@
 //  - bf16 kernel, fused: the partials are written with device-scope stores
 //    and the last workgroup of a head to finish (a per-head counter in the
 //    workspace) does the sum.  No release fence: a device-scope fence per
-//    workgroup would write back a whole XCD L2 each time.
+//    workgroup would write back a whole XCD L2 each time.  Used while a
+//    head's partials are at most 256 KB (LA_STATE_FUSED=1 forces it).
 //  - separate launch (la_state_combine_kernel): the kernel boundary makes
-//    the partials visible.  Used by the fp32 kernel, by the token-causal
-//    pass (its prefix kernel reads the partials) and when LA_STATE_FUSED=0.
+//    the partials visible, and the sum is spread over many workgroups.
+//    Used by the fp32 kernel, by the token-causal pass (its prefix kernel
+//    reads the partials), for larger partials and when LA_STATE_FUSED=0.
 #pragma once
 
 #include "la_common.h"
