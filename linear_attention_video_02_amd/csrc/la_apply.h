@@ -17,6 +17,7 @@ struct ApplyArgs {
     float eps;
     int chunk;       // tokens per workgroup
     int P;           // workgroups per (batch, head)
+    int ilv;         // bf16: 1 = the head's workgroups take interleaved units of the whole head
     LaGeom g;
 };
 
@@ -117,9 +118,12 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     int bh, p;
     apply_item_of_block(a.P, a.g.BH, bh, p);
     const int ntok = a.g.ntok;
-    const int c0 = p * a.chunk;
-    const int c1 = min(c0 + a.chunk, ntok);
+    const bool ilv = a.ilv != 0;
+    const int c0 = ilv ? 0 : p * a.chunk;
+    const int c1 = ilv ? ntok : min(c0 + a.chunk, ntok);
     const int len = c1 > c0 ? c1 - c0 : 0;
+    // queue position q (in tokens) -> first token of the unit, within [c0, c1)
+    auto tok_of = [&](int q) -> int { return ilv ? ((q / C::UNIT) * a.P + p) * C::UNIT : q; };
     // Q and O of this chunk through descriptors bounded to [c0, c1): rows
     // past c1 read as zeros and their stores are dropped.
     const size_t chunk_off = ((size_t)bh * ntok + c0) * D;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     int us[C::DEPTH];
 #pragma unroll
     for (int s = 0; s < C::DEPTH; ++s) {
-        us[s] = (s * C::NW + wave) * C::UNIT;
+        us[s] = tok_of((s * C::NW + wave) * C::UNIT);
         load_unit(qr[s], us[s]);
     }
 
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
                     for (int ks = 0; ks < C::KS; ++ks) qc[r][ks] = qr[s][r][ks];
             }
-            us[s] = grab();
+            us[s] = tok_of(grab());
             load_unit(qr[s], us[s]);
 
 #pragma unroll

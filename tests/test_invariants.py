@@ -74,6 +74,31 @@ def test_fused_combine_matches_separate_launch(la, d, monkeypatch):
     assert all(torch.equal(x, y) for x, y in zip(res["0"], res["1"]))
 
 
+@pytest.mark.parametrize("d", [32, 64, 112, 128])
+@pytest.mark.parametrize("B,H,N", [(2, 6, 4999), (1, 1, 2077)])
+def test_interleaved_apply_matches_contiguous(la, d, B, H, N, monkeypatch):
+    """The bf16 apply with the head's workgroups on interleaved units of the
+    whole head (the default) and with one contiguous chunk per workgroup give
+    bitwise equal outputs: with and without RoPE, and for a block at a global
+    offset (block-causal mode), on a ragged token count."""
+    import torch
+    _, (tq, tk, tv) = _inputs(B, H, N, d, "bf16", 23)
+    grid = (6, 23, 40)
+    S, z = la.state_reduce(tk, tv, grid)
+    qb, kb, vb = (t[:, :, 1000:2000].contiguous() for t in (tq, tk, tv))
+    res = {}
+    for ilv in ("0", "1"):
+        monkeypatch.setenv("LA_APPLY_ILV", ilv)
+        o_rope = la.apply(tq, S, z, grid, 1e-6)
+        o_plain = la.apply(tq, S, z, None, 1e-6)
+        Sc, zc = S.clone() * 0.5, z.clone() * 0.5
+        ob = la.block_causal_step(qb, kb, vb, Sc, zc, N, grid, 1000, 1, commit=False)
+        torch.cuda.synchronize()
+        res[ilv] = (o_rope, o_plain, ob)
+    assert all(torch.equal(x, y) for x, y in zip(res["0"], res["1"]))
+    say(f"  d={d} B={B} H={H} N={N}: interleaved and contiguous apply bitwise equal")
+
+
 def oracle_bf16(x):
     """x rounded to bf16 values (float32 array), as the GPU receives it."""
     return round_to_bf16(np.asarray(x, dtype=np.float32))
