@@ -161,7 +161,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
 
     // register ring: step s in slot s & 1
     u32x4 rk[2][2], rv[2][2], rq[2][C::KS];
-    auto load_step = [&](int slot, int s) {
+    auto load_kv = [&](int slot, int s) {
         const int t0 = s * C::STEP;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -169,12 +169,31 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
             rk[slot][j] = buf_load16(Kr, off);
             rv[slot][j] = buf_load16(Vr, off);
         }
+    };
+    auto load_q = [&](int slot, int s) {
+        const int t0 = s * C::STEP;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
             rq[slot][ks] = buf_load16(Qr, (uint32_t)((t0 + 16 * wave + n) * D + 32 * ks + 8 * g) * 2u);
     };
-    load_step(0, 0);
-    load_step(1, 1);
+    // ---- running state: wave w owns the 32 x 32 tile (ci, cj) of S' ----
+    // (fetched before the ring's first loads: loads return in order, and the
+    // state is needed first)
+    const int m32 = lane & 31, h32 = lane >> 5;
+    const int ci = wave >> 1, cj = wave & 1;
+    const float* pre = a.pre + ((size_t)bh * a.P + p) * (D * D + D);
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int k = 32 * ci + 8 * (r >> 2) + 4 * h32 + (r & 3);
+        sacc[r] = pre[k * D + perm_inv(32 * cj + m32)];
+    }
+    const float zpre = tid < D ? pre[D * D + tid] : 0.0f;
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the ring's
+    load_kv(0, 0);
+    load_q(0, 0);
+    load_kv(1, 1);
+    load_q(1, 1);
 
     int t_lo = 0, nt = 1;
     PairRef prk[4], prq[C::KS][4];
@@ -191,16 +210,6 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
             for (int i = 0; i < 4; ++i) prq[ks][i] = pair_ref(16 * ks + 4 * g + i, nt, a.g);
     }
 
-    // ---- running state: wave w owns the 32 x 32 tile (ci, cj) of S' ----
-    const int m32 = lane & 31, h32 = lane >> 5;
-    const int ci = wave >> 1, cj = wave & 1;
-    const float* pre = a.pre + ((size_t)bh * a.P + p) * (D * D + D);
-    f32x16 sacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int k = 32 * ci + 8 * (r >> 2) + 4 * h32 + (r & 3);
-        sacc[r] = pre[k * D + perm_inv(32 * cj + m32)];
-    }
     // bf16 hi / lo of the tile, transposed (row = permuted value channel), into S buffer `buf`
     auto write_state = [&](int buf) {
         uint16_t* sh = lds + C::OFF_S + buf * 2 * C::STILE;
@@ -218,7 +227,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
         }
     };
     write_state(0);
-    if (tid < D) zbuf[tid] = pre[D * D + tid];
+    if (tid < D) zbuf[tid] = zpre;
     lds_barrier();
 
     uint16_t* kh = lds + C::OFF_KH;
@@ -226,8 +235,19 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
     uint16_t* ku = lds + C::OFF_KU;
     uint16_t* vp = lds + C::OFF_V;
 
-    for (int s = 0; s < nsteps; ++s) {
-        const int slot = s & 1, cur = s & 1;
+    // Two steps per trip, so that each ring slot and state buffer is a fixed
+    // set of registers / a fixed LDS offset: with a run-time slot the
+    // compiler moves the ring registers at the end of every step and waits
+    // for the loads issued in that same step first.  An odd step count runs
+    // one more step past the chunk instead of leaving the trip early (an
+    // early exit makes the compiler wait for loads one step too soon): its
+    // loads read zeros, which add nothing to the state, and its stores are
+    // dropped by the bounded descriptor.
+    for (int s2 = 0; s2 < nsteps; s2 += 2)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int s = s2 + u;
+        const int slot = u, cur = u;
         const int t0 = s * C::STEP;
 
         // ---------------- A: stage K and V of this step ----------------
@@ -274,12 +294,10 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) zpart[tid * 8 + e] = zp[e];
-        // queries of this wave (registers only)
-        u32x4 qc[C::KS];
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) qc[ks] = rq[slot][ks];
-        // refill the ring with step s + 2
-        load_step(slot, s + 2);
+        // refill the ring with step s + 2: K and V now, Q once this step's
+        // queries have been read (below), so that the loads land in the
+        // slot's own registers
+        load_kv(slot, s + 2);
         lds_barrier();
 
         // ---------------- B: outputs of this wave's 16 queries ----------------
@@ -294,7 +312,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
             u32x4 u4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t w = relu_bf16x2(qc[ks][i]);
+                const uint32_t w = relu_bf16x2(rq[slot][ks][i]);
                 u4[i] = w;
                 x[2 * i] = bf_lo(w);
                 x[2 * i + 1] = bf_hi(w);
@@ -321,6 +339,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
             Bq[ks] = __builtin_bit_cast(bf16x8, hw);
             Bl[ks] = __builtin_bit_cast(bf16x8, lw);
         }
+        load_q(slot, s + 2);
 
         f32x4 acc[C::NT];
 #pragma unroll

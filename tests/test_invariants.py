@@ -252,6 +252,25 @@ def test_canaries_untouched(la):
     say("  canaries intact")
 
 
+def test_token_causal_canaries_untouched(la):
+    """Token-causal outputs stay inside their tensor, also when a head's last
+    chunk has an odd number of 64-token steps (937 tokens: chunks of 128 and a
+    last chunk of 41) and the scan runs one step past the chunk."""
+    import torch
+    B, H, N, d, grid = 1, 3, 937, 64, (3, 20, 20)
+    (q, k, v), (tq, tk, tv) = _inputs(B, H, N, d, "bf16", 29)
+    pad = 4096
+    n_o = B * H * N * d
+    canary = torch.full((n_o + 2 * pad,), -7.0, dtype=torch.bfloat16, device="cuda:0")
+    out = canary[pad:pad + n_o].view(B, H, N, d)
+    la.token_causal(tq, tk, tv, grid, 1e-6, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(canary[:pad] == -7.0) and torch.all(canary[-pad:] == -7.0)
+    ref, _, _ = oracle.token_causal(q, k, v, grid, 1e-6)
+    assert_close(host(out), ref, "bf16", "token-causal, odd last chunk")
+    say("  token-causal canaries intact")
+
+
 def test_stream_copy_is_exact(la):
     """The measurement copy (la_stream_copy) moves every byte, at a size that
     is not a multiple of one sweep of the grid."""
