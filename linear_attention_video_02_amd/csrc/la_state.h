@@ -278,12 +278,15 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
     const int tgrp = wave / C::NCI;    // token group of this wave
 
     const int ntiles = c1 > c0 ? (c1 - c0 + C::TT - 1) / C::TT : 0;
+    // The loop sits inside this branch so that it is entered only after tile
+    // 0 is staged and tile DEPTH requested: reachable straight from the ring's
+    // first loads, the loop made the compiler wait for every load in flight
+    // at every other tile.
     if (ntiles > 0) {
         lds_barrier();  // RoPE table complete
         stage(0, 0, 0);
         load_tile(kr[0], vr[0], C::DEPTH);
         lds_barrier();
-    }
     // Whole rounds of the ring, no early exit: tiles past the chunk end are
     // zeros from the bounded descriptor and add nothing, and a uniform trip
     // count keeps the compiler's count of outstanding loads exact.
@@ -322,6 +325,7 @@ __global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel
                 }
             lds_barrier();
         }
+    }
     }
 
     // ---- fold the token groups of each key-channel tile: pairwise tree in a
