@@ -163,10 +163,11 @@ struct Plan {
 // State pass: about LA_STATE_WGS workgroups in all (default: one 512-thread
 // workgroup per CU for bf16),
 // chunks a multiple of the 64-token tile, at most kMaxPartials per head.
-int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0) {
+int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0, int fixed_lds = 0) {
     if (force_chunk > 0) {  // chunking imposed by the caller (token-causal pass)
         const int P = g.ntok > 0 ? (g.ntok + force_chunk - 1) / force_chunk : 1;
-        const size_t lds = (size_t)state_fixed_lds(d, dtype) + table_entries(g, force_chunk) * 8;
+        const size_t lds = (size_t)(fixed_lds > 0 ? fixed_lds : state_fixed_lds(d, dtype)) +
+                           table_entries(g, force_chunk) * 8;
         if (P > kMaxPartials || lds > kLdsLimit) return LA_E_UNSUPPORTED;
         out->P = P;
         out->chunk = force_chunk;
@@ -412,7 +413,12 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     Plan pc, ps;
     int rc = plan_causal(g, &pc);
     if (rc != LA_OK) return rc;
-    rc = plan_state(g, d, LA_BF16, &ps, pc.chunk);
+    // Partial states in 512-thread workgroups, two per CU: the P chunks per
+    // head (512 workgroups at 720p-5s) then run in one round instead of two
+    // rounds of 1024-thread workgroups (235 -> 229 us per call at 720p-5s).
+    // LA_TC_STATE_THREADS=1024 selects the larger workgroups.
+    const bool half = env_int("LA_TC_STATE_THREADS", 512) == 512;
+    rc = plan_state(g, d, LA_BF16, &ps, pc.chunk, half ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
     if (rc != LA_OK) return rc;
     const WsLayout L = ws_layout(g.BH, d);
     float* partial = (float*)((char*)ws + L.partial);
@@ -425,8 +431,10 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     sa.P = ps.P;
     sa.g = g;
     sa.ticket = nullptr;  // partials only: the prefix kernel reads them
-    rc = launch_kernel<StateArgs>(state_kernel(d, LA_BF16, g.rope), dim3(ps.P * g.BH), ps.lds, st, sa,
-                                  StateBf16Cfg<64>::THREADS);
+    KernelFn<StateArgs> sk = state_kernel(d, LA_BF16, g.rope);
+    if (half) sk = g.rope ? la_state_bf16_kernel<64, true, 512> : la_state_bf16_kernel<64, false, 512>;
+    rc = launch_kernel<StateArgs>(sk, dim3(ps.P * g.BH), ps.lds, st, sa,
+                                  half ? 512 : StateBf16Cfg<64>::THREADS);
     if (rc != LA_OK) return rc;
     // 2. exclusive prefixes in place (+ carry), total -> carry
     PrefixArgs pa;

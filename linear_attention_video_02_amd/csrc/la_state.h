@@ -138,15 +138,15 @@ __device__ __forceinline__ void item_of_block(int P, int BH, int& bh, int& p) {
 // other, with one barrier per tile.  DEPTH tiles of K/V are in flight per
 // workgroup (a register ring refilled right after each tile is staged).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int THR = (D <= 64 ? 1024 : 512)>
 struct StateBf16Cfg {
     static constexpr int DP = Pad<D>::P;      // channels on chip (zero above D)
-    static constexpr int THREADS = D <= 64 ? 1024 : 512;
+    static constexpr int THREADS = THR;
     static constexpr int NW = THREADS / 64;
     static constexpr int CH = DP / 8;         // 16-byte pieces per token row
     static constexpr int ROWS = THREADS / CH; // token rows per load pass
     static constexpr int LP = D <= 64 ? 1 : 2;  // load passes per tile
-    static constexpr int TT = ROWS * LP;      // tokens per tile: 256, 128, 64
+    static constexpr int TT = ROWS * LP;      // tokens per tile: 256, 128, 64 (half at 512 threads, d <= 64)
     static constexpr int DEPTH = 2;           // tiles of K/V in flight per workgroup
     static constexpr int TILE = TT * DP;      // elements per LDS tile
     static constexpr int BUF = 3 * TILE;      // K hi, K lo, V
@@ -173,9 +173,9 @@ __device__ __forceinline__ int swz(int row, int ch) {
     return row * D + (((ch >> 5) ^ s) << 5) + (ch & 31);
 }
 
-template <int D, bool ROPE>
-__global__ __launch_bounds__(StateBf16Cfg<D>::THREADS) void la_state_bf16_kernel(StateArgs a) {
-    using C = StateBf16Cfg<D>;
+template <int D, bool ROPE, int THR = StateBf16Cfg<D>::THREADS>
+__global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
+    using C = StateBf16Cfg<D, THR>;
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* lds = (uint16_t*)smem;   // [2][3][TT*D]: buffer, (K hi, K lo, V)
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
