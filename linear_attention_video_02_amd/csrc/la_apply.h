@@ -164,22 +164,24 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     // (a lane's fragment entries lie in 8 different rows of S, which as
     // single-word global loads would be 64 per lane) and goes to LDS
     // transposed, where each lane reads its fragments as 16-byte rows.
+    // (d >= 112 likewise: S comes in with the same coalesced loads, ahead of
+    // Q's, and goes from registers straight into the fp16 copy in LDS.)
     const float* Sh = a.S + (size_t)bh * D * D;
-    constexpr int S4 = C::SLDS ? 1 : (D * D / 4 + C::THREADS - 1) / C::THREADS;  // float4s a thread
+    constexpr int S4 = (D * D / 4 + C::THREADS - 1) / C::THREADS;  // float4s a thread
     f32x4 sraw[S4];
     float zraw[C::SLDS ? 1 : C::KS][8];
-    if (!C::SLDS) {
 #pragma unroll
-        for (int i = 0; i < S4; ++i) {
-            const int f = threadIdx.x + i * C::THREADS;
-            if (f < D * D / 4) sraw[i] = *(const f32x4*)(Sh + 4 * f);
-        }
+    for (int i = 0; i < S4; ++i) {
+        const int f = threadIdx.x + i * C::THREADS;
+        if (f < D * D / 4) sraw[i] = *(const f32x4*)(Sh + 4 * f);
+    }
+    if (!C::SLDS) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) zraw[ks][e] = a.z[(size_t)bh * D + 32 * ks + 8 * g + e];
-        __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of Q's
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of Q's
     // first DEPTH units of each wave: fixed, so their loads go out before the
     // prologue work
     const int wave = threadIdx.x >> 6;
@@ -194,21 +196,17 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     f16x8 A16[C::SLDS ? 1 : C::NT][C::KS];
     float* sT = (float*)st;  // d <= 64: [D][SROW] fp32, sT[co][ci] = S[ci][co]
     float amax = 0.0f;       // this thread's largest |S| entry
-    if (!C::SLDS) {
 #pragma unroll
-        for (int i = 0; i < S4; ++i) {
-            const int f = threadIdx.x + i * C::THREADS;
-            if (f < D * D / 4) {
-                const int ci = f / (D / 4), co = 4 * (f % (D / 4));
+    for (int i = 0; i < S4; ++i) {
+        const int f = threadIdx.x + i * C::THREADS;
+        if (f < D * D / 4) {
+            const int ci = f / (D / 4), co = 4 * (f % (D / 4));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sT[(co + j) * C::SROW + ci] = sraw[i][j];
-                    amax = fmaxf(amax, fabsf(sraw[i][j]));
-                }
+            for (int j = 0; j < 4; ++j) {
+                if (!C::SLDS) sT[(co + j) * C::SROW + ci] = sraw[i][j];
+                amax = fmaxf(amax, fabsf(sraw[i][j]));
             }
         }
-    } else {
-        for (int e = threadIdx.x; e < D * D; e += C::THREADS) amax = fmaxf(amax, fabsf(Sh[e]));
     }
     amax = wave_max(amax);
     if (lane == 0) smax[wave] = amax;
@@ -231,13 +229,32 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         eS = head_scale();
         // row pr = 16 T + m of the copy holds value channel co(T, m), the MFMA
         // row order used below; element k is S[k][co] 2^-eS (zero past d)
-        for (int e = threadIdx.x; e < C::DP * C::DP; e += C::THREADS) {
-            const int k = e / C::DP, co = e % C::DP;   // coalesced over co
-            const float sv = (k < D && co < D) ? Sh[k * D + co] : 0.0f;
+        auto put_st = [&](int k, int co, float sv) {
             const int T = 2 * (co >> 5) + ((co >> 2) & 1);
             const int m = (((co >> 3) & 3) << 2) | (co & 3);
             st[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] =
                 __builtin_bit_cast(uint16_t, (_Float16)ldexpf(sv, -eS));
+        };
+#pragma unroll
+        for (int i = 0; i < S4; ++i) {
+            const int f = threadIdx.x + i * C::THREADS;
+            if (f < D * D / 4) {
+                const int k = f / (D / 4), co = 4 * (f % (D / 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put_st(k, co + j, sraw[i][j]);
+            }
+        }
+        // the padding rows and columns (key or value channel >= d)
+        for (int e = threadIdx.x; e < C::DP * C::DP - D * D; e += C::THREADS) {
+            int k, co;
+            if (e < D * (C::DP - D)) {
+                k = e / (C::DP - D);
+                co = D + e % (C::DP - D);
+            } else {
+                k = D + (e - D * (C::DP - D)) / C::DP;
+                co = (e - D * (C::DP - D)) % C::DP;
+            }
+            put_st(k, co, 0.0f);
         }
     }
     if (C::SLDS)  // (d <= 64 sums the denominator on the MFMA from registers)
