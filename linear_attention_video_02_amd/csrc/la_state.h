@@ -48,8 +48,9 @@ struct StateArgs {
 };
 
 // Stage 2: grid (ceil(E4 / 256), B*H), one float4 of (S, z) per thread.  Sums
-// the P partials in the fixed order p = 0..P-1 (eight partials' loads in
-// flight before they are added), then adds the carry: S_b = carry + sum_p S_p.
+// the P partials in the fixed order p = 0..P-1 (sixteen partials' loads in
+// flight before they are added: one round trip for P <= 16), then adds the
+// carry: S_b = carry + sum_p S_p.
 template <int D>
 __global__ __launch_bounds__(256) void la_state_combine_kernel(CombineArgs a) {
     constexpr int E = D * D + D;
@@ -59,23 +60,14 @@ __global__ __launch_bounds__(256) void la_state_combine_kernel(CombineArgs a) {
     if (f >= E4) return;
     const float4* part = (const float4*)(a.partial + (size_t)bh * a.P * E);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    int p = 0;
-    for (; p + 8 <= a.P; p += 8) {
-        float4 v[8];
+    constexpr int NB = 16;
+    for (int p = 0; p < a.P; p += NB) {
+        float4 v[NB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(p + u) * E4 + f];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
-        }
-    }
-    {
-        float4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < NB; ++u)
             if (p + u < a.P) v[u] = part[(size_t)(p + u) * E4 + f];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < NB; ++u)
             if (p + u < a.P) {
                 s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
             }
