@@ -125,7 +125,7 @@ __device__ __forceinline__ void item_of_block(int P, int BH, int& bh, int& p) {
 // MFMA: C[c_in][c_out] += A[c_in][tok] B[tok][c_out], A = (hi, lo)^T, B = V.
 // Wave w owns key-channel tile w % NCI (32 rows of S, all value channels)
 // and token group w / NCI of every tile; at the end the NTG token groups of
-// each key-channel tile are summed in LDS in a fixed pairwise-tree order.
+// each key-channel tile are summed in LDS in a fixed order (a tree of fan-in four).
 // Two LDS buffers: tile t's MFMAs read one while tile t+1 is staged into the
 // other, with one barrier per tile.  DEPTH tiles of K/V are in flight per
 // workgroup (a register ring refilled right after each tile is staged).
@@ -148,8 +148,10 @@ struct StateBf16Cfg {
     static constexpr int KSTEPS = TT / (16 * NTG);  // 16-token steps per wave per tile
     static constexpr int NACC = NJ * 16;      // accumulators per lane
     static constexpr int STAGE_BYTES = 2 * BUF * 2;
-    static constexpr int RED_BYTES = (NW / 2) * 64 * NACC * 4;
-    static constexpr int ZRED_BYTES = THREADS * 8 * 4;
+    // fold of the token groups in groups of four: the first level has the
+    // most senders, NTG - ceil(NTG / 4) per key-channel tile
+    static constexpr int RED_BYTES = (NTG - (NTG + 3) / 4) * NCI * 64 * NACC * 4;
+    static constexpr int ZRED_BYTES = NW * DP * 4;  // z: one row of DP sums per wave
     static constexpr int m1 = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
     static constexpr int SMEM_FIXED = m1 > ZRED_BYTES ? m1 : ZRED_BYTES;
     static_assert(KSTEPS >= 1 && KSTEPS * 16 * NTG == TT, "k-steps");
@@ -172,7 +174,8 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     uint16_t* lds = (uint16_t*)smem;   // [2][3][TT*D]: buffer, (K hi, K lo, V)
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: branches on it stay scalar)
     int bh, p;
     item_of_block(a.P, a.g.BH, bh, p);
     const int ntok = a.g.ntok;
@@ -320,29 +323,44 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     }
     }
 
-    // ---- fold the token groups of each key-channel tile: pairwise tree in a
-    //      fixed order, level by level (group g += group g + 2^l) ----
-    float* red = (float*)smem;
+    // ---- fold the token groups of each key-channel tile: a tree of fan-in
+    //      four in a fixed order, level by level (group g += g + l, then
+    //      g + 2l, then g + 3l, for l = 1, 4, 16, ...) ----
+    f32x4* red = (f32x4*)smem;
     static_assert(C::RED_BYTES <= C::SMEM_FIXED, "reduction buffer");
+    static_assert(C::NACC % 4 == 0, "fold in 16-byte pieces");
     lds_barrier();
 #pragma unroll
-    for (int lvl = 1; lvl < C::NTG; lvl <<= 1) {
-        const bool sender = (tgrp & (2 * lvl - 1)) == lvl;
-        const bool receiver = (tgrp & (2 * lvl - 1)) == 0;
-        // slot of the sending wave: one per (receiver group, key-channel tile)
-        const int slot = (tgrp / (2 * lvl)) * C::NCI + ctile;
-        if (sender) {
+    for (int lvl = 1; lvl < C::NTG; lvl *= 4) {
+        const int k = (tgrp % (4 * lvl)) / lvl;  // position in the group of four
+        const bool member = tgrp % lvl == 0;
+        const int base = (tgrp / (4 * lvl)) * 3;  // first slot of this group
+        if (member && k > 0) {
+            const int slot = (base + k - 1) * C::NCI + ctile;
 #pragma unroll
             for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) red[(slot * C::NACC + j * 16 + r) * 64 + lane] = acc[j][r];
+                for (int r = 0; r < 16; r += 4)
+                    red[(slot * (C::NACC / 4) + j * 4 + r / 4) * 64 + lane] =
+                        f32x4{acc[j][r], acc[j][r + 1], acc[j][r + 2], acc[j][r + 3]};
         }
         lds_barrier();
-        if (receiver) {
+        if (member && k == 0) {
 #pragma unroll
-            for (int j = 0; j < C::NJ; ++j)
+            for (int m = 1; m < 4; ++m) {
+                if (tgrp + m * lvl >= C::NTG) break;
+                const int slot = (base + m - 1) * C::NCI + ctile;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[j][r] += red[(slot * C::NACC + j * 16 + r) * 64 + lane];
+                for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 4) {
+                        const f32x4 v = red[(slot * (C::NACC / 4) + j * 4 + r / 4) * 64 + lane];
+                        acc[j][r] += v[0];
+                        acc[j][r + 1] += v[1];
+                        acc[j][r + 2] += v[2];
+                        acc[j][r + 3] += v[3];
+                    }
+            }
         }
         lds_barrier();
     }
@@ -369,14 +387,22 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
                 if (C::DP == D || (row < D && col < D)) put(&part[row * D + col], acc[j][r]);
             }
     }
-    // ---- z partial: threads sharing a channel block, summed in thread order ----
-    float* zr = (float*)smem;
+    // ---- z partial: the lanes of a wave that share a channel block (lane
+    //      % CH) summed across lanes, then the waves' sums in wave order ----
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zr[tid * 8 + e] = zp[e];
+    for (int msk = C::CH; msk < 64; msk <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zp[e] += __shfl_xor(zp[e], msk);
+    float* zr = (float*)smem;  // [NW][DP]
+    if (lane < C::CH) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zr[wave * C::DP + 8 * lane + e] = zp[e];
+    }
     lds_barrier();
     if (tid < D) {
         float sum = 0.0f;
-        for (int r = 0; r < C::ROWS; ++r) sum += zr[((tid >> 3) + C::CH * r) * 8 + (tid & 7)];
+#pragma unroll
+        for (int w = 0; w < C::NW; ++w) sum += zr[w * C::DP + tid];
         put(&part[D * D + tid], sum);
     }
     if (!fused) return;
