@@ -91,6 +91,13 @@ __device__ __forceinline__ u32x4 buf_load16_dev(BufRsrc r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
 }
 
+// Device-coherent store (cache policy sc1): written through to the coherence
+// point, for data that other workgroups of the same kernel read with
+// buf_load16_dev once the store has completed.
+__device__ __forceinline__ void buf_store16_dev(u32x4 v, BufRsrc r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16);
+}
+
 // Streaming store for outputs nobody reads back soon (cache policy sc1 nt).
 // A default store leaves the line dirty in the memory-side Infinity Cache; it
 // is written to HBM later, while the next kernel streams its own inputs, and

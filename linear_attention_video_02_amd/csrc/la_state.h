@@ -377,16 +377,34 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     };
     constexpr int E = D * D + D;
     float* part = a.partial + ((size_t)bh * a.P + p) * E;
+    // The sums go to LDS as rows (stride SR floats), and every thread then
+    // writes 16 contiguous bytes of the partial at a time (from the MFMA
+    // layout directly, a lane would store single words, up to 64 a lane).
+    constexpr int SR = C::DP + 4;
+    static_assert(C::DP * SR * 4 <= C::SMEM_FIXED, "partial staging");
+    float* srow = (float*)smem;
     if (tgrp == 0) {
 #pragma unroll
         for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 32 * ctile + 8 * (r >> 2) + 4 * gq + (r & 3);
-                const int col = 32 * j + m;
-                if (C::DP == D || (row < D && col < D)) put(&part[row * D + col], acc[j][r]);
+                srow[row * SR + 32 * j + m] = acc[j][r];
             }
     }
+    lds_barrier();
+    {
+        const BufRsrc pr16 = make_rsrc(part, (uint32_t)D * D * 4u);
+        for (int f = tid; f < D * D / 4; f += C::THREADS) {
+            const int row = f / (D / 4), c4 = f % (D / 4);
+            const u32x4 v = __builtin_bit_cast(u32x4, *(const f32x4*)(srow + row * SR + 4 * c4));
+            if (fused)
+                buf_store16_dev(v, pr16, (uint32_t)f * 16u);
+            else
+                buf_store16(v, pr16, (uint32_t)f * 16u);
+        }
+    }
+    lds_barrier();  // the rows are read before the z sums reuse the LDS
     // ---- z partial: the lanes of a wave that share a channel block (lane
     //      % CH) summed across lanes, then the waves' sums in wave order ----
 #pragma unroll
