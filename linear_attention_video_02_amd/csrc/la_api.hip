@@ -633,7 +633,7 @@ int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bi
     if ((long long)B * a.nft * a.npt >= (1ll << 31) / 8) return LA_E_UNSUPPORTED;
     a.mtiles = B * a.nft * a.npt;
     a.ntiles = (D + TconvCfg::BN - 1) / TconvCfg::BN;
-    a.gm = env_int("LA_TCONV_GM", 4);
+    a.gm = env_int("LA_TCONV_GM", 8);
     a.gn = env_int("LA_TCONV_GN", 7);
     if ((long long)a.mtiles * a.ntiles >= (1ll << 31)) return LA_E_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
