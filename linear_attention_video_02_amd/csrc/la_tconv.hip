@@ -175,11 +175,32 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
     // and three stages ahead of their use.  Before its closing barrier each
     // wave waits for its own loads other than those just issued, which covers
     // everything stage t + 1 reads.
+    //
+    // Each stage's barrier sits between its two k steps: by then the wave has
+    // issued all of the stage's fragment reads, so past the barrier it reads
+    // the next stage's first-step fragments (into the registers the first
+    // step's MFMAs just freed) while the second step's MFMAs run, and the
+    // next stage starts with its operands in registers.
+    // Every fragment's first row is a multiple of 16, so its swizzle is that
+    // of row fr: tc_off(r0 + fr, c) = 64 r0 + tc_off(fr, c).  A lane keeps the
+    // two k steps' offsets; the rest is wave-uniform.
+    const int lx0 = tc_off(fr, fc), lx1 = tc_off(fr, 4 + fc);
+    const int wrow = 64 * 80 * wn;
+    auto read_step = [&](bf16x8 (&xf)[C::WM], bf16x8 (&wf)[C::WN], const uint16_t* xs, const uint16_t* wb,
+                         int ks) {
+        const int lx = ks ? lx1 : lx0;
+#pragma unroll
+        for (int j = 0; j < C::WM; ++j) xf[j] = *(const bf16x8*)(xs + 64 * frow(j) + lx);
+#pragma unroll
+        for (int i = 0; i < C::WN; ++i) wf[i] = *(const bf16x8*)(wb + wrow + 64 * 16 * i + lx);
+    };
     dma_x(0, 0);
     dma_w(0, 0);
     if (KT > 1) dma_w(1, 1);
     wait_vmcnt(KT > 1 ? nw : 0);
     dma_barrier();
+    bf16x8 xf0[C::WM], wf0[C::WN];  // first k step of the coming stage
+    read_step(xf0, wf0, xbuf0, wbuf0, 0);
     for (int kk = 0; kk < nkk; ++kk) {
 #pragma unroll
         for (int seg = 0; seg < 3; ++seg) {  // unrolled: buffer indices are constants
@@ -197,34 +218,42 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
             const uint16_t* xb = xbuf0 + (kk & 1) * C::XSTAGE;
             const uint16_t* xs = xb + S * seg * 64;  // union rows shifted by this offset (S % 8 == 0:
                                                      // the swizzle of row u + S seg is that of row u)
-            // The stage's fragments, both k steps: the second step's LDS reads
-            // are issued among the first step's MFMAs (scheduling groups below)
-            bf16x8 xf[2][C::WM], wfr[2][C::WN];
+            static_assert(C::BK == 64, "two 32-deep k steps per stage");
+            // first k step (fragments read before the stage) with the second
+            // step's 10 reads, two after every five MFMAs
+            bf16x8 xf1[C::WM], wf1[C::WN];
+            read_step(xf1, wf1, xs, wb, 1);
 #pragma unroll
-            for (int ks = 0; ks < C::BK / 32; ++ks) {
+            for (int i = 0; i < C::WN; ++i)
 #pragma unroll
                 for (int j = 0; j < C::WM; ++j)
-                    xf[ks][j] = *(const bf16x8*)(xs + tc_off(frow(j) + fr, 4 * ks + fc));
-#pragma unroll
-                for (int i = 0; i < C::WN; ++i)
-                    wfr[ks][i] = *(const bf16x8*)(wb + tc_off(80 * wn + 16 * i + fr, 4 * ks + fc));
-            }
-#pragma unroll
-            for (int ks = 0; ks < C::BK / 32; ++ks)
-#pragma unroll
-                for (int i = 0; i < C::WN; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::WM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wfr[ks][i], xf[ks][j], acc[i][j], 0, 0, 0);
-            // order: step 0's 10 reads; its 25 MFMAs with step 1's 10 reads, two
-            // after every five; step 1's 25 MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);  // DS reads
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf0[i], xf0[j], acc[i][j], 0, 0, 0);
 #pragma unroll
             for (int g5 = 0; g5 < 5; ++g5) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);  // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+            }
+            wait_vmcnt(issued);
+            dma_barrier();
+            // second k step with the next stage's first-step reads (after the
+            // last stage these read stale LDS into registers nobody uses: no
+            // condition, so that the reads and MFMAs share one block and can
+            // be interleaved)
+            {
+                const int sn = seg == 2 ? 0 : seg + 1, kn = seg == 2 ? kk + 1 : kk;
+                const uint16_t* xbn = xbuf0 + (kn & 1) * C::XSTAGE;
+                read_step(xf0, wf0, xbn + S * sn * 64, wbuf0 + sn * C::WSTAGE, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < C::WN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::WM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf1[i], xf1[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int g5 = 0; g5 < 5; ++g5) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 25, 0);
             if (seg == 1) {
                 // The shortcut: the union's own-frame rows of chunk kk hold X for the
                 // 16-channel blocks of this wave that fall in the chunk (a block never
@@ -242,8 +271,6 @@ __global__ __launch_bounds__(TconvCfg::THREADS) void la_tconv_bf16_kernel(TconvA
                     }
                 }
             }
-            wait_vmcnt(issued);
-            dma_barrier();
         }
     }
 
