@@ -8,7 +8,7 @@ nothing from it.
 from .linattn_oracle import (  # noqa: F401
     ROPE_BASE, phi, rope_axis_pairs, grid_positions, rope_angles, rope,
     state, apply, bidirectional_head, block_causal_head, weights_form_head,
-    bidirectional, states, block_causal, rel_row_error,
+    bidirectional, block_causal, rel_row_error,
     cross_attention_head, cross_attention, token_causal_head, token_causal,
 )
 from .temporal_conv_oracle import (  # noqa: F401

@@ -33,6 +33,10 @@ Readings where the page is silent (each is a stated definition here):
   token's global index n.
 * A row whose phi(Q_i) is all zero has output exactly zero (the numerator is
   exactly zero; with eps = 0 the 0/0 is defined as 0).
+* Any other row is the IEEE quotient num / den.  Its denominator is zero only
+  when eps = 0 and z is zero on every channel where phi(Q_i) is positive (for
+  instance cross-attention over no keys): the row is then NaN where the
+  numerator is zero and +-inf elsewhere.  Non-finite inputs propagate.
 
 Everything is evaluated in float64 on whatever values the caller passes
 (bf16 inputs are passed as their exact float values).
@@ -130,7 +134,8 @@ def apply(Q: np.ndarray, S: np.ndarray, z: np.ndarray, grid, eps: float, n0: int
     den = q @ z + eps
     out = np.zeros_like(num)
     live = np.any(q > 0.0, axis=1)
-    out[live] = num[live] / den[live, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out[live] = num[live] / den[live, None]
     return out
 
 
@@ -252,17 +257,6 @@ def bidirectional(Q, K, V, grid=None, eps=1e-6):
         for h in range(H):
             out[b, h] = bidirectional_head(Q[b, h], K[b, h], V[b, h], grid, eps)
     return out
-
-
-def states(K, V, grid=None):
-    """S[B,H,d,d] and z[B,H,d] of whole tensors."""
-    B, H, N, d = np.shape(K)
-    S = np.empty((B, H, d, d))
-    z = np.empty((B, H, d))
-    for b in range(B):
-        for h in range(H):
-            S[b, h], z[b, h] = state(K[b, h], V[b, h], grid)
-    return S, z
 
 
 def block_causal(Q, K, V, grid, block_tokens, eps=1e-6):

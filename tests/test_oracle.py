@@ -140,6 +140,23 @@ def brute_force_cross_loops(Q, K, V, eps):
     return out
 
 
+def brute_force_state_loops(K, V, grid):
+    """S[c_in][c_out] = sum_j RoPE(relu K_j)[c_in] V_j[c_out], z = sum_j relu K_j, with loops."""
+    N, d = K.shape
+    split = load_axis_split()[d] if grid is not None else None
+    pos = enumerate_positions(grid, N) if grid is not None else None
+    S = np.zeros((d, d))
+    z = np.zeros(d)
+    for j in range(N):
+        k = [max(float(a), 0.0) for a in K[j]]
+        kr = rotate_loop(k, pos[j], split) if grid is not None else k
+        for a in range(d):
+            z[a] += k[a]
+            for b in range(d):
+                S[a][b] += kr[a] * float(V[j][b])
+    return S, z
+
+
 def rand(shape, seed):
     return np.random.default_rng(seed).standard_normal(shape)
 
@@ -193,6 +210,41 @@ def check_brute_force_token_causal():
         ref = brute_force_loops(Q, K, V, grid, 1e-6, token_causal=True)
         got, _, _ = oracle.token_causal_head(Q, K, V, grid, 1e-6)
         np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12, err_msg=f"N={N} d={d}")
+
+
+def check_batched_wrappers():
+    """The [B, H, N, d] entry points route every argument to every (batch, head) slice.
+
+    Each wrapper runs on B = 2, H = 3 with a large, non-default eps (so that an
+    eps that falls back to its default shows), a grid and a block size, and is
+    compared slice by slice with the loop brute force of that slice.
+    """
+    B, H, N, d, grid, L, eps = 2, 3, 14, 8, (2, 2, 4), 5, 0.37
+    rng = np.random.default_rng(61)
+    Q, K, V = rng.standard_normal((3, B, H, N, d))
+    got = oracle.bidirectional(Q, K, V, grid, eps)
+    got_bc, S_bc, z_bc = oracle.block_causal(Q, K, V, grid, L, eps)
+    got_tc, S_tc, z_tc = oracle.token_causal(Q, K, V, grid, eps)
+    Kc, Vc = rng.standard_normal((2, B, H, 5, d))
+    got_x = oracle.cross_attention(Q, Kc, Vc, eps)
+    for b in range(B):
+        for h in range(H):
+            where = f"slice ({b}, {h})"
+            q, k, v = Q[b, h], K[b, h], V[b, h]
+            np.testing.assert_allclose(got[b, h], brute_force_loops(q, k, v, grid, eps),
+                                       rtol=1e-10, atol=1e-12, err_msg="bidirectional " + where)
+            np.testing.assert_allclose(got_bc[b, h], brute_force_loops(q, k, v, grid, eps, block=L),
+                                       rtol=1e-10, atol=1e-12, err_msg="block_causal " + where)
+            np.testing.assert_allclose(got_tc[b, h], brute_force_loops(q, k, v, grid, eps, token_causal=True),
+                                       rtol=1e-10, atol=1e-12, err_msg="token_causal " + where)
+            np.testing.assert_allclose(got_x[b, h], brute_force_cross_loops(q, Kc[b, h], Vc[b, h], eps),
+                                       rtol=1e-10, atol=1e-12, err_msg="cross_attention " + where)
+            S_ref, z_ref = brute_force_state_loops(k, v, grid)
+            for S_got, z_got, what in ((S_bc, z_bc, "block_causal"), (S_tc, z_tc, "token_causal")):
+                np.testing.assert_allclose(S_got[b, h], S_ref, rtol=1e-10, atol=1e-12,
+                                           err_msg=f"{what} final S " + where)
+                np.testing.assert_allclose(z_got[b, h], z_ref, rtol=1e-12, atol=1e-13,
+                                           err_msg=f"{what} final z " + where)
 
 
 def check_axis_split():
@@ -284,6 +336,10 @@ def test_token_causal_identities():
     o2, S2, z2 = oracle.token_causal_head(Q[m:], K[m:], V[m:], grid, 1e-6, n0=m, carry=(S1, z1))
     np.testing.assert_allclose(np.concatenate([o1, o2]), o_tc, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(S2, S_tc, rtol=1e-12, atol=1e-13)
+
+
+def test_batched_wrappers():
+    check_batched_wrappers()
 
 
 def test_axis_split():
@@ -516,6 +572,39 @@ def _mut_freq(n, grid, d):
     return ang * 1.0001
 
 
+def _mut_wrap_bidir_eps_default(Q, K, V, grid=None, eps=1e-6):
+    return _ORIG["bidirectional"](Q, K, V, grid)
+
+
+def _mut_wrap_block_eps_default(Q, K, V, grid, block_tokens, eps=1e-6):
+    return _ORIG["block_causal"](Q, K, V, grid, block_tokens)
+
+
+def _mut_wrap_token_no_grid(Q, K, V, grid=None, eps=1e-6):
+    return _ORIG["token_causal"](Q, K, V, None, eps)
+
+
+def _mut_wrap_cross_k_for_v(Q, K, V, eps=1e-6):
+    return _ORIG["cross_attention"](Q, K, K, eps)
+
+
+def _mut_wrap_bidir_head_shift(Q, K, V, grid=None, eps=1e-6):
+    """Slice (b, h) reads K and V of head h + 1: an indexing slip in the loop."""
+    B, H, N, d = np.shape(Q)
+    out = np.empty((B, H, N, d))
+    for b in range(B):
+        for h in range(H):
+            hh = (h + 1) % H
+            out[b, h] = orc.bidirectional_head(Q[b, h], K[b, hh], V[b, hh], grid, eps)
+    return out
+
+
+def _mut_wrap_block_carry_batch0(Q, K, V, grid, block_tokens, eps=1e-6):
+    """Every batch element reports the carry of batch element 0."""
+    out, S, z = _ORIG["block_causal"](Q, K, V, grid, block_tokens, eps)
+    return out, np.broadcast_to(S[:1], S.shape).copy(), np.broadcast_to(z[:1], z.shape).copy()
+
+
 _ORIG = {}
 MUTANTS = [
     ("rope", _mut_rope_sign),
@@ -530,15 +619,22 @@ MUTANTS = [
     ("block_causal_head", _mut_block_exclusive),
     ("rope_angles", _mut_freq),
     ("token_causal_head", _mut_token_exclusive),
+    ("bidirectional", _mut_wrap_bidir_eps_default),
+    ("block_causal", _mut_wrap_block_eps_default),
+    ("token_causal", _mut_wrap_token_no_grid),
+    ("cross_attention", _mut_wrap_cross_k_for_v),
+    ("bidirectional", _mut_wrap_bidir_head_shift),
+    ("block_causal", _mut_wrap_block_carry_batch0),
 ]
 PIN_CHECKS = [check_worked_examples, check_axis_split, check_rotation_axes_and_frequencies,
               check_brute_force_bidirectional, check_brute_force_block_causal, check_brute_force_cross,
-              check_brute_force_token_causal]
+              check_brute_force_token_causal, check_batched_wrappers]
 
 
 @pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
 def test_pins_catch_planted_mistakes(monkeypatch, name, mutant):
-    for key in ("rope", "rope_axis_pairs", "state", "apply", "rope_angles"):
+    for key in ("rope", "rope_axis_pairs", "state", "apply", "rope_angles", "bidirectional",
+                "block_causal", "token_causal", "cross_attention"):
         _ORIG[key] = getattr(orc, key)
     monkeypatch.setattr(orc, name, mutant)
     # the package namespace re-exports the functions; patch it too
@@ -550,3 +646,30 @@ def test_pins_catch_planted_mistakes(monkeypatch, name, mutant):
         except AssertionError:
             failed.append(check.__name__)
     assert failed, f"no pin caught the planted mistake {mutant.__name__}"
+
+
+def test_zero_denominator_rows():
+    """eps = 0 and a live query whose channels meet no key mass: the IEEE quotient.
+
+    With no keys at all, S = 0 and z = 0: a live row is 0/0 = NaN in every
+    channel, a dead row (relu(Q_i) = 0) is exactly zero.  With keys that are
+    zero on every channel where the query is positive, the denominator is 0
+    while RoPE can still give the numerator a non-zero value (+-inf there).
+    """
+    rng = np.random.default_rng(62)
+    Q = rng.standard_normal((9, 8))
+    Q[3] = -np.abs(Q[3])  # a dead row
+    got = oracle.cross_attention_head(Q, np.zeros((0, 8)), np.zeros((0, 8)), 0.0)
+    live = (Q > 0).any(axis=1)
+    assert np.isnan(got[live]).all() and not np.any(got[~live])
+    # d = 8 on a 1x2x2 grid: pair 3 (channels 6, 7) turns with w by angle w.  The
+    # query is positive on channel 6 only, the keys on channel 7 only, so z is
+    # zero where the query lives, but keys one w step away contribute -+sin(1)
+    Qp = np.zeros((4, 8))
+    Qp[:, 6] = 1.0
+    Kp = np.zeros((4, 8))
+    Kp[:, 7] = 1.0
+    Vp = np.ones((4, 8))
+    out = oracle.bidirectional_head(Qp, Kp, Vp, (1, 2, 2), 0.0)
+    assert np.isinf(out).all()
+    assert (np.sign(out[:, 0]) == [-1, 1, -1, 1]).all()
