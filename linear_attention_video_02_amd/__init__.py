@@ -117,32 +117,80 @@ def _stream(t):
 
 
 def _check_qkv(*ts):
+    """Q/K/V/O-like tensors: 4-D [B, H, n, d], contiguous, one dtype, on one GPU.
+
+    Shapes are checked before placement, so a mis-sized tensor is reported as
+    such (the library trusts the sizes it is given: an undersized buffer would
+    be read or written out of bounds).
+    """
     ref = ts[0]
+    _check_dims(*ts)
     for t in ts:
+        if t.dtype != ref.dtype:
+            raise ValueError("Q/K/V/O must share one dtype")
         if not t.is_cuda:
             raise ValueError("tensors must be on a GPU")
+        if t.device != ref.device:
+            raise ValueError("Q/K/V/O must be on one device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, N, d]")
+
+
+def _check_dims(*ts):
+    for t in ts:
         if t.dim() != 4:
-            raise ValueError("tensors must be 4-D [B, H, N, d]")
-        if t.dtype != ref.dtype or t.device != ref.device:
-            raise ValueError("Q/K/V/O must share dtype and device")
+            raise ValueError(f"tensors must be 4-D [B, H, N, d], got shape {tuple(t.shape)}")
+
+
+def _check_same_shape(what, *ts):
+    _check_dims(*ts)
+    shapes = [tuple(t.shape) for t in ts]
+    if any(sh != shapes[0] for sh in shapes):
+        raise ValueError(f"{what}: shapes must match, got {shapes}")
+
+
+def _check_state(S, z, B, H, d, device, what):
+    """S [B, H, d, d] and z [B, H, d]: contiguous float32 on the inputs' device."""
+    torch = _torch()
+    if tuple(S.shape) != (B, H, d, d):
+        raise ValueError(f"{what}: S must have shape {(B, H, d, d)}, got {tuple(S.shape)}")
+    if tuple(z.shape) != (B, H, d):
+        raise ValueError(f"{what}: z must have shape {(B, H, d)}, got {tuple(z.shape)}")
+    for t in (S, z):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{what}: S and z must be float32")
+        if not t.is_contiguous():
+            raise ValueError(f"{what}: S and z must be contiguous")
+        if t.device != device:
+            raise ValueError(f"{what}: S and z must be on the inputs' device")
 
 
 _ws_cache: dict = {}
 
 
-def workspace(B: int, H: int, N: int, d: int, device):
-    """A zero-filled workspace, cached per (device, size); reusable on one stream."""
+def workspace(B: int, H: int, N: int, d: int, device, stream=None):
+    """A zero-filled workspace, cached per (device, stream, size).
+
+    The library's calls keep per-head counters and partial states in their
+    workspace, so two calls that may run at the same time must not share one:
+    the cache hands each stream its own (stream = None: the device's current
+    stream).
+    """
     torch = _torch()
     nbytes = workspace_bytes(B, H, N, d)
     if nbytes == 0:
         raise ValueError("invalid sizes for a workspace")
     dev = torch.device(device)
-    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device(), nbytes)
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    key = (dev.type, dev.index, int(stream.cuda_stream), nbytes)
     ws = _ws_cache.get(key)
     if ws is None:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        # zero-filled on the stream that will use it, so no other stream's work can race with the fill
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 
@@ -155,10 +203,14 @@ def _state_tensors(B, H, d, device):
 
 def state_reduce(k, v, grid=None, S=None, z=None, ws=None):
     """S = sum_j RoPE(relu K_j)^T V_j and z = sum_j relu K_j per (batch, head)."""
-    _check_qkv(k, v)
+    _check_same_shape("state_reduce k/v", k, v)
     B, H, N, d = k.shape
-    if S is None or z is None:
+    if (S is None) != (z is None):
+        raise ValueError("state_reduce: give both S and z, or neither")
+    if S is None:
         S, z = _state_tensors(B, H, d, k.device)
+    _check_state(S, z, B, H, d, k.device, "state_reduce")
+    _check_qkv(k, v)
     if ws is None:
         ws = workspace(B, H, N, d, k.device)
     gt, gh, gw = _grid(grid)
@@ -173,8 +225,12 @@ def state_reduce(k, v, grid=None, S=None, z=None, ws=None):
 def apply(q, S, z, grid=None, eps=1e-6, out=None):
     """O_i = RoPE(relu Q_i) S / (relu Q_i . z + eps)."""
     torch = _torch()
-    _check_qkv(q)
+    _check_dims(q)
     B, H, N, d = q.shape
+    _check_state(S, z, B, H, d, q.device, "apply")
+    if out is not None:
+        _check_same_shape("apply q/out", q, out)
+    _check_qkv(q)
     if out is None:
         out = torch.empty_like(q)
     _check_qkv(q, out)
@@ -188,6 +244,10 @@ def apply(q, S, z, grid=None, eps=1e-6, out=None):
 
 def bidirectional(q, k, v, grid=None, eps=1e-6, out=None, ws=None):
     """Bidirectional ReLU linear attention with (optional) 3D RoPE."""
+    _check_same_shape("bidirectional q/k/v", q, k, v)
+    if out is not None:
+        _check_same_shape("bidirectional q/out", q, out)
+    _check_qkv(q, k, v)
     S, z = state_reduce(k, v, grid, ws=ws)
     return apply(q, S, z, grid, eps, out)
 
@@ -198,9 +258,12 @@ def cross_attention(q, k, v, eps=1e-6, out=None, ws=None):
     The same two library calls as self-attention (la_state_reduce over the
     N_kv keys/values, la_apply over the N_q queries); N_kv = 0 gives zeros.
     """
-    _check_qkv(q, k, v)
+    _check_dims(q, k, v)
     if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
         raise ValueError("k and v must be [B, H, N_kv, d] with q's B, H and d")
+    if out is not None:
+        _check_same_shape("cross_attention q/out", q, out)
+    _check_qkv(q, k, v)
     S, z = state_reduce(k, v, None, ws=ws)
     return apply(q, S, z, None, eps, out)
 
@@ -209,8 +272,18 @@ def block_causal_step(q, k, v, S_carry, z_carry, N, grid, block_tokens, block_id
                       commit=True, eps=1e-6, out=None, ws=None):
     """One block of block-causal mode; q/k/v/out hold only this block."""
     torch = _torch()
-    _check_qkv(q, k, v)
+    _check_same_shape("block_causal_step q/k/v", q, k, v)
     B, H, Lb, d = q.shape
+    N, block_tokens, block_idx = int(N), int(block_tokens), int(block_idx)
+    if block_tokens < 1 or block_idx < 0 or block_idx * block_tokens >= N:
+        raise ValueError(f"block {block_idx} of {block_tokens} tokens is not inside a sequence of {N}")
+    want = min(block_tokens, N - block_idx * block_tokens)
+    if Lb != want:
+        raise ValueError(f"block {block_idx} holds {want} tokens, but q/k/v hold {Lb}")
+    _check_state(S_carry, z_carry, B, H, d, q.device, "block_causal_step carry")
+    if out is not None:
+        _check_same_shape("block_causal_step q/out", q, out)
+    _check_qkv(q, k, v)
     if out is None:
         out = torch.empty_like(q)
     _check_qkv(q, out)
@@ -234,8 +307,15 @@ def token_causal(q, k, v, grid=None, eps=1e-6, S_carry=None, z_carry=None, n_off
     scan starts from that state and leaves the final state in them.
     """
     torch = _torch()
-    _check_qkv(q, k, v)
+    _check_same_shape("token_causal q/k/v", q, k, v)
     B, H, N, d = q.shape
+    if (S_carry is None) != (z_carry is None):
+        raise ValueError("token_causal: give both S_carry and z_carry, or neither")
+    if S_carry is not None:
+        _check_state(S_carry, z_carry, B, H, d, q.device, "token_causal carry")
+    if out is not None:
+        _check_same_shape("token_causal q/out", q, out)
+    _check_qkv(q, k, v)
     if out is None:
         out = torch.empty_like(q)
     _check_qkv(q, out)
