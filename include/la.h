@@ -177,6 +177,21 @@ LA_API int la_temporal_conv_step(const void* X, void* Y, const void* W, const fl
  * 2^42 bytes returns LA_E_UNSUPPORTED. */
 LA_API int la_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/* Measurement only, not part of the method: set a tuning knob of this
+ * process's library instance, for A/B runs on one build.  Knobs (value < 0
+ * restores the default choice, which is what every figure quoted for this
+ * library uses):
+ *   "state_wgs", "apply_wgs", "causal_wgs"  target workgroup counts (>= 1)
+ *   "state_fused"      0 / 1: separate / in-kernel stage 2 of the state pass
+ *   "apply_ilv"        0: one contiguous chunk per apply workgroup
+ *   "apply_heads"      1..8: heads per apply workgroup (if they fit)
+ *   "tc_state_threads" 512 / 1024: token-causal partial-state workgroups
+ *   "tconv_gm", "tconv_gn"  temporal-convolution tile-order group (1..64)
+ * Returns LA_OK, LA_E_NULLPTR, LA_E_UNSUPPORTED (unknown name) or
+ * LA_E_SHAPE (value out of range).  Not thread-safe: set knobs while no
+ * other thread calls the library.  Results are correct under every value. */
+LA_API int la_set_tuning(const char* name, int value);
+
 /* Static text for a status code (never NULL). */
 LA_API const char* la_strerror(int status);
 

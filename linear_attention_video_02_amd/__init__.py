@@ -14,6 +14,7 @@ last-frame caching and zero padding) -- temporal_conv_step.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.la_strerror.restype = ctypes.c_char_p
         L.la_last_hip_error.argtypes = []
         L.la_last_hip_error.restype = ctypes.c_char_p
+        L.la_set_tuning.argtypes = [ctypes.c_char_p, ci]
+        L.la_set_tuning.restype = ci
         _lib = L
     return _lib
 
@@ -80,6 +83,25 @@ def strerror(status: int) -> str:
 
 def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(lib().la_workspace_bytes(B, H, N, d))
+
+
+def set_tuning(name: str, value: int) -> None:
+    """Set one of the library's tuning knobs (measurement only; value < 0 restores the default)."""
+    rc = lib().la_set_tuning(name.encode(), int(value))
+    if rc:
+        raise LinAttnError(rc, f"la_set_tuning({name!r}, {value})")
+
+
+@contextlib.contextmanager
+def tuning(**knobs):
+    """Run a block with tuning knobs set, restoring their defaults afterwards."""
+    try:
+        for name, value in knobs.items():
+            set_tuning(name, value)
+        yield
+    finally:
+        for name in knobs:
+            lib().la_set_tuning(name.encode(), -1)
 
 
 # ---------------------------------------------------------------------------

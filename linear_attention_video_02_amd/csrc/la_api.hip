@@ -33,17 +33,25 @@ constexpr size_t kFusedCombineBytes = 256 * 1024;  // per-head partials summed i
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int env_flag(const char* name, int dflt) {
-    const char* s = getenv(name);
-    return (s && *s) ? atoi(s) : dflt;
-}
+// Tuning knobs, for measurement only (A/B runs on one build): every knob
+// starts unset, meaning the default choice, and changes only through
+// la_set_tuning().  Nothing here reads the process environment.
+enum Knob {
+    K_STATE_WGS, K_APPLY_WGS, K_CAUSAL_WGS, K_STATE_FUSED, K_APPLY_ILV, K_APPLY_HEADS,
+    K_TC_STATE_THREADS, K_TCONV_GM, K_TCONV_GN, K_COUNT
+};
+struct KnobInfo {
+    const char* name;
+    int lo, hi;  // accepted values (a negative value resets the knob)
+};
+const KnobInfo kKnobs[K_COUNT] = {
+    {"state_wgs", 1, 1 << 20},  {"apply_wgs", 1, 1 << 20},  {"causal_wgs", 1, 1 << 20},
+    {"state_fused", 0, 1},      {"apply_ilv", 0, 1},        {"apply_heads", 1, 8},
+    {"tc_state_threads", 512, 1024}, {"tconv_gm", 1, 64},   {"tconv_gn", 1, 64},
+};
+int g_knob[K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
 
-int env_int(const char* name, int dflt) {
-    const char* s = getenv(name);
-    if (!s || !*s) return dflt;
-    const int v = atoi(s);
-    return v > 0 ? v : dflt;  // only positive overrides (workgroup counts)
-}
+int knob(Knob k, int dflt) { return g_knob[k] >= 0 ? g_knob[k] : dflt; }
 
 struct WsLayout {
     size_t ticket, partial, state, total;
@@ -138,15 +146,24 @@ int state_fixed_lds(int d, int dtype) {
     }
 }
 
-int apply_fixed_lds(int d, int dtype) {
-    if (dtype == LA_BF16) {
-        switch (d) {
-            case 32: return ApplyBf16Cfg<32>::FIXED;
-            case 64: return ApplyBf16Cfg<64>::FIXED;
-            case 112: return ApplyBf16Cfg<112>::FIXED;
-            default: return ApplyBf16Cfg<128>::FIXED;
-        }
+// LDS of the bf16 apply: fixed part, and per head it holds (S^T copy + z)
+void apply_bf16_lds(int d, int* fixed, int* perhead, int* maxph, int* unit) {
+#define LA_CFG(D)                           \
+    if (d == D) {                           \
+        *fixed = ApplyBf16Cfg<D>::FIXED;    \
+        *perhead = ApplyBf16Cfg<D>::PERHEAD; \
+        *maxph = ApplyBf16Cfg<D>::MAXPH;    \
+        *unit = ApplyBf16Cfg<D>::UNIT;      \
+        return;                             \
     }
+    LA_CFG(32)
+    LA_CFG(64)
+    LA_CFG(112)
+    LA_CFG(128)
+#undef LA_CFG
+}
+
+int apply_f32_lds(int d) {
     switch (d) {
         case 32: return ApplyF32Cfg<32>::SMEM_FIXED;
         case 64: return ApplyF32Cfg<64>::SMEM_FIXED;
@@ -160,7 +177,7 @@ struct Plan {
     size_t lds;
 };
 
-// State pass: about LA_STATE_WGS workgroups in all (default: one 512-thread
+// State pass: about state_wgs workgroups in all (default: one 512-thread
 // workgroup per CU for bf16),
 // chunks a multiple of the 64-token tile, at most kMaxPartials per head.
 int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0, int fixed_lds = 0) {
@@ -174,7 +191,7 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0
         out->lds = lds;
         return LA_OK;
     }
-    const int target = env_int("LA_STATE_WGS", dtype == LA_BF16 ? 256 : 1024);
+    const int target = knob(K_STATE_WGS, dtype == LA_BF16 ? 256 : 1024);
     // chunks are whole tiles (the kernel's ring then runs on to a whole round
     // with zero tiles: a little compute, no memory traffic)
     const int tile = dtype == LA_BF16 ? (d == 32   ? StateBf16Cfg<32>::TT
@@ -205,13 +222,63 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0
     }
 }
 
-// Apply pass: about LA_APPLY_WGS workgroups in all (default: one 512-thread
-// workgroup per CU for bf16).
-int plan_apply(const LaGeom& g, int d, int dtype, Plan* out) {
-    const int target = env_int("LA_APPLY_WGS", dtype == LA_BF16 ? 256 : 1024);
-    const int tile = 128;
+// Apply pass.
+//  - bf16, interleaved (the default): nph heads per workgroup one after
+//    another, P workgroups per head taking interleaved units of it, hs = BH /
+//    nph head slots, about apply_wgs (256) workgroups in all.  The most heads
+//    per workgroup (fewest heads in flight) such that nph divides BH, the
+//    workgroups still fill the chip, every workgroup has at least 8 units
+//    per head, and the S^T copies plus the RoPE table of the whole head fit
+//    in LDS.
+//  - otherwise (fp32, a table too large for LDS, or apply_ilv = 0): one
+//    contiguous chunk per workgroup, P chunks per head.
+struct ApplyPlan {
+    int ilv, P, nph, hs, chunk, grid;
+    size_t lds;
+};
+
+int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
+    const int target = knob(K_APPLY_WGS, dtype == LA_BF16 ? 256 : 1024);
     const int ntok = g.ntok;
-    int P = target / g.BH;  // at most `target` workgroups (see plan_state)
+    const int BH = g.BH;
+    int fixed = 0, perhead = 0, maxph = 1, unit = 32;
+    if (dtype == LA_BF16) apply_bf16_lds(d, &fixed, &perhead, &maxph, &unit);
+    if (dtype == LA_BF16 && ntok > 0 && knob(K_APPLY_ILV, 1) != 0) {
+        const int U = (ntok + unit - 1) / unit;  // units per head
+        const int pmax = U / 8 > 1 ? U / 8 : 1;
+        const long long want = (long long)BH * pmax < target ? (long long)BH * pmax : target;
+        const size_t table = table_entries(g, ntok) * 8;
+        const int forced = knob(K_APPLY_HEADS, 0);
+        for (int nph = forced > 0 ? forced : maxph; nph >= 1; --nph) {
+            if (nph > maxph || BH % nph != 0) {
+                if (forced > 0) break;
+                continue;
+            }
+            const int hs = BH / nph;
+            int P = target / hs;
+            P = P < 1 ? 1 : (P > pmax ? pmax : P);
+            // enough workgroups to fill the chip (one head per workgroup always qualifies)
+            if (forced <= 0 && nph > 1 && (long long)hs * P * 10 < want * 9) continue;
+            const size_t lds = (size_t)fixed + (size_t)nph * perhead + table;
+            if (lds > kLdsLimit) {
+                if (forced > 0) break;
+                continue;
+            }
+            // buffer offsets of units past a head's end stay below 2^32
+            if (((size_t)ntok + (size_t)(P + 1) * unit) * d * 2 >= (1ull << 32)) break;
+            if ((long long)hs * P >= (1ll << 31)) break;
+            out->ilv = 1;
+            out->P = P;
+            out->nph = nph;
+            out->hs = hs;
+            out->chunk = ntok;
+            out->grid = hs * P;
+            out->lds = lds;
+            return LA_OK;
+        }
+    }
+    const int tile = 128;
+    int P = target / BH;  // at most `target` workgroups (see plan_state)
     if (P < 1) P = 1;
     const int max_p = ntok > 0 ? (ntok + tile - 1) / tile : 1;
     if (P > max_p) P = max_p;
@@ -219,10 +286,16 @@ int plan_apply(const LaGeom& g, int d, int dtype, Plan* out) {
         int chunk = ntok > 0 ? (ntok + P - 1) / P : tile;
         chunk = (int)align_up((size_t)chunk, tile);
         const int Peff = ntok > 0 ? (ntok + chunk - 1) / chunk : 1;
-        const size_t lds = (size_t)apply_fixed_lds(d, dtype) + table_entries(g, chunk) * 8;
+        const size_t base = dtype == LA_BF16 ? (size_t)fixed + perhead : (size_t)apply_f32_lds(d);
+        const size_t lds = base + table_entries(g, chunk) * 8;
         if (lds <= kLdsLimit) {
+            if ((long long)Peff * BH >= (1ll << 31)) return LA_E_UNSUPPORTED;
+            out->ilv = 0;
             out->P = Peff;
+            out->nph = 1;
+            out->hs = BH;
             out->chunk = chunk;
+            out->grid = Peff * BH;
             out->lds = lds;
             return LA_OK;
         }
@@ -317,9 +390,9 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     // to one workgroup.  That pays while a head's partials are small (P = 4 at
     // d = 64: 66 KB); with many large partials (P = 12 at d = 112: 607 KB per
     // head) the separate combine launch, spread over many workgroups, is faster.
-    // LA_STATE_FUSED = 0 / 1 forces one of the two.
+    // The tuning knob state_fused = 0 / 1 forces one of the two.
     const size_t head_partials = (size_t)pl.P * (size_t)(d * d + d) * 4;
-    const int force = env_flag("LA_STATE_FUSED", -1);
+    const int force = knob(K_STATE_FUSED, -1);
     const bool fused = dtype == LA_BF16 && (force >= 0 ? force != 0 : head_partials <= kFusedCombineBytes);
     StateArgs a;
     a.K = K;
@@ -345,7 +418,7 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
               int d, int gt, int gh, int gw, float eps, int dtype, hipStream_t st) {
     if (ntok == 0) return LA_OK;
     const LaGeom g = make_geom(B, H, ntok, n_offset, d, gt, gh, gw);
-    Plan pl;
+    ApplyPlan pl;
     int rc = plan_apply(g, d, dtype, &pl);
     if (rc != LA_OK) return rc;
     ApplyArgs a;
@@ -356,35 +429,24 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
     a.eps = eps;
     a.chunk = pl.chunk;
     a.P = pl.P;
-    a.ilv = 0;
+    a.ilv = pl.ilv;
+    a.nph = pl.nph;
+    a.hs = pl.hs;
     a.g = g;
-    // bf16: the head's P workgroups take interleaved units of the whole head
-    // instead of one contiguous chunk each, so that each head's reads and
-    // writes advance as one window rather than P separate streams (3-4%
-    // faster at 720p-5s; same arithmetic per token, so bitwise equal outputs).
-    // LA_APPLY_ILV=0 keeps contiguous chunks.
-    if (dtype == LA_BF16 && pl.P > 1 && env_flag("LA_APPLY_ILV", 1) != 0 &&
-        ((size_t)ntok + (size_t)pl.P * 1024) * d * 2 < (1ull << 32)) {  // units overrun the head by < P * 1024 tokens
-        const size_t lds = pl.lds - table_entries(g, pl.chunk) * 8 + table_entries(g, ntok) * 8;
-        if (lds <= kLdsLimit) {
-            a.ilv = 1;
-            pl.lds = lds;
-        }
-    }
     const int threads = dtype != LA_BF16 ? 256
                         : d == 32        ? ApplyBf16Cfg<32>::THREADS
                         : d == 64        ? ApplyBf16Cfg<64>::THREADS
                         : d == 112       ? ApplyBf16Cfg<112>::THREADS
                                          : ApplyBf16Cfg<128>::THREADS;
-    return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.P * g.BH), pl.lds, st, a, threads);
+    return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.grid), pl.lds, st, a, threads);
 }
 
-// Token-causal pass: about LA_CAUSAL_WGS workgroups (default two 256-thread
+// Token-causal pass: about causal_wgs workgroups (default two 256-thread
 // workgroups per CU), chunks a multiple of 128 tokens (the state kernel's tile
 // at d = 64 and two causal steps), at most kMaxPartials per head.
 int plan_causal(const LaGeom& g, Plan* out) {
     constexpr int unit = 128;
-    const int target = env_int("LA_CAUSAL_WGS", 512);
+    const int target = knob(K_CAUSAL_WGS, 512);
     const int ntok = g.ntok;
     int P = target / g.BH;  // at most `target` workgroups (see plan_state)
     P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
@@ -416,8 +478,8 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     // Partial states in 512-thread workgroups, two per CU: the P chunks per
     // head (512 workgroups at 720p-5s) then run in one round instead of two
     // rounds of 1024-thread workgroups (235 -> 229 us per call at 720p-5s).
-    // LA_TC_STATE_THREADS=1024 selects the larger workgroups.
-    const bool half = env_int("LA_TC_STATE_THREADS", 512) == 512;
+    // The tuning knob tc_state_threads = 1024 selects the larger workgroups.
+    const bool half = knob(K_TC_STATE_THREADS, 512) == 512;
     rc = plan_state(g, d, LA_BF16, &ps, pc.chunk, half ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
     if (rc != LA_OK) return rc;
     const WsLayout L = ws_layout(g.BH, d);
@@ -473,7 +535,8 @@ int precheck_plans(int B, int H, int ntok, int n_offset, int d, int gt, int gh, 
         if (rc != LA_OK) return rc;
     }
     if (apply && ntok > 0) {
-        int rc = plan_apply(g, d, dtype, &pl);
+        ApplyPlan pa;
+        int rc = plan_apply(g, d, dtype, &pa);
         if (rc != LA_OK) return rc;
     }
     return LA_OK;
@@ -633,8 +696,8 @@ int la_temporal_conv_step(const void* X, void* Y, const void* W, const float* bi
     if ((long long)B * a.nft * a.npt >= (1ll << 31) / 8) return LA_E_UNSUPPORTED;
     a.mtiles = B * a.nft * a.npt;
     a.ntiles = (D + TconvCfg::BN - 1) / TconvCfg::BN;
-    a.gm = env_int("LA_TCONV_GM", 8);
-    a.gn = env_int("LA_TCONV_GN", 7);
+    a.gm = knob(K_TCONV_GM, 8);
+    a.gn = knob(K_TCONV_GN, 7);
     if ((long long)a.mtiles * a.ntiles >= (1ll << 31)) return LA_E_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours
@@ -670,6 +733,22 @@ int la_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
 }
 
 const char* la_last_hip_error(void) { return g_hip_msg; }
+
+int la_set_tuning(const char* name, int value) {
+    if (!name) return LA_E_NULLPTR;
+    for (int k = 0; k < K_COUNT; ++k) {
+        if (strcmp(name, kKnobs[k].name) != 0) continue;
+        if (value < 0) {
+            g_knob[k] = -1;
+            return LA_OK;
+        }
+        if (value < kKnobs[k].lo || value > kKnobs[k].hi) return LA_E_SHAPE;
+        if (k == K_TC_STATE_THREADS && value != 512 && value != 1024) return LA_E_SHAPE;
+        g_knob[k] = value;
+        return LA_OK;
+    }
+    return LA_E_UNSUPPORTED;
+}
 
 const char* la_strerror(int status) {
     switch (status) {

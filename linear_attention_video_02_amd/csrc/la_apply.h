@@ -15,9 +15,11 @@ struct ApplyArgs {
     const float* S;  // [BH][D*D]
     const float* z;  // [BH][D]
     float eps;
-    int chunk;       // tokens per workgroup
-    int P;           // workgroups per (batch, head)
-    int ilv;         // bf16: 1 = the head's workgroups take interleaved units of the whole head
+    int chunk;       // ilv = 0: tokens per workgroup
+    int P;           // workgroups per head
+    int ilv;         // bf16: 1 = the head's P workgroups take interleaved units of the whole head
+    int nph;         // ilv = 1: heads per workgroup, one after another (phases)
+    int hs;          // ilv = 1: head slots; phase k of slot j is head k * hs + j
     LaGeom g;
 };
 
@@ -43,15 +45,24 @@ struct ApplyArgs {
 // so a lane ends with 8 consecutive output channels per pair of tiles: one
 // 16-byte store each.  The denominator is summed over the 4 lanes of a token
 // with two cross-lane xors.
-// One 512-thread workgroup (8 waves; 4 at d = 128) per CU over a chunk of one head; each
-// wave takes UNIT-token units of the chunk from an LDS queue and keeps DEPTH
-// units of Q in flight.
+//
+// Work split (interleaved mode, the default).  Few heads are in flight at a
+// time: P workgroups share each head (unit u of the head goes to workgroup
+// u mod P), and every workgroup works through nph heads one after another
+// (phase k of head slot j is head k * hs + j).  A copy of Q to O shaped like
+// this runs at the rate of a plain copy when a handful of heads are in
+// flight, and ~10% slower when every head of the call is (one read and one
+// write window per head).  The S^T copies (fp16, scaled) and z of all the
+// workgroup's heads are prepared in LDS at the start; a wave that moves on to
+// the next head reloads its operands from there, so no wave waits for another.
+// Each wave takes UNIT-token units from the workgroup's LDS queue of the
+// current phase and keeps DEPTH units of Q in flight.
 // ---------------------------------------------------------------------------
 template <int D>
 struct ApplyBf16Cfg {
     static constexpr int DP = Pad<D>::P;  // channels on chip (zero above D)
     // d <= 64: 8 waves per CU (2 per SIMD: S^T hi + lo in registers);
-    // d >= 112: 12 waves (S^T in LDS, <= 168 registers a lane)
+    // d >= 112: 12 waves (S^T read from LDS per k-step, <= 168 registers a lane)
     static constexpr int THREADS = D <= 64 ? 512 : 768;
     static constexpr int NW = THREADS / 64;
     static constexpr int KS = DP / 32;  // 32-channel k-steps
@@ -59,21 +70,23 @@ struct ApplyBf16Cfg {
     static constexpr int GR = D <= 64 ? 2 : 1;   // 16-token groups per unit of work
     static constexpr int UNIT = 16 * GR;         // tokens a wave takes from the queue at a time
     static constexpr int DEPTH = D <= 64 ? 3 : 2;  // units of Q in flight per wave
-    // d >= 112: S^T (fp16) lives in LDS instead of registers (128 x 128
-    // fp16 would take 128 registers a lane); MFMA A fragments are read from it
+    // d >= 112: the MFMA A fragments are read from the LDS copy of S^T per
+    // k-step (128 x 128 fp16 in registers would take 128 a lane)
     static constexpr bool SLDS = DP > 64;
+    // heads per workgroup at most (their S^T copies share the LDS)
+    static constexpr int MAXPH = DP > 64 ? 2 : 8;
     // d = 64: Q and O pass through a per-wave LDS tile so that every global
     // load / store instruction moves 8 whole 128-byte rows (the MFMA operand
     // layout would touch 16 rows per instruction, half of each line).
     static constexpr bool STG = D == 64;
     static constexpr int RPI = 8;                          // rows per staged load / store
     static constexpr int NI = UNIT / RPI;                  // staged loads per unit (= GR * KS)
-    static constexpr int ZBYTES = DP * 4;                  // z, S^T, staging, then the RoPE table
-    // d <= 64: S^T in fp32 (row stride d + 4), read once into the fragments
-    static constexpr int SROW = D + 4;
-    static constexpr int SBYTES = SLDS ? DP * DP * 2 : D * SROW * 4;
     static constexpr int STGBYTES = STG ? NW * 2 * UNIT * D * 2 : 0;
-    static constexpr int FIXED = ZBYTES + SBYTES + STGBYTES;
+    static constexpr int SHEAD = DP * DP * 2;              // fp16 S^T of one head
+    static constexpr int ZHEAD = DP * 4;                   // z of one head (zero above d)
+    // LDS: staging tiles, then nph x (S^T, z), then the RoPE table
+    static constexpr int FIXED = STGBYTES;
+    static constexpr int PERHEAD = SHEAD + ZHEAD;
     static_assert(!STG || NI == GR * KS, "staged unit = register ring slot");
 };
 
@@ -86,19 +99,19 @@ __device__ __forceinline__ int stg_off(int r, int c) {
 }
 
 // Element offset of S^T row pr (= 16 T + m, see below), 16-byte chunk c, in
-// the LDS copy used at d >= 112: chunks are XOR-swizzled by row so that 16
-// consecutive rows read at one chunk hit 16 distinct bank groups.
+// the LDS copy: chunks are XOR-swizzled by row (within the row's DP / 8
+// chunks) so that consecutive rows read at one chunk spread over the banks.
 template <int DP>
 __device__ __forceinline__ int st_off(int pr, int c) {
-    return pr * DP + ((c ^ (pr & 15)) << 3);
+    return pr * DP + ((c ^ (pr & (DP / 8 - 1))) << 3);
 }
 
 // Work item mapping shared with the state pass (whole heads per XCD).
-__device__ __forceinline__ void apply_item_of_block(int P, int BH, int& bh, int& p) {
-    const int T = P * BH;
+__device__ __forceinline__ void apply_item_of_block(int P, int NS, int& slot, int& p) {
+    const int T = P * NS;
     const int i = blockIdx.x;
     const int k = (T % 8 == 0) ? (i % 8) * (T / 8) + i / 8 : i;
-    bh = k / P;
+    slot = k / P;
     p = k % P;
 }
 
@@ -106,41 +119,76 @@ template <int D, bool ROPE>
 __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel(ApplyArgs a) {
     using C = ApplyBf16Cfg<D>;
     extern __shared__ __align__(16) unsigned char smem[];
-    float* zs = (float*)smem;                        // [DP] z (zero above d)
-    uint16_t* st = (uint16_t*)(smem + C::ZBYTES);    // [DP][DP] S^T hi (d >= 112)
-    uint16_t* stg = (uint16_t*)(smem + C::ZBYTES + C::SBYTES);  // [NW][Q, O][UNIT][D] (d = 64)
-    float2* tab = (float2*)(smem + C::FIXED);
-    __shared__ int q_next;  // next unit of this workgroup's chunk, in tokens
-    __shared__ float smax[C::NW];  // per-wave max |S|
+    const bool ilv = a.ilv != 0;
+    const int nph = ilv ? a.nph : 1;
+    uint16_t* stg = (uint16_t*)smem;                                // [NW][Q, O][UNIT][D] (d = 64)
+    uint16_t* st16 = (uint16_t*)(smem + C::FIXED);                  // [nph][DP*DP] fp16 S^T
+    float* zs = (float*)(smem + C::FIXED + nph * C::SHEAD);         // [nph][DP] z
+    float2* tab = (float2*)(smem + C::FIXED + nph * C::PERHEAD);
+    __shared__ int q_next[C::MAXPH];         // next unit of each phase's queue, in tokens
+    __shared__ float smax[C::MAXPH][C::NW];  // per-wave max |S| of each head
+    __shared__ int eSs[C::MAXPH];            // per-head exponent of the S^T scale
 
     const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
-    int bh, p;
-    apply_item_of_block(a.P, a.g.BH, bh, p);
+    const int BH = a.g.BH;
+    int slot, p;
+    apply_item_of_block(a.P, ilv ? a.hs : BH, slot, p);
+    auto head_of = [&](int ph) -> int { return ilv ? ph * a.hs + slot : slot; };
     const int ntok = a.g.ntok;
-    const bool ilv = a.ilv != 0;
     const int c0 = ilv ? 0 : p * a.chunk;
     const int c1 = ilv ? ntok : min(c0 + a.chunk, ntok);
     const int len = c1 > c0 ? c1 - c0 : 0;
     // queue position q (in tokens) -> first token of the unit, within [c0, c1)
     auto tok_of = [&](int q) -> int { return ilv ? ((q / C::UNIT) * a.P + p) * C::UNIT : q; };
-    // Q and O of this chunk through descriptors bounded to [c0, c1): rows
+    // Q and O of a head's chunk through descriptors bounded to [c0, c1): rows
     // past c1 read as zeros and their stores are dropped.
-    const size_t chunk_off = ((size_t)bh * ntok + c0) * D;
     const uint32_t chunk_bytes = (uint32_t)len * D * 2;
-    const BufRsrc Qr = make_rsrc((const uint16_t*)a.Q + chunk_off, chunk_bytes);
-    const BufRsrc Or = make_rsrc((uint16_t*)a.O + chunk_off, chunk_bytes);
+    auto q_rsrc = [&](int head) {
+        return make_rsrc((const uint16_t*)a.Q + ((size_t)head * ntok + c0) * D, chunk_bytes);
+    };
+    auto o_rsrc = [&](int head) { return make_rsrc((uint16_t*)a.O + ((size_t)head * ntok + c0) * D, chunk_bytes); };
 
-    if (threadIdx.x == 0) q_next = C::NW * C::DEPTH * C::UNIT;  // the first units are pre-assigned
-    // Units of UNIT tokens are taken from the workgroup's queue, so waves that
-    // run faster (the sequencer favours older waves) take more of the chunk.
-    auto grab = [&]() -> int {
-        int v = 0;
-        if (lane == 0) v = atomicAdd(&q_next, C::UNIT);
-        return __builtin_amdgcn_readfirstlane(v);
+    if (threadIdx.x < C::MAXPH) q_next[threadIdx.x] = threadIdx.x == 0 ? C::NW * C::DEPTH * C::UNIT : 0;
+
+    // S of every head of this workgroup, fetched before the first Q loads.
+    // Loads return in order, so fetched after them the conversion below (and
+    // every wave's first MFMA) would wait until all of the first units of Q
+    // had arrived.  S comes in with coalesced 16-byte loads and goes to LDS
+    // transposed and rounded to fp16, where each lane reads its fragments.
+    constexpr int S4 = (D * D / 4 + C::THREADS - 1) / C::THREADS;  // float4s a thread per head
+    f32x4 sraw[C::MAXPH][S4];
+#pragma unroll
+    for (int ph = 0; ph < C::MAXPH; ++ph) {
+        const int hd = head_of(ph);
+        if (ph < nph && hd < BH) {
+            const float* Sh = a.S + (size_t)hd * D * D;
+#pragma unroll
+            for (int i = 0; i < S4; ++i) {
+                const int f = threadIdx.x + i * C::THREADS;
+                if (f < D * D / 4) sraw[ph][i] = *(const f32x4*)(Sh + 4 * f);
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of Q's
+
+    // the ring: slot s holds the unit (phase, first token) whose Q is in qr[s]
+    int wph = 0;  // this wave's current phase for taking units
+    auto take = [&]() -> int2 {
+        for (;;) {
+            if (wph >= nph) return make_int2(nph, 0);
+            int v = 0;
+            if (lane == 0) v = atomicAdd(&q_next[wph], C::UNIT);
+            const int tok = tok_of(__builtin_amdgcn_readfirstlane(v));
+            if (tok < len && head_of(wph) < BH) return make_int2(wph, tok);
+            ++wph;
+        }
     };
     u32x4 qr[C::DEPTH][C::GR][C::KS];
-    auto load_unit = [&](u32x4 (&q)[C::GR][C::KS], int u0) {
+    auto load_unit = [&](u32x4 (&q)[C::GR][C::KS], int2 u) {
+        const BufRsrc Qr = q_rsrc(u.x < nph ? head_of(u.x) : slot);
+        const int u0 = u.x < nph ? u.y : len;  // none: a read past the end (zeros)
         if (C::STG) {  // whole rows: lane -> row RPI*i + lane/8, 16-byte chunk lane%8
 #pragma unroll
             for (int i = 0; i < C::NI; ++i)
@@ -156,123 +204,18 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 q[r][ks] = buf_load16(Qr, (uint32_t)(tl * D + 32 * ks + 8 * g) * 2u);
         }
     };
-    // d <= 64: S and this lane's z entries are fetched before the first Q
-    // loads.  Loads return in order, so fetched after them the conversion
-    // below (and every wave's first MFMA) would wait until all of the first
-    // units of Q had arrived -- at kernel start, when every CU asks at once,
-    // that is several microseconds.  S comes in with coalesced 16-byte loads
-    // (a lane's fragment entries lie in 8 different rows of S, which as
-    // single-word global loads would be 64 per lane) and goes to LDS
-    // transposed, where each lane reads its fragments as 16-byte rows.
-    // (d >= 112 likewise: S comes in with the same coalesced loads, ahead of
-    // Q's, and goes from registers straight into the fp16 copy in LDS.)
-    const float* Sh = a.S + (size_t)bh * D * D;
-    constexpr int S4 = (D * D / 4 + C::THREADS - 1) / C::THREADS;  // float4s a thread
-    f32x4 sraw[S4];
-    float zraw[C::SLDS ? 1 : C::KS][8];
-#pragma unroll
-    for (int i = 0; i < S4; ++i) {
-        const int f = threadIdx.x + i * C::THREADS;
-        if (f < D * D / 4) sraw[i] = *(const f32x4*)(Sh + 4 * f);
-    }
-    if (!C::SLDS) {
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) zraw[ks][e] = a.z[(size_t)bh * D + 32 * ks + 8 * g + e];
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of Q's
-    // first DEPTH units of each wave: fixed, so their loads go out before the
-    // prologue work
-    const int wave = threadIdx.x >> 6;
-    int us[C::DEPTH];
+    // first DEPTH units of each wave: fixed positions of phase 0's queue (the
+    // queue starts past them), so their loads go out before the prologue work.
+    // A position past the head's end (tiny heads) leaves the slot to be
+    // filled from the queues once they are initialised (x = -1).
+    int2 us[C::DEPTH];
+    bool fixed = head_of(0) < BH;
 #pragma unroll
     for (int s = 0; s < C::DEPTH; ++s) {
-        us[s] = tok_of((s * C::NW + wave) * C::UNIT);
-        load_unit(qr[s], us[s]);
-    }
-
-    // S^T fragments (fp16, scaled by 2^-eS) and this lane's z entries
-    f16x8 A16[C::SLDS ? 1 : C::NT][C::KS];
-    float* sT = (float*)st;  // d <= 64: [D][SROW] fp32, sT[co][ci] = S[ci][co]
-    float amax = 0.0f;       // this thread's largest |S| entry
-#pragma unroll
-    for (int i = 0; i < S4; ++i) {
-        const int f = threadIdx.x + i * C::THREADS;
-        if (f < D * D / 4) {
-            const int ci = f / (D / 4), co = 4 * (f % (D / 4));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (!C::SLDS) sT[(co + j) * C::SROW + ci] = sraw[i][j];
-                amax = fmaxf(amax, fabsf(sraw[i][j]));
-            }
-        }
-    }
-    amax = wave_max(amax);
-    if (lane == 0) smax[wave] = amax;
-    // eS: the head's largest |S| times 2^-eS lies in [2^13, 2^14) (read after
-    // a barrier that follows the smax writes)
-    auto head_scale = [&]() -> int {
-        float hmax = 0.0f;
-#pragma unroll
-        for (int w = 0; w < C::NW; ++w) hmax = fmaxf(hmax, smax[w]);
-        int e = 0;
-        if (hmax > 0.0f) {
-            (void)frexpf(hmax, &e);
-            e -= 14;
-        }
-        return e;
-    };
-    int eS = 0;
-    if (C::SLDS) {
-        lds_barrier();
-        eS = head_scale();
-        // row pr = 16 T + m of the copy holds value channel co(T, m), the MFMA
-        // row order used below; element k is S[k][co] 2^-eS (zero past d)
-        auto put_st = [&](int k, int co, float sv) {
-            const int T = 2 * (co >> 5) + ((co >> 2) & 1);
-            const int m = (((co >> 3) & 3) << 2) | (co & 3);
-            st[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] =
-                __builtin_bit_cast(uint16_t, (_Float16)ldexpf(sv, -eS));
-        };
-#pragma unroll
-        for (int i = 0; i < S4; ++i) {
-            const int f = threadIdx.x + i * C::THREADS;
-            if (f < D * D / 4) {
-                const int k = f / (D / 4), co = 4 * (f % (D / 4));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put_st(k, co + j, sraw[i][j]);
-            }
-        }
-        // the padding rows and columns (key or value channel >= d)
-        for (int e = threadIdx.x; e < C::DP * C::DP - D * D; e += C::THREADS) {
-            int k, co;
-            if (e < D * (C::DP - D)) {
-                k = e / (C::DP - D);
-                co = D + e % (C::DP - D);
-            } else {
-                k = D + (e - D * (C::DP - D)) / C::DP;
-                co = (e - D * (C::DP - D)) % C::DP;
-            }
-            put_st(k, co, 0.0f);
-        }
-    }
-    if (C::SLDS)  // (d <= 64 sums the denominator on the MFMA from registers)
-        for (int c = threadIdx.x; c < C::DP; c += C::THREADS) zs[c] = c < D ? a.z[(size_t)bh * D + c] : 0.0f;
-    // d <= 64: the denominator relu(q).z runs on the MFMA too, with z as an A
-    // tile of 16 identical rows (bf16 hi + lo) and the un-rotated relu(q) --
-    // exact in bf16 -- as B: every accumulator of a token's lanes is its sum.
-    bf16x8 Azh[C::SLDS ? 1 : C::KS], Azl[C::SLDS ? 1 : C::KS];
-    if (!C::SLDS) {
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float zv = zraw[ks][e];
-                const __bf16 hi = (__bf16)zv;
-                Azh[ks][e] = hi;
-                Azl[ks][e] = (__bf16)(zv - (float)hi);
-            }
+        const int tok = tok_of((s * C::NW + wave) * C::UNIT);
+        fixed = fixed && tok < len;  // (tokens grow with s: once past the end, all later are too)
+        us[s] = fixed ? make_int2(0, tok) : make_int2(-1, 0);
+        if (fixed) load_unit(qr[s], us[s]);
     }
 
     int t_lo = 0, nt = 1;
@@ -288,31 +231,127 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             for (int i = 0; i < 4; ++i)
                 pr[ks][i] = pair_ref((C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g + i : 0, nt, a.g);
     }
-    lds_barrier();  // RoPE table, S^T copy, per-wave max |S| and queue head visible
-    if (!C::SLDS) eS = head_scale();
-    // this lane's S^T fragments: value channel co(T, n), key channels
-    // 32 ks + 8 g .. +7 -- two 16-byte LDS reads each
+
+    // each head's largest |S|: per thread, per wave, then over the waves
 #pragma unroll
-    for (int T = 0; T < (C::SLDS ? 0 : C::NT); ++T) {
-        const int co = 32 * (T >> 1) + 8 * (n >> 2) + 4 * (T & 1) + (n & 3);
+    for (int ph = 0; ph < C::MAXPH; ++ph) {
+        if (ph < nph && head_of(ph) < BH) {
+            float amax = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            const f32x4 v0 = *(const f32x4*)(sT + co * C::SROW + 32 * ks + 8 * g);
-            const f32x4 v1 = *(const f32x4*)(sT + co * C::SROW + 32 * ks + 8 * g + 4);
+            for (int i = 0; i < S4; ++i) {
+                const int f = threadIdx.x + i * C::THREADS;
+                if (f < D * D / 4)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) A16[T][ks][e] = (_Float16)ldexpf(e < 4 ? v0[e] : v1[e - 4], -eS);
+                    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(sraw[ph][i][j]));
+            }
+            amax = wave_max(amax);
+            if (lane == 0) smax[ph][wave] = amax;
         }
     }
+    lds_barrier();  // per-wave maxima (and the RoPE table) visible
+    // eS: the head's largest |S| times 2^-eS lies in [2^13, 2^14); S^T rows in
+    // the MFMA row order: row pr = 16 T + m holds value channel co(T, m),
+    // element k is S[k][co] 2^-eS (zero past d)
+#pragma unroll
+    for (int ph = 0; ph < C::MAXPH; ++ph) {
+        const int hd = head_of(ph);
+        if (ph < nph && hd < BH) {
+            float hmax = 0.0f;
+#pragma unroll
+            for (int w = 0; w < C::NW; ++w) hmax = fmaxf(hmax, smax[ph][w]);
+            int eS = 0;
+            if (hmax > 0.0f) {
+                (void)frexpf(hmax, &eS);
+                eS -= 14;
+            }
+            if (threadIdx.x == 0) eSs[ph] = eS;
+            uint16_t* sth = st16 + ph * C::DP * C::DP;
+            auto put_st = [&](int k, int co, float sv) {
+                const int T = 2 * (co >> 5) + ((co >> 2) & 1);
+                const int m = (((co >> 3) & 3) << 2) | (co & 3);
+                sth[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] =
+                    __builtin_bit_cast(uint16_t, (_Float16)ldexpf(sv, -eS));
+            };
+#pragma unroll
+            for (int i = 0; i < S4; ++i) {
+                const int f = threadIdx.x + i * C::THREADS;
+                if (f < D * D / 4) {
+                    const int k = f / (D / 4), co = 4 * (f % (D / 4));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) put_st(k, co + j, sraw[ph][i][j]);
+                }
+            }
+            // the padding rows and columns (key or value channel >= d)
+            for (int e = threadIdx.x; e < C::DP * C::DP - D * D; e += C::THREADS) {
+                int k, co;
+                if (e < D * (C::DP - D)) {
+                    k = e / (C::DP - D);
+                    co = D + e % (C::DP - D);
+                } else {
+                    k = D + (e - D * (C::DP - D)) / C::DP;
+                    co = (e - D * (C::DP - D)) % C::DP;
+                }
+                put_st(k, co, 0.0f);
+            }
+            for (int c = threadIdx.x; c < C::DP; c += C::THREADS)
+                zs[ph * C::DP + c] = c < D ? a.z[(size_t)hd * D + c] : 0.0f;
+        }
+    }
+    lds_barrier();  // S^T copies, z, exponents and the queue heads visible
+#pragma unroll
+    for (int s = 0; s < C::DEPTH; ++s)
+        if (us[s].x < 0) {
+            us[s] = take();
+            load_unit(qr[s], us[s]);
+        }
+
+    // operands of the head in use: S^T fragments (d <= 64, registers) --
+    // value channel co(T, n), key channels 32 ks + 8 g .. +7 -- and z; d <= 64
+    // also holds z as an A tile of 16 identical rows (bf16 hi + lo) for the
+    // denominator on the MFMA (the un-rotated relu(q), exact in bf16, is B)
+    f16x8 A16[C::SLDS ? 1 : C::NT][C::KS];
+    bf16x8 Azh[C::SLDS ? 1 : C::KS], Azl[C::SLDS ? 1 : C::KS];
+    int cur = -1, eS = 0;
+    const uint16_t* sth = st16;
+    const float* zh = zs;
+    auto use_head = [&](int ph) {
+        cur = ph;
+        eS = eSs[ph];
+        sth = st16 + ph * C::DP * C::DP;
+        zh = zs + ph * C::DP;
+        if (!C::SLDS) {
+#pragma unroll
+            for (int T = 0; T < C::NT; ++T)
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks)
+                    A16[T][ks] = *(const f16x8*)(sth + st_off<C::DP>(16 * T + n, 4 * ks + g));
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const f32x4 z0 = *(const f32x4*)(zh + 32 * ks + 8 * g);
+                const f32x4 z1 = *(const f32x4*)(zh + 32 * ks + 8 * g + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float zv = e < 4 ? z0[e] : z1[e - 4];
+                    const __bf16 hi = (__bf16)zv;
+                    Azh[ks][e] = hi;
+                    Azl[ks][e] = (__bf16)(zv - (float)hi);
+                }
+            }
+        }
+    };
 
     bool more = true;
     while (more) {
 #pragma unroll
         for (int s = 0; s < C::DEPTH; ++s) {
-            const int u0 = us[s];
-            if (u0 >= len) {  // units are taken in increasing order: nothing left
+            const int2 uc = us[s];
+            if (uc.x >= nph) {  // units are taken in increasing order: nothing left
                 more = false;
                 break;
             }
+            const int u0 = uc.y;
+            if (uc.x != cur) use_head(uc.x);
+            const BufRsrc Or = o_rsrc(head_of(uc.x));
             u32x4 qc[C::GR][C::KS];
             uint16_t* wq = stg + wave * (2 * C::UNIT * D);  // this wave's Q tile, then its O tile
             uint16_t* wo = wq + C::UNIT * D;
@@ -334,7 +373,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
                     for (int ks = 0; ks < C::KS; ++ks) qc[r][ks] = qr[s][r][ks];
             }
-            us[s] = tok_of(grab());
+            us[s] = take();
             load_unit(qr[s], us[s]);
 
 #pragma unroll
@@ -348,10 +387,11 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
                 for (int T = 0; T < C::NT; ++T) acc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
                 // relu(Q) of the group (channels past d, loaded from the next
-                // row at d = 112, are zeroed), and whether any lane holds a
-                // value fp16 cannot carry exactly enough: then every token of
-                // the group is scaled by 2^sc, sc = 13 - (exponent of its
-                // largest relu(Q) value)
+                // row at d = 112, are zeroed): the token's largest value (0:
+                // the row is zero and so is its output), and whether any lane
+                // holds a value fp16 cannot carry exactly enough: then every
+                // token of the group is scaled by 2^sc, sc = 13 - (exponent of
+                // its largest relu(Q) value)
                 uint32_t m16 = 0;
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
@@ -359,18 +399,15 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     const uint32_t mk = live ? max_relu_bits8(qc[r][ks]) : 0u;
                     m16 = mk > m16 ? mk : m16;
                 }
+                uint32_t tm = m16;
+                tm = max(tm, (uint32_t)__shfl_xor((int)tm, 16));
+                tm = max(tm, (uint32_t)__shfl_xor((int)tm, 32));
                 // bf16 bit patterns of 2^-6 and 2^14
                 const bool odd = m16 != 0 && (m16 < 0x3C80u || m16 >= 0x4680u);
                 // (d >= 112: always, without a branch -- a branch inside the
                 // k-step loop makes the 768-thread kernel spill registers)
                 const bool scaled = C::SLDS || __builtin_amdgcn_ballot_w64(odd) != 0;
-                int sc = 0;
-                if (scaled) {
-                    uint32_t tm = m16;
-                    tm = max(tm, (uint32_t)__shfl_xor((int)tm, 16));
-                    tm = max(tm, (uint32_t)__shfl_xor((int)tm, 32));
-                    sc = tm != 0 ? 13 - ((int)(tm >> 7) - 127) : 0;
-                }
+                const int sc = scaled && tm != 0 ? 13 - ((int)(tm >> 7) - 127) : 0;
                 // one 32-channel k-step at a time: its B fragments, then its MFMAs
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
@@ -384,8 +421,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                         x[2 * i + 1] = bf_hi(w4[i]);
                     }
                     if (C::SLDS) {
-                        const float4 za = *(const float4*)(zs + 32 * ks + 8 * g);
-                        const float4 zb = *(const float4*)(zs + 32 * ks + 8 * g + 4);
+                        const float4 za = *(const float4*)(zh + 32 * ks + 8 * g);
+                        const float4 zb = *(const float4*)(zh + 32 * ks + 8 * g + 4);
                         den = fmaf(x[0], za.x, den); den = fmaf(x[1], za.y, den);
                         den = fmaf(x[2], za.z, den); den = fmaf(x[3], za.w, den);
                         den = fmaf(x[4], zb.x, den); den = fmaf(x[5], zb.y, den);
@@ -409,7 +446,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     const f16x8 Bq = __builtin_bit_cast(f16x8, hw);
 #pragma unroll
                     for (int T = 0; T < C::NT; ++T) {
-                        const f16x8 A = C::SLDS ? *(const f16x8*)(st + st_off<C::DP>(16 * T + n, 4 * ks + g))
+                        const f16x8 A = C::SLDS ? *(const f16x8*)(sth + st_off<C::DP>(16 * T + n, 4 * ks + g))
                                                 : A16[C::SLDS ? 0 : T][ks];
                         acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq, acc[T], 0, 0, 0);
                     }
@@ -424,8 +461,10 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     den = dacc[0];
                 }
                 den += a.eps;
-                // undo the scalings: S by 2^-eS, the group's tokens by 2^sc
-                const float inv = den > 0.0f ? ldexpf(1.0f / den, eS - sc) : 0.0f;
+                // undo the scalings (S by 2^-eS, the group's tokens by 2^sc)
+                // and divide; a zero row stays zero, a live row takes the IEEE
+                // quotient (NaN or inf only where its denominator is 0 or NaN)
+                const float inv = tm != 0 ? ldexpf(1.0f / den, eS - sc) : 0.0f;
 #pragma unroll
                 for (int sp = 0; sp < C::NT / 2; ++sp) {
                     u32x4 o;
@@ -460,7 +499,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 template <int D>
 struct ApplyF32Cfg {
     static constexpr int TT = 32;
-    static constexpr int SMEM_FIXED = (D * D + D + 2 * TT * D + TT) * 4;
+    static constexpr int SMEM_FIXED = (D * D + D + 2 * TT * D + 2 * TT) * 4;
 };
 
 template <int D, bool ROPE>
@@ -471,7 +510,8 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
     float* zs = Ss + D * D;          // [D]
     float* qp = zs + D;              // [TT][D] relu(Q)
     float* qq = qp + C::TT * D;      // [TT][D] RoPE(relu(Q))
-    float* dn = qq + C::TT * D;      // [TT]
+    float* dn = qq + C::TT * D;      // [TT] denominators
+    int* lv = (int*)(dn + C::TT);    // [TT] 1: relu(Q) of the row is not all zero
     float2* tab = (float2*)(smem + C::SMEM_FIXED);
 
     const int tid = threadIdx.x;
@@ -516,8 +556,13 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
         lds_barrier();
         if (tid < C::TT) {
             float s = 0.0f;
-            for (int c = 0; c < D; ++c) s = fmaf(qp[tid * D + c], zs[c], s);
+            bool live = false;
+            for (int c = 0; c < D; ++c) {
+                s = fmaf(qp[tid * D + c], zs[c], s);
+                live = live || qp[tid * D + c] > 0.0f;
+            }
             dn[tid] = s + a.eps;
+            lv[tid] = live;
         }
         lds_barrier();
         for (int i = tid; i < C::TT * D; i += 256) {
@@ -526,8 +571,8 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
             if (tok >= c1) continue;
             float s = 0.0f;
             for (int ci = 0; ci < D; ++ci) s = fmaf(qq[tl * D + ci], Ss[ci * D + co], s);
-            const float den = dn[tl];
-            Oh[(size_t)tok * D + co] = den > 0.0f ? s / den : 0.0f;
+            // a zero row stays zero; a live row takes the IEEE quotient
+            Oh[(size_t)tok * D + co] = lv[tl] ? s / dn[tl] : 0.0f;
         }
     }
 }

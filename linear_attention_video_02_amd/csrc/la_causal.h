@@ -304,6 +304,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
         // ---------------- B: outputs of this wave's 16 queries ----------------
         const float* zc = zbuf + cur * D;
         float den = 0.0f;
+        uint32_t qbits = 0;  // non-zero iff this lane's relu(Q) values are not all zero
         bf16x8 Bq[C::KS], Bl[C::KS], Bu[C::KS];
         Pos3 qps;
         if (ROPE) qps = token_pos((uint32_t)(a.g.n_offset + min(c0 + t0 + 16 * wave + n, c1 - 1)), t_lo, a.g);
@@ -319,6 +320,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
                 x[2 * i + 1] = bf_hi(w);
             }
             Bu[ks] = __builtin_bit_cast(bf16x8, u4);
+            qbits |= (u4[0] | u4[1]) | (u4[2] | u4[3]);
             const float4 za = *(const float4*)(zc + 32 * ks + 8 * g);
             const float4 zb = *(const float4*)(zc + 32 * ks + 8 * g + 4);
             den = fmaf(x[0], za.x, den); den = fmaf(x[1], za.y, den);
@@ -402,7 +404,11 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, 2) void la_causal_bf16_k
         den += __shfl_xor(den, 16);
         den += __shfl_xor(den, 32);
         den += a.eps;
-        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        // a zero row stays zero; a live row takes the IEEE quotient (NaN or
+        // inf only where its denominator is 0 or NaN)
+        qbits |= (uint32_t)__shfl_xor((int)qbits, 16);
+        qbits |= (uint32_t)__shfl_xor((int)qbits, 32);
+        const float inv = qbits != 0 ? 1.0f / den : 0.0f;
         {
             const int tl = t0 + 16 * wave + n;
 #pragma unroll

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
                           "la_block_causal_step", "la_token_causal", "la_temporal_conv_step",
-                          "la_stream_copy", "la_strerror", "la_last_hip_error"}
+                          "la_stream_copy", "la_strerror", "la_last_hip_error", "la_set_tuning"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -232,6 +232,20 @@ def test_stream_copy_rejects(L):
     assert L.la_stream_copy(p(8), p(1 << 30), 64, None) == E["LA_E_ALIGN"]
     assert L.la_stream_copy(p(0), p(1 << 30), 60, None) == E["LA_E_ALIGN"]
     assert L.la_stream_copy(p(0), p(32), 64, None) == E["LA_E_ALIAS"]
+
+
+def test_set_tuning(L):
+    assert L.la_set_tuning(b"apply_heads", 4) == 0
+    assert L.la_set_tuning(b"apply_heads", -1) == 0              # back to the default
+    assert L.la_set_tuning(b"apply_heads", 9) == E["LA_E_SHAPE"]
+    assert L.la_set_tuning(b"state_fused", 2) == E["LA_E_SHAPE"]
+    assert L.la_set_tuning(b"tc_state_threads", 700) == E["LA_E_SHAPE"]
+    assert L.la_set_tuning(b"no_such_knob", 1) == E["LA_E_UNSUPPORTED"]
+    assert L.la_set_tuning(None, 1) == E["LA_E_NULLPTR"]
+    with la.tuning(apply_wgs=12, state_fused=0):
+        pass
+    with pytest.raises(la.LinAttnError):
+        la.set_tuning("apply_wgs", 0)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

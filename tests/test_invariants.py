@@ -48,7 +48,7 @@ def test_determinism_bidirectional(la):
 
 
 @pytest.mark.parametrize("d", [32, 64, 112, 128])
-def test_fused_combine_matches_separate_launch(la, d, monkeypatch):
+def test_fused_combine_matches_separate_launch(la, d):
     """The bf16 state kernel's in-kernel stage 2 (last workgroup of a head sums
     the partials) and the separate combine launch give bitwise equal S and z,
     also with a carry (block-causal), over repeated calls on one workspace."""
@@ -57,46 +57,53 @@ def test_fused_combine_matches_separate_launch(la, d, monkeypatch):
     grid = (6, 23, 40)
     qb, kb, vb = (t[:, :, 1000:2000].contiguous() for t in (tq, tk, tv))
     res = {}
-    for fused in ("0", "1"):
-        monkeypatch.setenv("LA_STATE_FUSED", fused)
+    for fused in (0, 1):
         runs = []
-        for _ in range(3):
-            S, z = la.state_reduce(tk, tv, grid)
-            Sc = S.clone() * 0.5
-            zc = z.clone() * 0.5
-            la.block_causal_step(qb, kb, vb, Sc, zc, 5000, grid, 1000, 1, commit=True)
-            runs.append((S, z, Sc, zc))
-        torch.cuda.synchronize()
+        with la.tuning(state_fused=fused):
+            for _ in range(3):
+                S, z = la.state_reduce(tk, tv, grid)
+                Sc = S.clone() * 0.5
+                zc = z.clone() * 0.5
+                la.block_causal_step(qb, kb, vb, Sc, zc, 5000, grid, 1000, 1, commit=True)
+                runs.append((S, z, Sc, zc))
+            torch.cuda.synchronize()
         for r in runs[1:]:
             assert all(torch.equal(x, y) for x, y in zip(r, runs[0])), fused
         res[fused] = runs[0]
     say(f"  d={d}: fused and separate stage 2 bitwise equal")
-    assert all(torch.equal(x, y) for x, y in zip(res["0"], res["1"]))
+    assert all(torch.equal(x, y) for x, y in zip(res[0], res[1]))
+
+
+APPLY_SPLITS = [dict(apply_ilv=0), dict(), dict(apply_heads=1), dict(apply_heads=2),
+                dict(apply_heads=3), dict(apply_heads=4), dict(apply_wgs=7)]
 
 
 @pytest.mark.parametrize("d", [32, 64, 112, 128])
-@pytest.mark.parametrize("B,H,N", [(2, 6, 4999), (1, 1, 2077)])
-def test_interleaved_apply_matches_contiguous(la, d, B, H, N, monkeypatch):
-    """The bf16 apply with the head's workgroups on interleaved units of the
-    whole head (the default) and with one contiguous chunk per workgroup give
-    bitwise equal outputs: with and without RoPE, and for a block at a global
-    offset (block-causal mode), on a ragged token count."""
+@pytest.mark.parametrize("B,H,N", [(2, 6, 4999), (1, 1, 2077), (3, 4, 700)])
+def test_apply_work_splits_are_bitwise_equal(la, d, B, H, N):
+    """The bf16 apply gives bitwise equal outputs however its work is split:
+    one contiguous chunk per workgroup, or interleaved units of the whole head
+    with 1, 2, 3 or 4 heads per workgroup (when B*H allows), or few
+    workgroups; with and without RoPE, and for a block at a global offset
+    (block-causal mode), on ragged token counts."""
     import torch
     _, (tq, tk, tv) = _inputs(B, H, N, d, "bf16", 23)
     grid = (6, 23, 40)
     S, z = la.state_reduce(tk, tv, grid)
-    qb, kb, vb = (t[:, :, 1000:2000].contiguous() for t in (tq, tk, tv))
-    res = {}
-    for ilv in ("0", "1"):
-        monkeypatch.setenv("LA_APPLY_ILV", ilv)
-        o_rope = la.apply(tq, S, z, grid, 1e-6)
-        o_plain = la.apply(tq, S, z, None, 1e-6)
-        Sc, zc = S.clone() * 0.5, z.clone() * 0.5
-        ob = la.block_causal_step(qb, kb, vb, Sc, zc, N, grid, 1000, 1, commit=False)
-        torch.cuda.synchronize()
-        res[ilv] = (o_rope, o_plain, ob)
-    assert all(torch.equal(x, y) for x, y in zip(res["0"], res["1"]))
-    say(f"  d={d} B={B} H={H} N={N}: interleaved and contiguous apply bitwise equal")
+    L = N // 3  # block 1 of three: tokens [L, 2L)
+    qb, kb, vb = (t[:, :, L:2 * L].contiguous() for t in (tq, tk, tv))
+    res = []
+    for knobs in APPLY_SPLITS:
+        with la.tuning(**knobs):
+            o_rope = la.apply(tq, S, z, grid, 1e-6)
+            o_plain = la.apply(tq, S, z, None, 1e-6)
+            Sc, zc = S.clone() * 0.5, z.clone() * 0.5
+            ob = la.block_causal_step(qb, kb, vb, Sc, zc, N, grid, L, 1, commit=False)
+            torch.cuda.synchronize()
+        res.append((o_rope, o_plain, ob))
+    for knobs, r in zip(APPLY_SPLITS[1:], res[1:]):
+        assert all(torch.equal(x, y) for x, y in zip(res[0], r)), knobs
+    say(f"  d={d} B={B} H={H} N={N}: {len(APPLY_SPLITS)} apply work splits bitwise equal")
 
 
 def oracle_bf16(x):

@@ -1,10 +1,11 @@
-"""GPU parity under the library's tuning overrides.
+"""GPU parity under the library's tuning knobs.
 
-The library reads a few environment variables at every call (workgroup
-counts, the stage-2 choice, the apply's unit interleave, token-causal's
-partial-state workgroup size, the temporal convolution's tile order).  The
-other tests run the defaults; here every non-default path is run on small
-ragged shapes and checked against the fp64 oracle with the same tolerances.
+The library has a few tuning knobs, set only through la_set_tuning
+(workgroup counts, the stage-2 choice, the apply's unit interleave and heads
+per workgroup, token-causal's partial-state workgroup size, the temporal
+convolution's tile order).  The other tests run the defaults; here every
+non-default path is run on small ragged shapes and checked against the fp64
+oracle with the same tolerances.
 """
 import numpy as np
 import pytest
@@ -26,56 +27,57 @@ def la():
 # B, H, N (ragged: not a multiple of any tile), d, grid, eps
 BIDIR = [(2, 3, 2500, 64, (4, 23, 40), 1e-6), (1, 2, 1900, 112, (3, 23, 40), 1e-6)]
 BIDIR_OVERRIDES = [
-    ("LA_STATE_WGS", "6"),       # one workgroup per head
-    ("LA_STATE_WGS", "64"),
-    ("LA_STATE_WGS", "5000"),    # as many partials as whole tiles allow (and at most 64)
-    ("LA_APPLY_WGS", "6"),
-    ("LA_APPLY_WGS", "5000"),
-    ("LA_STATE_FUSED", "0"),     # separate combine launch
-    ("LA_STATE_FUSED", "1"),     # in-kernel stage 2 at any partial size
-    ("LA_APPLY_ILV", "0"),       # contiguous apply chunks
+    ("state_wgs", 6),        # one workgroup per head
+    ("state_wgs", 64),
+    ("state_wgs", 5000),     # as many partials as whole tiles allow (and at most 64)
+    ("apply_wgs", 6),
+    ("apply_wgs", 5000),
+    ("state_fused", 0),      # separate combine launch
+    ("state_fused", 1),      # in-kernel stage 2 at any partial size
+    ("apply_ilv", 0),        # contiguous apply chunks
+    ("apply_heads", 1),      # one head per apply workgroup
+    ("apply_heads", 3),      # three heads per apply workgroup (B*H = 6)
+    ("apply_heads", 2),
 ]
 
 
 @pytest.mark.parametrize("case", BIDIR, ids=[f"d{c[3]}" for c in BIDIR])
 @pytest.mark.parametrize("var,val", BIDIR_OVERRIDES, ids=[f"{v}={x}" for v, x in BIDIR_OVERRIDES])
-def test_bidirectional_under_override(la, case, var, val, monkeypatch):
+def test_bidirectional_under_override(la, case, var, val):
     import torch
     B, H, N, d, grid, eps = case
-    monkeypatch.setenv(var, val)
     say(f"[override] {var}={val} B={B} H={H} N={N} d={d}")
     q, k, v = make_qkv(B, H, N, d, "bf16", seed=7100 + d)
-    out = la.bidirectional(upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, eps)
-    torch.cuda.synchronize()
+    with la.tuning(**{var: val}):
+        out = la.bidirectional(upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, eps)
+        torch.cuda.synchronize()
     assert_close(host(out), oracle.bidirectional(q, k, v, grid, eps), "bf16", f"{var}={val} d={d}")
 
 
 TC_OVERRIDES = [
-    ("LA_CAUSAL_WGS", "8"),          # two chunks per head
-    ("LA_CAUSAL_WGS", "4096"),       # one 128-token chunk per workgroup
-    ("LA_TC_STATE_THREADS", "1024"),  # partial states in 1024-thread workgroups
+    ("causal_wgs", 8),            # two chunks per head
+    ("causal_wgs", 4096),         # one 128-token chunk per workgroup
+    ("tc_state_threads", 1024),   # partial states in 1024-thread workgroups
 ]
 
 
 @pytest.mark.parametrize("var,val", TC_OVERRIDES, ids=[f"{v}={x}" for v, x in TC_OVERRIDES])
-def test_token_causal_under_override(la, var, val, monkeypatch):
+def test_token_causal_under_override(la, var, val):
     import torch
     B, H, N, d, grid, eps = 1, 3, 2600, 64, (5, 23, 40), 1e-6
-    monkeypatch.setenv(var, val)
     say(f"[override] token-causal {var}={val}")
     q, k, v = make_qkv(B, H, N, d, "bf16", seed=7200)
-    out = la.token_causal(upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, eps)
-    torch.cuda.synchronize()
+    with la.tuning(**{var: val}):
+        out = la.token_causal(upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, eps)
+        torch.cuda.synchronize()
     ref, _, _ = oracle.token_causal(q, k, v, grid, eps)
     assert_close(host(out), ref, "bf16", f"token-causal {var}={val}")
 
 
-@pytest.mark.parametrize("gm,gn", [("1", "1"), ("3", "5"), ("16", "2")])
-def test_temporal_conv_under_tile_order(la, gm, gn, monkeypatch):
+@pytest.mark.parametrize("gm,gn", [(1, 1), (3, 5), (16, 2)])
+def test_temporal_conv_under_tile_order(la, gm, gn):
     """Any tile-order group is a permutation of the tiles: same output."""
     import torch
-    monkeypatch.setenv("LA_TCONV_GM", gm)
-    monkeypatch.setenv("LA_TCONV_GN", gn)
     say(f"[override] temporal conv tile order {gm} x {gn}")
     X, W, cache, bias = make_tconv(1, 9, 90, 384, 31)   # 2 frame groups x 3 position tiles x 3 channel tiles
     dev = "cuda:0"
@@ -83,8 +85,9 @@ def test_temporal_conv_under_tile_order(la, gm, gn, monkeypatch):
     tW = torch.from_numpy(W).to(dev).to(torch.bfloat16)
     tc = torch.from_numpy(cache).to(dev).to(torch.bfloat16)
     tb = torch.from_numpy(np.ascontiguousarray(bias, dtype=np.float32)).to(dev)
-    out = la.temporal_conv_step(tX, tW, tc, tb, commit=False)
-    torch.cuda.synchronize()
+    with la.tuning(tconv_gm=gm, tconv_gn=gn):
+        out = la.temporal_conv_step(tX, tW, tc, tb, commit=False)
+        torch.cuda.synchronize()
     ref, _ = oracle.temporal_conv(X, W, cache, bias)
     got = host(out).astype(np.float64)
     scale = float(np.sqrt(np.mean(ref * ref)))

@@ -211,6 +211,43 @@ def test_cross_attention(la, case):
         assert_close(host(out), ref, dt, f"cross {case}")
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 112])
+def test_zero_denominator_rows(la, dt, d):
+    """eps = 0 with a live query whose denominator is 0: the IEEE quotient.
+
+    Cross-attention over no keys gives NaN rows for live queries and exact
+    zeros for dead ones; a RoPE pair that turns keys living only on the
+    partner channel of the query's channel gives +-inf (the oracle's
+    definition, pinned on the CPU)."""
+    import torch
+    rng = np.random.default_rng(4100 + d)
+    q = rng.standard_normal((1, 2, 40, d)).astype(np.float32)
+    q[0, 0, 5] = -np.abs(q[0, 0, 5])  # a dead row
+    if dt == "bf16":
+        from linear_attention_video_02_amd.inputs import round_to_bf16
+        q = round_to_bf16(q)
+    k = np.zeros((1, 2, 0, d), np.float32)
+    out = host(la.cross_attention(upload(q, dt), upload(k, dt), upload(k, dt), 0.0))
+    torch.cuda.synchronize()
+    ref = oracle.cross_attention(q, k, k, 0.0)
+    assert np.array_equal(np.isnan(out), np.isnan(ref)) and np.isnan(ref).sum() == 79 * d
+    assert np.array_equal(out[~np.isnan(ref)], ref[~np.isnan(ref)])
+    # pair p = d/2 - floor(d/6) is the first w pair (angle = w); query on its
+    # even channel, keys on its odd channel, V = 1, a 1 x 2 x 2 grid
+    c = 2 * (d // 2 - d // 6)
+    Q = np.zeros((1, 1, 4, d), np.float32)
+    Q[..., c] = 1.0
+    K = np.zeros((1, 1, 4, d), np.float32)
+    K[..., c + 1] = 1.0
+    V = np.ones((1, 1, 4, d), np.float32)
+    out = host(la.bidirectional(upload(Q, dt), upload(K, dt), upload(V, dt), (1, 2, 2), 0.0))
+    torch.cuda.synchronize()
+    ref = oracle.bidirectional(Q, K, V, (1, 2, 2), 0.0)
+    assert np.isinf(ref).all()
+    assert np.array_equal(out, ref), (out[0, 0, :, :4], ref[0, 0, :, :4])
+
+
 def test_cross720p(la):
     """The cross-attention workload at full size: 19320 video tokens over 300 text tokens."""
     import torch
