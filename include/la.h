@@ -37,14 +37,17 @@
  *    into t, h, w ranges of d/2 - 2*floor(d/6), floor(d/6), floor(d/6) pairs;
  *    pair k of an axis with P_a pairs turns by pos_a * 10000^(-k/P_a).
  *  - ws is a device workspace of at least la_workspace_bytes(B, H, N, d)
- *    bytes: per-workgroup partial states and one completion counter per
- *    (batch, head).  Zero-fill it ONCE before its first use (e.g. right after
- *    allocating it); every call that completes leaves the counters at zero
- *    again, so no later call needs a fill.  A workspace with non-zero
- *    counters gives wrong S/z (not a fault).  One workspace must not be used
- *    by two calls that may overlap in time (two streams): they would race on
- *    it.
- *  - All pointers must be 16-byte aligned.  O must not overlap Q, K, V, S or z.
+ *    bytes (la_workspace_bytes_grid() for a given grid): per-head counters,
+ *    the per-workgroup partial states of the state pass and, in block mode,
+ *    the block's sums.  Zero-fill it ONCE before its first use (e.g. right
+ *    after allocating it).  The counters carry the epoch of the call that
+ *    last used them (an increasing per-process number), so no call needs to
+ *    reset them and a call that never completed leaves nothing a later call
+ *    misreads.  One workspace must not be used by two calls that may overlap
+ *    in time (two streams): they would race on it.  Calls check ws_bytes
+ *    against their own plan and return LA_E_WORKSPACE if it is too small.
+ *  - All pointers must be 16-byte aligned.  O must not overlap Q, K, V, S or
+ *    z, and ws must not overlap any other buffer of the call (LA_E_ALIAS).
  *  - stream is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues kernels: it never allocates, never synchronises, and returns as
  *    soon as the launches are queued.
@@ -81,9 +84,14 @@ enum {
     LA_E_ALIAS = -7        /* O overlaps an input */
 };
 
-/* Upper bound on the workspace any call below needs for these sizes
- * (N = tokens of the whole sequence).  Returns 0 for invalid sizes. */
+/* Workspace bytes that every call below needs for these sizes, N = tokens
+ * of the whole sequence (largest partial count any of their plans chooses
+ * in either dtype, with the tuning knobs as they are set now).  Calls with
+ * RoPE on a grid whose table forces smaller chunks -- long sequences on
+ * grid planes of a few positions -- can need more: la_workspace_bytes_grid
+ * covers those.  Returns 0 for invalid sizes. */
 LA_API size_t la_workspace_bytes(int B, int H, int N, int d);
+LA_API size_t la_workspace_bytes_grid(int B, int H, int N, int d, int gt, int gh, int gw);
 
 /* State pass (the two sums of the linear-attention equation, Eq. 2 form):
  *   S[b,h] = sum_{n<N} RoPE(relu(K[b,h,n]))^T V[b,h,n],  z[b,h] = sum_n relu(K[b,h,n]).
@@ -184,9 +192,10 @@ LA_API int la_stream_copy(const void* src, void* dst, size_t bytes, void* stream
  *   "state_wgs", "apply_wgs", "causal_wgs"  target workgroup counts (>= 1)
  *   "state_fused"      0 / 1: separate / in-kernel stage 2 of the state pass
  *   "apply_ilv"        0: one contiguous chunk per apply workgroup
- *   "apply_heads"      1..8: heads per apply workgroup (if they fit)
+ *   "apply_heads"      1..8: heads per apply slot (if they divide B*H and fit)
  *   "tc_state_threads" 512 / 1024: token-causal partial-state workgroups
  *   "tconv_gm", "tconv_gn"  temporal-convolution tile-order group (1..64)
+ *   "apply_spread"     0: a head's apply workgroups on as few XCDs as possible
  * Returns LA_OK, LA_E_NULLPTR, LA_E_UNSUPPORTED (unknown name) or
  * LA_E_SHAPE (value out of range).  Not thread-safe: set knobs while no
  * other thread calls the library.  Results are correct under every value. */

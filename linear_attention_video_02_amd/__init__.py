@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         common = [ci] * 8 + [cf, ci]  # B H N d gt gh gw block_tokens, eps, dtype
         L.la_workspace_bytes.argtypes = [ci, ci, ci, ci]
         L.la_workspace_bytes.restype = cs
+        L.la_workspace_bytes_grid.argtypes = [ci] * 7
+        L.la_workspace_bytes_grid.restype = cs
         L.la_state_reduce.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [vp]
         L.la_state_reduce.restype = ci
         L.la_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [vp]
@@ -81,8 +83,10 @@ def strerror(status: int) -> str:
     return lib().la_strerror(int(status)).decode()
 
 
-def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    return int(lib().la_workspace_bytes(B, H, N, d))
+def workspace_bytes(B: int, H: int, N: int, d: int, grid=None) -> int:
+    if grid is None:
+        return int(lib().la_workspace_bytes(B, H, N, d))
+    return int(lib().la_workspace_bytes_grid(B, H, N, d, *_grid(grid)))
 
 
 def set_tuning(name: str, value: int) -> None:
@@ -190,7 +194,7 @@ def _check_state(S, z, B, H, d, device, what):
 _ws_cache: dict = {}
 
 
-def workspace(B: int, H: int, N: int, d: int, device, stream=None):
+def workspace(B: int, H: int, N: int, d: int, device, stream=None, grid=None):
     """A zero-filled workspace, cached per (device, stream, size).
 
     The library's calls keep per-head counters and partial states in their
@@ -199,7 +203,7 @@ def workspace(B: int, H: int, N: int, d: int, device, stream=None):
     stream).
     """
     torch = _torch()
-    nbytes = workspace_bytes(B, H, N, d)
+    nbytes = workspace_bytes(B, H, N, d, grid)
     if nbytes == 0:
         raise ValueError("invalid sizes for a workspace")
     dev = torch.device(device)
@@ -234,7 +238,7 @@ def state_reduce(k, v, grid=None, S=None, z=None, ws=None):
     _check_state(S, z, B, H, d, k.device, "state_reduce")
     _check_qkv(k, v)
     if ws is None:
-        ws = workspace(B, H, N, d, k.device)
+        ws = workspace(B, H, N, d, k.device, grid=grid)
     gt, gh, gw = _grid(grid)
     rc = lib().la_state_reduce(None, _ptr(k), _ptr(v), None, _ptr(S), _ptr(z), _ptr(ws),
                                ws.numel(), B, H, N, d, gt, gh, gw, 0, 0.0,
@@ -310,7 +314,7 @@ def block_causal_step(q, k, v, S_carry, z_carry, N, grid, block_tokens, block_id
         out = torch.empty_like(q)
     _check_qkv(q, out)
     if ws is None:
-        ws = workspace(B, H, N, d, q.device)
+        ws = workspace(B, H, N, d, q.device, grid=grid)
     gt, gh, gw = _grid(grid)
     rc = lib().la_block_causal_step(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_carry),
                                     _ptr(z_carry), _ptr(ws), ws.numel(), B, H, N, d,
@@ -342,7 +346,7 @@ def token_causal(q, k, v, grid=None, eps=1e-6, S_carry=None, z_carry=None, n_off
         out = torch.empty_like(q)
     _check_qkv(q, out)
     if ws is None:
-        ws = workspace(B, H, max(N, 1), d, q.device)
+        ws = workspace(B, H, max(N, 1), d, q.device, grid=grid)
     gt, gh, gw = _grid(grid)
     rc = lib().la_token_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S_carry), _ptr(z_carry),
                                _ptr(ws), ws.numel(), B, H, N, d, gt, gh, gw, int(n_offset), float(eps),

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <atomic>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -38,7 +40,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // la_set_tuning().  Nothing here reads the process environment.
 enum Knob {
     K_STATE_WGS, K_APPLY_WGS, K_CAUSAL_WGS, K_STATE_FUSED, K_APPLY_ILV, K_APPLY_HEADS,
-    K_TC_STATE_THREADS, K_TCONV_GM, K_TCONV_GN, K_COUNT
+    K_TC_STATE_THREADS, K_TCONV_GM, K_TCONV_GN, K_APPLY_SPREAD, K_COUNT
 };
 struct KnobInfo {
     const char* name;
@@ -48,22 +50,37 @@ const KnobInfo kKnobs[K_COUNT] = {
     {"state_wgs", 1, 1 << 20},  {"apply_wgs", 1, 1 << 20},  {"causal_wgs", 1, 1 << 20},
     {"state_fused", 0, 1},      {"apply_ilv", 0, 1},        {"apply_heads", 1, 8},
     {"tc_state_threads", 512, 1024}, {"tconv_gm", 1, 64},   {"tconv_gn", 1, 64},
+    {"apply_spread", 0, 1},
 };
-int g_knob[K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1};
+int g_knob[K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 
 int knob(Knob k, int dflt) { return g_knob[k] >= 0 ? g_knob[k] : dflt; }
 
+// Workspace: per-head stage-2 counters (64-bit, epoch-tagged), the partial
+// states [BH][P][d*d + d] of the state pass, then the block-mode sums
+// S_b/z_b [BH][d*d + d].  P is the partial count of the call's plan.
 struct WsLayout {
     size_t ticket, partial, state, total;
 };
 
-WsLayout ws_layout(int BH, int d) {
+WsLayout ws_layout(int BH, int d, int P) {
     WsLayout L;
     L.ticket = 0;
-    L.partial = align_up((size_t)BH * 4, 256);
-    L.state = L.partial + align_up((size_t)BH * kMaxPartials * (d * d + d) * 4, 256);
+    L.partial = align_up((size_t)BH * 8, 256);
+    L.state = L.partial + align_up((size_t)BH * (size_t)P * (d * d + d) * 4, 256);
     L.total = L.state + align_up((size_t)BH * (d * d + d) * 4, 256);
     return L;
+}
+
+// Epoch of a call's counters: increases from call to call across the process
+// (never 0, the value of a zero-filled workspace), so a counter a call finds
+// from an earlier call -- even one that never completed -- restarts at zero.
+std::atomic<unsigned> g_epoch{0};
+
+unsigned next_epoch() {
+    unsigned e = ++g_epoch;
+    while (e == 0) e = ++g_epoch;
+    return e;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -146,15 +163,17 @@ int state_fixed_lds(int d, int dtype) {
     }
 }
 
-// LDS of the bf16 apply: fixed part, and per head it holds (S^T copy + z)
+// LDS of the bf16 apply: fixed part (staging tiles) and the operand buffer
+// each head of a slot takes (the RoPE table comes on top), heads per slot at
+// most, and the unit of work
 void apply_bf16_lds(int d, int* fixed, int* perhead, int* maxph, int* unit) {
-#define LA_CFG(D)                           \
-    if (d == D) {                           \
-        *fixed = ApplyBf16Cfg<D>::FIXED;    \
+#define LA_CFG(D)                            \
+    if (d == D) {                            \
+        *fixed = ApplyBf16Cfg<D>::FIXED;     \
         *perhead = ApplyBf16Cfg<D>::PERHEAD; \
-        *maxph = ApplyBf16Cfg<D>::MAXPH;    \
-        *unit = ApplyBf16Cfg<D>::UNIT;      \
-        return;                             \
+        *maxph = ApplyBf16Cfg<D>::MAXPH;     \
+        *unit = ApplyBf16Cfg<D>::UNIT;       \
+        return;                              \
     }
     LA_CFG(32)
     LA_CFG(64)
@@ -233,9 +252,14 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0
 //  - otherwise (fp32, a table too large for LDS, or apply_ilv = 0): one
 //    contiguous chunk per workgroup, P chunks per head.
 struct ApplyPlan {
-    int ilv, P, nph, hs, chunk, grid;
+    int ilv, P, nph, hs, spread, chunk, grid;
     size_t lds;
 };
+
+// Heads per bf16 apply workgroup unless the apply_heads knob says otherwise:
+// at d <= 64 two halve the per-workgroup setup against one, more cost S
+// registers and setup latency than they save; past 64 channels one.
+int default_apply_heads(int d) { return d <= 64 ? 2 : 1; }
 
 int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
     const int target = knob(K_APPLY_WGS, dtype == LA_BF16 ? 256 : 1024);
@@ -249,7 +273,8 @@ int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
         const long long want = (long long)BH * pmax < target ? (long long)BH * pmax : target;
         const size_t table = table_entries(g, ntok) * 8;
         const int forced = knob(K_APPLY_HEADS, 0);
-        for (int nph = forced > 0 ? forced : maxph; nph >= 1; --nph) {
+        const int first = forced > 0 ? forced : (maxph < default_apply_heads(d) ? maxph : default_apply_heads(d));
+        for (int nph = first; nph >= 1; --nph) {
             if (nph > maxph || BH % nph != 0) {
                 if (forced > 0) break;
                 continue;
@@ -264,13 +289,17 @@ int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
                 if (forced > 0) break;
                 continue;
             }
-            // buffer offsets of units past a head's end stay below 2^32
+            // buffer offsets of units past a head's end stay below 2^32, and
+            // unit numbers fit the 20 bits of a mailbox word
             if (((size_t)ntok + (size_t)(P + 1) * unit) * d * 2 >= (1ull << 32)) break;
+            if (U >= (1 << 20)) break;
             if ((long long)hs * P >= (1ll << 31)) break;
             out->ilv = 1;
             out->P = P;
             out->nph = nph;
             out->hs = hs;
+            // a slot's workgroups on all 8 XCDs (workgroup i runs on XCD i % 8)
+            out->spread = P % 8 == 0 && knob(K_APPLY_SPREAD, 1) != 0;
             out->chunk = ntok;
             out->grid = hs * P;
             out->lds = lds;
@@ -288,12 +317,15 @@ int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
         const int Peff = ntok > 0 ? (ntok + chunk - 1) / chunk : 1;
         const size_t base = dtype == LA_BF16 ? (size_t)fixed + perhead : (size_t)apply_f32_lds(d);
         const size_t lds = base + table_entries(g, chunk) * 8;
-        if (lds <= kLdsLimit) {
+        // a chunk's byte range and unit numbers fit 32-bit offsets and 20-bit words
+        const bool small = ((size_t)chunk + 2 * (size_t)tile) * d * 4 < (1ull << 32) && chunk / unit < (1 << 20);
+        if (lds <= kLdsLimit && small) {
             if ((long long)Peff * BH >= (1ll << 31)) return LA_E_UNSUPPORTED;
             out->ilv = 0;
             out->P = Peff;
             out->nph = 1;
             out->hs = BH;
+            out->spread = 0;
             out->chunk = chunk;
             out->grid = Peff * BH;
             out->lds = lds;
@@ -353,10 +385,19 @@ KernelFn<StateArgs> state_kernel(int d, int dtype, bool rope) {
     return nullptr;
 }
 
-KernelFn<ApplyArgs> apply_kernel(int d, int dtype, bool rope) {
+// bf16: the instance with the fewest S register slots that holds nph heads
+template <int D, bool ROPE>
+KernelFn<ApplyArgs> apply_bf16_kernel(int nph) {
+    constexpr int M = ApplyBf16Cfg<D>::MAXPH;
+    if (nph <= 1) return la_apply_bf16_kernel<D, ROPE, 1>;
+    if (nph <= 2 || M <= 2) return la_apply_bf16_kernel<D, ROPE, (M < 2 ? M : 2)>;
+    return la_apply_bf16_kernel<D, ROPE, M>;
+}
+
+KernelFn<ApplyArgs> apply_kernel(int d, int dtype, bool rope, int nph) {
 #define LA_PICK(D)                                                                              \
     if (d == D) {                                                                               \
-        if (dtype == LA_BF16) return rope ? la_apply_bf16_kernel<D, true> : la_apply_bf16_kernel<D, false>; \
+        if (dtype == LA_BF16) return rope ? apply_bf16_kernel<D, true>(nph) : apply_bf16_kernel<D, false>(nph); \
         return rope ? la_apply_f32_kernel<D, true> : la_apply_f32_kernel<D, false>;             \
     }
     LA_PICK(32)
@@ -375,7 +416,7 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     Plan pl;
     int rc = plan_state(g, d, dtype, &pl);
     if (rc != LA_OK) return rc;
-    const WsLayout L = ws_layout(g.BH, d);
+    const WsLayout L = ws_layout(g.BH, d, pl.P);
     CombineArgs c;
     c.partial = (float*)((char*)ws + L.partial);
     c.S_out = S_out;
@@ -401,7 +442,8 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     a.chunk = pl.chunk;
     a.P = pl.P;
     a.g = g;
-    a.ticket = fused ? (unsigned*)((char*)ws + L.ticket) : nullptr;
+    a.ticket = fused ? (unsigned long long*)((char*)ws + L.ticket) : nullptr;
+    a.epoch = next_epoch();
     a.cmb = c;
     const int threads = dtype != LA_BF16 ? 256
                         : d == 32        ? StateBf16Cfg<32>::THREADS
@@ -432,13 +474,14 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
     a.ilv = pl.ilv;
     a.nph = pl.nph;
     a.hs = pl.hs;
+    a.spread = pl.spread;
     a.g = g;
     const int threads = dtype != LA_BF16 ? 256
                         : d == 32        ? ApplyBf16Cfg<32>::THREADS
                         : d == 64        ? ApplyBf16Cfg<64>::THREADS
                         : d == 112       ? ApplyBf16Cfg<112>::THREADS
                                          : ApplyBf16Cfg<128>::THREADS;
-    return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope), dim3(pl.grid), pl.lds, st, a, threads);
+    return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope, pl.nph), dim3(pl.grid), pl.lds, st, a, threads);
 }
 
 // Token-causal pass: about causal_wgs workgroups (default two 256-thread
@@ -482,7 +525,7 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     const bool half = knob(K_TC_STATE_THREADS, 512) == 512;
     rc = plan_state(g, d, LA_BF16, &ps, pc.chunk, half ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
     if (rc != LA_OK) return rc;
-    const WsLayout L = ws_layout(g.BH, d);
+    const WsLayout L = ws_layout(g.BH, d, ps.P);
     float* partial = (float*)((char*)ws + L.partial);
     // 1. one partial state per chunk
     StateArgs sa;
@@ -526,13 +569,16 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
 size_t elem_bytes(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
 
 // Plans depend only on sizes, so a plan failure is reported before any launch.
+// *partials: the state plan's partial count (0 without a state pass).
 int precheck_plans(int B, int H, int ntok, int n_offset, int d, int gt, int gh, int gw, int dtype,
-                   bool state, bool apply) {
+                   bool state, bool apply, int* partials = nullptr) {
     const LaGeom g = make_geom(B, H, ntok, n_offset, d, gt, gh, gw);
     Plan pl;
+    if (partials) *partials = 0;
     if (state) {
         int rc = plan_state(g, d, dtype, &pl);
         if (rc != LA_OK) return rc;
+        if (partials) *partials = pl.P;
     }
     if (apply && ntok > 0) {
         ApplyPlan pa;
@@ -542,13 +588,38 @@ int precheck_plans(int B, int H, int ntok, int n_offset, int d, int gt, int gh, 
     return LA_OK;
 }
 
+// Largest partial count any call of these sizes plans (state pass in either
+// dtype, token-causal pass): plans only grow with the token count, so this
+// covers every block of a block-causal sequence of N tokens too.
+int max_partials(int B, int H, int N, int d, int gt, int gh, int gw) {
+    int P = 1;
+    for (int dtype : {LA_BF16, LA_FP32}) {
+        const LaGeom g = make_geom(B, H, N, 0, d, gt, gh, gw);
+        Plan pl;
+        if (plan_state(g, d, dtype, &pl) == LA_OK && pl.P > P) P = pl.P;
+    }
+    {
+        const LaGeom g = make_geom(B, H, N > 0 ? N : 1, 0, d, gt, gh, gw);
+        Plan pc;
+        if (d == 64 && plan_causal(g, &pc) == LA_OK && pc.P > P) P = pc.P;
+    }
+    return P;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t la_workspace_bytes(int B, int H, int N, int d) {
     if (check_common(B, H, N, d, 0, 0, 0, 0.0f, LA_BF16) != LA_OK) return 0;
-    return ws_layout(B * H, d).total;
+    return ws_layout(B * H, d, max_partials(B, H, N, d, 0, 0, 0)).total;
+}
+
+size_t la_workspace_bytes_grid(int B, int H, int N, int d, int gt, int gh, int gw) {
+    if (check_common(B, H, N, d, gt, gh, gw, 0.0f, LA_BF16) != LA_OK) return 0;
+    const int P0 = max_partials(B, H, N, d, 0, 0, 0);
+    const int P1 = max_partials(B, H, N, d, gt, gh, gw);
+    return ws_layout(B * H, d, P0 > P1 ? P0 : P1).total;
 }
 
 int la_state_reduce(const void* Q, const void* K, const void* V, void* O, float* S, float* z, void* ws,
@@ -561,14 +632,16 @@ int la_state_reduce(const void* Q, const void* K, const void* V, void* O, float*
     if (rc != LA_OK) return rc;
     if (!S || !z || !ws || (N > 0 && (!K || !V))) return LA_E_NULLPTR;
     if (!aligned16(K) || !aligned16(V) || !aligned16(S) || !aligned16(z) || !aligned16(ws)) return LA_E_ALIGN;
-    if (ws_bytes < ws_layout(B * H, d).total) return LA_E_WORKSPACE;
+    int partials = 0;
+    rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, true, false, &partials);
+    if (rc != LA_OK) return rc;
+    if (ws_bytes < ws_layout(B * H, d, partials).total) return LA_E_WORKSPACE;
     const size_t nS = (size_t)B * H * d * d * 4, nz = (size_t)B * H * d * 4;
     const size_t nkv = (size_t)B * H * N * d * elem_bytes(dtype);
     if (overlaps(S, nS, K, nkv) || overlaps(S, nS, V, nkv) || overlaps(z, nz, K, nkv) ||
-        overlaps(z, nz, V, nkv) || overlaps(S, nS, z, nz))
+        overlaps(z, nz, V, nkv) || overlaps(S, nS, z, nz) || overlaps(ws, ws_bytes, K, nkv) ||
+        overlaps(ws, ws_bytes, V, nkv) || overlaps(ws, ws_bytes, S, nS) || overlaps(ws, ws_bytes, z, nz))
         return LA_E_ALIAS;
-    rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, true, false);
-    if (rc != LA_OK) return rc;
     return run_state(K, V, S, z, nullptr, nullptr, nullptr, nullptr, ws, B, H, N, 0, d, gt, gh, gw, dtype,
                      (hipStream_t)stream);
 }
@@ -587,8 +660,8 @@ int la_apply(const void* Q, const void* K, const void* V, void* O, const float* 
     if (!Q || !O || !S || !z) return LA_E_NULLPTR;
     if (!aligned16(Q) || !aligned16(O) || !aligned16(S) || !aligned16(z)) return LA_E_ALIGN;
     const size_t nqo = (size_t)B * H * N * d * elem_bytes(dtype);
-    if (overlaps(O, nqo, Q, nqo) || overlaps(O, nqo, S, (size_t)B * H * d * d * 4) ||
-        overlaps(O, nqo, z, (size_t)B * H * d * 4))
+    const size_t nS = (size_t)B * H * d * d * 4, nz = (size_t)B * H * d * 4;
+    if (overlaps(O, nqo, Q, nqo) || overlaps(O, nqo, S, nS) || overlaps(O, nqo, z, nz))
         return LA_E_ALIAS;
     rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, false, true);
     if (rc != LA_OK) return rc;
@@ -608,17 +681,20 @@ int la_block_causal_step(const void* Q, const void* K, const void* V, void* O, f
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(S_carry) ||
         !aligned16(z_carry) || !aligned16(ws))
         return LA_E_ALIGN;
-    const WsLayout L = ws_layout(B * H, d);
+    int partials = 0;
+    rc = precheck_plans(B, H, Lb, (int)start, d, gt, gh, gw, dtype, true, true, &partials);
+    if (rc != LA_OK) return rc;
+    const WsLayout L = ws_layout(B * H, d, partials);
     if (ws_bytes < L.total) return LA_E_WORKSPACE;
     const size_t nb = (size_t)B * H * Lb * d * elem_bytes(dtype);
     const size_t nS = (size_t)B * H * d * d * 4, nz = (size_t)B * H * d * 4;
     if (overlaps(O, nb, Q, nb) || overlaps(O, nb, K, nb) || overlaps(O, nb, V, nb) ||
         overlaps(O, nb, S_carry, nS) || overlaps(O, nb, z_carry, nz) || overlaps(S_carry, nS, z_carry, nz) ||
         overlaps(S_carry, nS, K, nb) || overlaps(S_carry, nS, V, nb) || overlaps(z_carry, nz, K, nb) ||
-        overlaps(z_carry, nz, V, nb) || overlaps(ws, ws_bytes, S_carry, nS) || overlaps(ws, ws_bytes, z_carry, nz))
+        overlaps(z_carry, nz, V, nb) || overlaps(ws, ws_bytes, S_carry, nS) || overlaps(ws, ws_bytes, z_carry, nz) ||
+        overlaps(ws, ws_bytes, O, nb) || overlaps(ws, ws_bytes, Q, nb) || overlaps(ws, ws_bytes, K, nb) ||
+        overlaps(ws, ws_bytes, V, nb))
         return LA_E_ALIAS;
-    rc = precheck_plans(B, H, Lb, (int)start, d, gt, gh, gw, dtype, true, true);
-    if (rc != LA_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
     float* Sb = (float*)((char*)ws + L.state);
     float* zb = Sb + (size_t)B * H * d * d;
@@ -640,9 +716,17 @@ int la_token_causal(const void* Q, const void* K, const void* V, void* O, float*
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(ws) ||
         !aligned16(S_carry) || !aligned16(z_carry))
         return LA_E_ALIGN;
-    const WsLayout L = ws_layout(B * H, d);
-    if (ws_bytes < L.total) return LA_E_WORKSPACE;
-    if (N == 0) return LA_OK;  // no token: the carry stays as it is
+    if (N == 0) return ws_bytes < ws_layout(B * H, d, 1).total ? LA_E_WORKSPACE : LA_OK;  // the carry stays
+    Plan pc, ps;
+    {
+        const LaGeom g = make_geom(B, H, N, n_offset, d, gt, gh, gw);
+        rc = plan_causal(g, &pc);
+        if (rc != LA_OK) return rc;
+        rc = plan_state(g, d, LA_BF16, &ps, pc.chunk,
+                        knob(K_TC_STATE_THREADS, 512) == 512 ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
+        if (rc != LA_OK) return rc;
+    }
+    if (ws_bytes < ws_layout(B * H, d, ps.P).total) return LA_E_WORKSPACE;
     const size_t nb = (size_t)B * H * N * d * elem_bytes(dtype);
     const size_t nS = S_carry ? (size_t)B * H * d * d * 4 : 0, nz = z_carry ? (size_t)B * H * d * 4 : 0;
     if (overlaps(O, nb, Q, nb) || overlaps(O, nb, K, nb) || overlaps(O, nb, V, nb) ||
@@ -650,14 +734,9 @@ int la_token_causal(const void* Q, const void* K, const void* V, void* O, float*
         overlaps(S_carry, nS, K, nb) || overlaps(S_carry, nS, V, nb) || overlaps(S_carry, nS, Q, nb) ||
         overlaps(z_carry, nz, K, nb) || overlaps(z_carry, nz, V, nb) || overlaps(z_carry, nz, Q, nb) ||
         overlaps(ws, ws_bytes, S_carry, nS) || overlaps(ws, ws_bytes, z_carry, nz) ||
-        overlaps(ws, ws_bytes, O, nb))
+        overlaps(ws, ws_bytes, O, nb) || overlaps(ws, ws_bytes, Q, nb) || overlaps(ws, ws_bytes, K, nb) ||
+        overlaps(ws, ws_bytes, V, nb))
         return LA_E_ALIAS;
-    {
-        const LaGeom g = make_geom(B, H, N, n_offset, d, gt, gh, gw);
-        Plan pc;
-        rc = plan_causal(g, &pc);
-        if (rc != LA_OK) return rc;
-    }
     return run_token_causal(Q, K, V, O, S_carry, z_carry, ws, B, H, N, n_offset, d, gt, gh, gw, eps,
                             (hipStream_t)stream);
 }

@@ -20,6 +20,7 @@ struct ApplyArgs {
     int ilv;         // bf16: 1 = the head's P workgroups take interleaved units of the whole head
     int nph;         // ilv = 1: heads per workgroup, one after another (phases)
     int hs;          // ilv = 1: head slots; phase k of slot j is head k * hs + j
+    int spread;      // ilv = 1: a slot's workgroups lie on all 8 XCDs (P % 8 == 0)
     LaGeom g;
 };
 
@@ -52,11 +53,14 @@ struct ApplyArgs {
 // (phase k of head slot j is head k * hs + j).  A copy of Q to O shaped like
 // this runs at the rate of a plain copy when a handful of heads are in
 // flight, and ~10% slower when every head of the call is (one read and one
-// write window per head).  The S^T copies (fp16, scaled) and z of all the
-// workgroup's heads are prepared in LDS at the start; a wave that moves on to
-// the next head reloads its operands from there, so no wave waits for another.
-// Each wave takes UNIT-token units from the workgroup's LDS queue of the
-// current phase and keeps DEPTH units of Q in flight.
+// write window per head).  Each head of the workgroup has an LDS operand
+// buffer (S^T in fp16, scaled, and z).  Phase 0's is converted by every wave
+// before the start, while the first units of Q are in flight; wave w
+// converts phase w + 1's after its first unit (or before it would first
+// wait), so the start does not wait for every head's S.  A wave that moves on
+// to the next head reloads its operands from that head's buffer.  Each wave
+// takes UNIT-token units from the workgroup's LDS queue of the current phase
+// and keeps DEPTH units of Q in flight.
 // ---------------------------------------------------------------------------
 template <int D>
 struct ApplyBf16Cfg {
@@ -106,16 +110,98 @@ __device__ __forceinline__ int st_off(int pr, int c) {
     return pr * DP + ((c ^ (pr & (DP / 8 - 1))) << 3);
 }
 
-// Work item mapping shared with the state pass (whole heads per XCD).
-__device__ __forceinline__ void apply_item_of_block(int P, int NS, int& slot, int& p) {
-    const int T = P * NS;
+// Row of the S^T copy that holds value channel co: the MFMA output tile T
+// and row m within it (value channel 32 (T/2) + 8 (m/4) + 4 (T%2) + m%4).
+__device__ __forceinline__ int st_row(int co) {
+    const int T = 2 * (co >> 5) + ((co >> 2) & 1);
+    const int m = (((co >> 3) & 3) << 2) | (co & 3);
+    return 16 * T + m;
+}
+
+// Which slot and position the workgroup takes.  With `spread` the P
+// workgroups of a slot lie on all 8 XCDs (workgroup i runs on XCD i % 8);
+// otherwise on as few as possible (whole heads per XCD).
+__device__ __forceinline__ void apply_item_of_block(int P, int NS, int spread, int& slot, int& p) {
     const int i = blockIdx.x;
+    if (spread) {
+        const int q = i >> 3;
+        slot = q % NS;
+        p = (q / NS) * 8 + (i & 7);
+        return;
+    }
+    const int T = P * NS;
     const int k = (T % 8 == 0) ? (i % 8) * (T / 8) + i / 8 : i;
     slot = k / P;
     p = k % P;
 }
 
-template <int D, bool ROPE>
+// One wave converts a head's S (fp32 [d][d], row = key channel) and z into an
+// LDS operand buffer: fp16 S^T scaled by 2^-eS (largest |S| to [2^13, 2^14)),
+// zero above d, and z; returns eS.  Two passes over S (from L2): the largest
+// magnitude, then the conversion, in coalesced 16-byte loads.
+template <int D, int DP>
+__device__ int convert_head_wave(const float* Sh, const float* zg, uint16_t* sth, float* zsh, int lane) {
+    constexpr int F4 = D * D / 4;  // float4 pieces of S
+    float amax = 0.0f;
+#pragma unroll 1
+    for (int f0 = 0; f0 < F4; f0 += 256) {
+        f32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f = f0 + 64 * i + lane;
+            v[i] = f < F4 ? *(const f32x4*)(Sh + 4 * f) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+    }
+    amax = wave_max(amax);
+    int eS = 0;
+    if (amax > 0.0f) {
+        (void)frexpf(amax, &eS);
+        eS -= 14;
+    }
+#pragma unroll 1
+    for (int f0 = 0; f0 < F4; f0 += 256) {
+        f32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f = f0 + 64 * i + lane;
+            v[i] = f < F4 ? *(const f32x4*)(Sh + 4 * f) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int f = f0 + 64 * i + lane;
+            if (f < F4) {
+                const int k = f / (D / 4), co = 4 * (f % (D / 4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    sth[st_off<DP>(st_row(co + j), k >> 3) + (k & 7)] =
+                        __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v[i][j], -eS));
+            }
+        }
+    }
+    if constexpr (DP > D) {  // the padding rows and columns (key or value channel >= d)
+#pragma unroll 1
+        for (int e = lane; e < DP * DP - D * D; e += 64) {
+            int k, co;
+            if (e < D * (DP - D)) {
+                k = e / (DP - D);
+                co = D + e % (DP - D);
+            } else {
+                k = D + (e - D * (DP - D)) / DP;
+                co = (e - D * (DP - D)) % DP;
+            }
+            sth[st_off<DP>(st_row(co), k >> 3) + (k & 7)] = 0;
+        }
+    }
+    for (int c = lane; c < DP; c += 64) zsh[c] = c < D ? zg[c] : 0.0f;
+    return eS;
+}
+
+// NPH: register slots for S, at least the heads per workgroup (a.nph)
+template <int D, bool ROPE, int NPH>
 __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel(ApplyArgs a) {
     using C = ApplyBf16Cfg<D>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -125,16 +211,16 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     uint16_t* st16 = (uint16_t*)(smem + C::FIXED);                  // [nph][DP*DP] fp16 S^T
     float* zs = (float*)(smem + C::FIXED + nph * C::SHEAD);         // [nph][DP] z
     float2* tab = (float2*)(smem + C::FIXED + nph * C::PERHEAD);
-    __shared__ int q_next[C::MAXPH];         // next unit of each phase's queue, in tokens
-    __shared__ float smax[C::MAXPH][C::NW];  // per-wave max |S| of each head
-    __shared__ int eSs[C::MAXPH];            // per-head exponent of the S^T scale
+    __shared__ int q_next[NPH];         // next unit of each phase's queue, in tokens
+    __shared__ float smax[NPH][C::NW];  // per-wave max |S| of each head
+    __shared__ int eSs[NPH];            // per-head exponent of the S^T scale
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int BH = a.g.BH;
     int slot, p;
-    apply_item_of_block(a.P, ilv ? a.hs : BH, slot, p);
+    apply_item_of_block(a.P, ilv ? a.hs : BH, ilv ? a.spread : 0, slot, p);
     auto head_of = [&](int ph) -> int { return ilv ? ph * a.hs + slot : slot; };
     const int ntok = a.g.ntok;
     const int c0 = ilv ? 0 : p * a.chunk;
@@ -150,27 +236,26 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     };
     auto o_rsrc = [&](int head) { return make_rsrc((uint16_t*)a.O + ((size_t)head * ntok + c0) * D, chunk_bytes); };
 
-    if (threadIdx.x < C::MAXPH) q_next[threadIdx.x] = threadIdx.x == 0 ? C::NW * C::DEPTH * C::UNIT : 0;
+    if (threadIdx.x < NPH) q_next[threadIdx.x] = threadIdx.x == 0 ? C::NW * C::DEPTH * C::UNIT : 0;
 
-    // S of every head of this workgroup, fetched before the first Q loads.
-    // Loads return in order, so fetched after them the conversion below (and
-    // every wave's first MFMA) would wait until all of the first units of Q
-    // had arrived.  S comes in with coalesced 16-byte loads and goes to LDS
-    // transposed and rounded to fp16, where each lane reads its fragments.
+    // S of every head of this workgroup: phase 0's before the first Q loads,
+    // the others after them.  Loads return in order: phase 0's conversion
+    // then waits for its own S only, and the first units of Q do not queue
+    // behind every head's S.  Every register slot loads (a phase past nph
+    // reloads phase 0's head) so that the compiler counts the loads exactly.
+    // S comes in with coalesced 16-byte loads and goes to LDS transposed and
+    // rounded to fp16, where each lane reads its fragments.
     constexpr int S4 = (D * D / 4 + C::THREADS - 1) / C::THREADS;  // float4s a thread per head
-    f32x4 sraw[C::MAXPH][S4];
+    f32x4 sraw[NPH][S4];
+    auto load_s = [&](int ph) {
+        const float* Sh = a.S + (size_t)head_of(ph < nph ? ph : 0) * D * D;
 #pragma unroll
-    for (int ph = 0; ph < C::MAXPH; ++ph) {
-        const int hd = head_of(ph);
-        if (ph < nph && hd < BH) {
-            const float* Sh = a.S + (size_t)hd * D * D;
-#pragma unroll
-            for (int i = 0; i < S4; ++i) {
-                const int f = threadIdx.x + i * C::THREADS;
-                if (f < D * D / 4) sraw[ph][i] = *(const f32x4*)(Sh + 4 * f);
-            }
+        for (int i = 0; i < S4; ++i) {
+            const int f = threadIdx.x + i * C::THREADS;
+            sraw[ph][i] = *(const f32x4*)(Sh + 4 * (f < D * D / 4 ? f : 0));
         }
-    }
+    };
+    load_s(0);
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of Q's
 
     // the ring: slot s holds the unit (phase, first token) whose Q is in qr[s]
@@ -215,8 +300,13 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         const int tok = tok_of((s * C::NW + wave) * C::UNIT);
         fixed = fixed && tok < len;  // (tokens grow with s: once past the end, all later are too)
         us[s] = fixed ? make_int2(0, tok) : make_int2(-1, 0);
-        if (fixed) load_unit(qr[s], us[s]);
+        // (unconditional, a pending slot reading past the end: with every
+        // load issued the compiler can count them exactly)
+        load_unit(qr[s], fixed ? us[s] : make_int2(nph, 0));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ph = 1; ph < NPH; ++ph) load_s(ph);
 
     int t_lo = 0, nt = 1;
     PairRef pr[C::KS][4];
@@ -234,7 +324,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 
     // each head's largest |S|: per thread, per wave, then over the waves
 #pragma unroll
-    for (int ph = 0; ph < C::MAXPH; ++ph) {
+    for (int ph = 0; ph < NPH; ++ph) {
         if (ph < nph && head_of(ph) < BH) {
             float amax = 0.0f;
 #pragma unroll
@@ -253,7 +343,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     // the MFMA row order: row pr = 16 T + m holds value channel co(T, m),
     // element k is S[k][co] 2^-eS (zero past d)
 #pragma unroll
-    for (int ph = 0; ph < C::MAXPH; ++ph) {
+    for (int ph = 0; ph < NPH; ++ph) {
         const int hd = head_of(ph);
         if (ph < nph && hd < BH) {
             float hmax = 0.0f;
@@ -516,7 +606,7 @@ __global__ __launch_bounds__(256) void la_apply_f32_kernel(ApplyArgs a) {
 
     const int tid = threadIdx.x;
     int bh, p;
-    apply_item_of_block(a.P, a.g.BH, bh, p);
+    apply_item_of_block(a.P, a.g.BH, 0, bh, p);
     const int ntok = a.g.ntok;
     const int c0 = p * a.chunk;
     const int c1 = min(c0 + a.chunk, ntok);

@@ -11,13 +11,14 @@
 // for a given shape.  Stage 2 runs in one of two ways, with identical sums:
 //  - bf16 kernel, fused: the partials are written with device-scope stores
 //    and the last workgroup of a head to finish (a per-head counter in the
-//    workspace) does the sum.  No release fence: a device-scope fence per
-//    workgroup would write back a whole XCD L2 each time.  Used while a
-//    head's partials are at most 256 KB (LA_STATE_FUSED=1 forces it).
+//    workspace, tagged with the call's epoch) does the sum.  No release
+//    fence: a device-scope fence per workgroup would write back a whole XCD
+//    L2 each time.  Used while a head's partials are at most 256 KB (the
+//    tuning knob state_fused = 1 forces it).
 //  - separate launch (la_state_combine_kernel): the kernel boundary makes
 //    the partials visible, and the sum is spread over many workgroups.
 //    Used by the fp32 kernel, by the token-causal pass (its prefix kernel
-//    reads the partials), for larger partials and when LA_STATE_FUSED=0.
+//    reads the partials), for larger partials and with state_fused = 0.
 #pragma once
 
 #include "la_common.h"
@@ -43,7 +44,10 @@ struct StateArgs {
     LaGeom g;
     // Stage 2 inside the bf16 kernel (ticket != null): the last workgroup of
     // a head to finish sums that head's partials (see the kernel's end).
-    unsigned* ticket;      // [BH] counters, zero between calls
+    // Counters hold (epoch << 32) | count: each call counts from zero in its
+    // own epoch, so no call has to reset them.
+    unsigned long long* ticket;  // [BH]
+    unsigned epoch;              // this call's epoch (never 0)
     CombineArgs cmb;
 };
 
@@ -437,9 +441,15 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     lds_barrier();  // every thread's stores done; zr reads done (flag reuses zr[0])
     int* flag = (int*)smem;
-    if (tid == 0)
-        *flag = __hip_atomic_fetch_add(&a.ticket[bh], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (unsigned)(a.P - 1);
+    if (tid == 0) {
+        // the head's counter moves to this call's epoch (count 0) unless a
+        // workgroup of this call got there first; then count this partial
+        __hip_atomic_fetch_max(&a.ticket[bh], (unsigned long long)a.epoch << 32, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long old =
+            __hip_atomic_fetch_add(&a.ticket[bh], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = (unsigned)old == (unsigned)(a.P - 1);
+    }
     lds_barrier();
     if (*flag) {
         const CombineArgs& c = a.cmb;
@@ -468,8 +478,6 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
                 if (c.z_out2) *(f32x4*)(c.z_out2 + o) = s;
             }
         }
-        // back to zero for the next call (kernels of one stream do not overlap)
-        if (tid == 0) __hip_atomic_store(&a.ticket[bh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

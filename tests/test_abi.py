@@ -39,7 +39,8 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
                           "la_block_causal_step", "la_token_causal", "la_temporal_conv_step",
-                          "la_stream_copy", "la_strerror", "la_last_hip_error", "la_set_tuning"}
+                          "la_stream_copy", "la_strerror", "la_last_hip_error", "la_set_tuning",
+                          "la_workspace_bytes_grid"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -61,8 +62,15 @@ def test_workspace_bytes(L):
     a = la.workspace_bytes(2, 32, 19320, 64)
     b = la.workspace_bytes(2, 32, 19320, 128)
     assert a > 64 * 4160 * 4 and b > a
-    # independent of N (the state is O(d^2) per head)
+    # sized from the plans: the partial states of at most ~1024 workgroups (fp32
+    # plan) plus O(d^2) per head -- not 64 partials per head
+    assert a < 64 * (16 + 2) * 4160 * 4 + 64 * 1024
+    assert la.workspace_bytes(32, 32, 4096, 64) < 64 * 1024 * 1024
+    # the same for the whole sequence and for one of its blocks (constant memory)
     assert la.workspace_bytes(1, 32, 220800, 64) == la.workspace_bytes(1, 32, 22080, 64)
+    # a grid whose RoPE tables force smaller chunks can need more, never less
+    assert la.workspace_bytes(1, 2, 200000, 128, (200000, 1, 1)) >= la.workspace_bytes(1, 2, 200000, 128)
+    assert la.workspace_bytes(2, 32, 19320, 64, (21, 23, 40)) == a
     assert la.workspace_bytes(1, 1, 10, 48) == 0
     assert la.workspace_bytes(0, 1, 10, 64) == 0
     assert la.workspace_bytes(1, 1, -1, 64) == 0
@@ -86,11 +94,11 @@ def state_call(L, **kw):
 
 
 def apply_call(L, **kw):
-    a = dict(Q=p(0), O=p(1 << 30), S=p(2 << 30), z=p(3 << 30), B=1, H=2, N=256, d=64,
+    a = dict(Q=p(0), O=p(1 << 30), S=p(2 << 30), z=p(3 << 30), ws=None, ws_bytes=0, B=1, H=2, N=256, d=64,
              gt=0, gh=0, gw=0, eps=1e-6, dtype=la.LA_BF16)
     a.update(kw)
-    return L.la_apply(a["Q"], None, None, a["O"], a["S"], a["z"], None, 0, a["B"], a["H"], a["N"],
-                      a["d"], a["gt"], a["gh"], a["gw"], 0, a["eps"], a["dtype"], None)
+    return L.la_apply(a["Q"], None, None, a["O"], a["S"], a["z"], a["ws"], a["ws_bytes"], a["B"], a["H"],
+                      a["N"], a["d"], a["gt"], a["gh"], a["gw"], 0, a["eps"], a["dtype"], None)
 
 
 def step_call(L, **kw):
@@ -123,6 +131,8 @@ E = {v: k for k, v in la.STATUS.items()}
     (dict(V=p(8)), "LA_E_ALIGN"),
     (dict(ws_bytes=1000), "LA_E_WORKSPACE"),
     (dict(S=p(64)), "LA_E_ALIAS"),                 # S inside K
+    (dict(ws=p(1 << 30)), "LA_E_ALIAS"),           # workspace over V
+    (dict(ws=p((3 << 30) - 64)), "LA_E_ALIAS"),    # workspace running into z
     (dict(gt=1, gh=3000, gw=3000), "LA_E_UNSUPPORTED"),  # RoPE table cannot fit LDS
 ])
 def test_state_reduce_rejects(L, kw, want):
@@ -150,6 +160,8 @@ def test_apply_rejects(L, kw, want):
     (dict(ws_bytes=10), "LA_E_WORKSPACE"),
     (dict(O=p(1 << 30)), "LA_E_ALIAS"),           # O == K
     (dict(z=p(4 << 30)), "LA_E_ALIAS"),           # z == S
+    (dict(ws=p(3 << 30)), "LA_E_ALIAS"),          # workspace over O
+    (dict(ws=p(64)), "LA_E_ALIAS"),               # workspace over Q
     (dict(d=100), "LA_E_UNSUPPORTED"),
     (dict(Q=p(2)), "LA_E_ALIGN"),
 ])

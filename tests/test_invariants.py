@@ -75,17 +75,18 @@ def test_fused_combine_matches_separate_launch(la, d):
 
 
 APPLY_SPLITS = [dict(apply_ilv=0), dict(), dict(apply_heads=1), dict(apply_heads=2),
-                dict(apply_heads=3), dict(apply_heads=4), dict(apply_wgs=7)]
+                dict(apply_heads=3), dict(apply_heads=4), dict(apply_wgs=7),
+                dict(apply_spread=0), dict(apply_heads=6), dict(apply_wgs=24, apply_heads=2)]
 
 
 @pytest.mark.parametrize("d", [32, 64, 112, 128])
 @pytest.mark.parametrize("B,H,N", [(2, 6, 4999), (1, 1, 2077), (3, 4, 700)])
 def test_apply_work_splits_are_bitwise_equal(la, d, B, H, N):
     """The bf16 apply gives bitwise equal outputs however its work is split:
-    one contiguous chunk per workgroup, or interleaved units of the whole head
-    with 1, 2, 3 or 4 heads per workgroup (when B*H allows), or few
-    workgroups; with and without RoPE, and for a block at a global offset
-    (block-causal mode), on ragged token counts."""
+    one contiguous chunk per workgroup, or interleaved units of whole heads
+    with 1, 2, 3, 4 or 6 heads per slot (when B*H allows), few workgroups,
+    a slot's workgroups on all XCDs or on few; with and without RoPE, and for a block at a global
+    offset (block-causal mode), on ragged token counts."""
     import torch
     _, (tq, tk, tv) = _inputs(B, H, N, d, "bf16", 23)
     grid = (6, 23, 40)
@@ -287,3 +288,25 @@ def test_stream_copy_is_exact(la):
     la.stream_copy(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_stale_counters_heal(la):
+    """Counters a call finds from an earlier call that never completed (an
+    older epoch, a partial count) restart at zero: the same outputs, bitwise."""
+    import torch
+    _, (tq, tk, tv) = _inputs(2, 8, 6000, 64, "bf16", 29)
+    grid = (7, 23, 40)
+    ws = la.workspace(2, 8, 6000, 64, tq.device, grid=grid)
+    ref = la.bidirectional(tq, tk, tv, grid, ws=ws).clone()
+    S0, z0 = la.state_reduce(tk, tv, grid, ws=ws)
+    S0, z0 = S0.clone(), z0.clone()
+    torch.cuda.synchronize()
+    # epoch 1, count 3: what an interrupted first call could leave
+    stale = torch.full((2048,), (1 << 32) | 3, dtype=torch.int64, device=tq.device)
+    ws[:16384].copy_(stale.view(torch.uint8))
+    out = la.bidirectional(tq, tk, tv, grid, ws=ws)
+    ws[:16384].copy_(stale.view(torch.uint8))
+    S, z = la.state_reduce(tk, tv, grid, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.equal(S, S0) and torch.equal(z, z0)
