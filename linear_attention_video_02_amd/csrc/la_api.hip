@@ -56,17 +56,24 @@ int g_knob[K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 
 int knob(Knob k, int dflt) { return g_knob[k] >= 0 ? g_knob[k] : dflt; }
 
-// Workspace: per-head stage-2 counters (64-bit, epoch-tagged), the partial
-// states [BH][P][d*d + d] of the state pass, then the block-mode sums
+// Workspace: per-head stage-2 counters (64-bit, epoch-tagged, a fixed 32 KB
+// region), the partial states [BH][P][d*d + d] of the state pass, then the
+// block-mode sums
 // S_b/z_b [BH][d*d + d].  P is the partial count of the call's plan.
 struct WsLayout {
     size_t ticket, partial, state, total;
 };
 
+// The counters sit at the same place for every shape, ahead of everything
+// else: a workspace shared by calls of different sizes never has one call's
+// partial states land on another's counters.  The fused stage 2 (which uses
+// them) is limited to kTicketHeads (batch, head) pairs.
+constexpr int kTicketHeads = 4096;
+
 WsLayout ws_layout(int BH, int d, int P) {
     WsLayout L;
     L.ticket = 0;
-    L.partial = align_up((size_t)BH * 8, 256);
+    L.partial = (size_t)kTicketHeads * 8;
     L.state = L.partial + align_up((size_t)BH * (size_t)P * (d * d + d) * 4, 256);
     L.total = L.state + align_up((size_t)BH * (d * d + d) * 4, 256);
     return L;
@@ -434,7 +441,8 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     // The tuning knob state_fused = 0 / 1 forces one of the two.
     const size_t head_partials = (size_t)pl.P * (size_t)(d * d + d) * 4;
     const int force = knob(K_STATE_FUSED, -1);
-    const bool fused = dtype == LA_BF16 && (force >= 0 ? force != 0 : head_partials <= kFusedCombineBytes);
+    const bool fused = dtype == LA_BF16 && g.BH <= kTicketHeads &&
+                       (force >= 0 ? force != 0 : head_partials <= kFusedCombineBytes);
     StateArgs a;
     a.K = K;
     a.V = V;
@@ -606,6 +614,26 @@ int max_partials(int B, int H, int N, int d, int gt, int gh, int gw) {
     return P;
 }
 
+// Argument checks of the state pass (everything but the workspace);
+// *need = workspace bytes of the call's plan.
+int state_reduce_checks(const void* K, const void* V, const float* S, const float* z, int B, int H, int N, int d,
+                        int gt, int gh, int gw, float eps, int dtype, size_t* need) {
+    int rc = check_common(B, H, N, d, gt, gh, gw, eps, dtype);
+    if (rc != LA_OK) return rc;
+    if (!S || !z || (N > 0 && (!K || !V))) return LA_E_NULLPTR;
+    if (!aligned16(K) || !aligned16(V) || !aligned16(S) || !aligned16(z)) return LA_E_ALIGN;
+    int partials = 0;
+    rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, true, false, &partials);
+    if (rc != LA_OK) return rc;
+    *need = ws_layout(B * H, d, partials).total;
+    const size_t nS = (size_t)B * H * d * d * 4, nz = (size_t)B * H * d * 4;
+    const size_t nkv = (size_t)B * H * N * d * elem_bytes(dtype);
+    if (overlaps(S, nS, K, nkv) || overlaps(S, nS, V, nkv) || overlaps(z, nz, K, nkv) ||
+        overlaps(z, nz, V, nkv) || overlaps(S, nS, z, nz))
+        return LA_E_ALIAS;
+    return LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -628,19 +656,16 @@ int la_state_reduce(const void* Q, const void* K, const void* V, void* O, float*
     (void)Q;
     (void)O;
     (void)block_tokens;
-    int rc = check_common(B, H, N, d, gt, gh, gw, eps, dtype);
+    size_t need = 0;
+    int rc = state_reduce_checks(K, V, S, z, B, H, N, d, gt, gh, gw, eps, dtype, &need);
     if (rc != LA_OK) return rc;
-    if (!S || !z || !ws || (N > 0 && (!K || !V))) return LA_E_NULLPTR;
-    if (!aligned16(K) || !aligned16(V) || !aligned16(S) || !aligned16(z) || !aligned16(ws)) return LA_E_ALIGN;
-    int partials = 0;
-    rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, true, false, &partials);
-    if (rc != LA_OK) return rc;
-    if (ws_bytes < ws_layout(B * H, d, partials).total) return LA_E_WORKSPACE;
+    if (!ws) return LA_E_NULLPTR;
+    if (!aligned16(ws)) return LA_E_ALIGN;
+    if (ws_bytes < need) return LA_E_WORKSPACE;
     const size_t nS = (size_t)B * H * d * d * 4, nz = (size_t)B * H * d * 4;
     const size_t nkv = (size_t)B * H * N * d * elem_bytes(dtype);
-    if (overlaps(S, nS, K, nkv) || overlaps(S, nS, V, nkv) || overlaps(z, nz, K, nkv) ||
-        overlaps(z, nz, V, nkv) || overlaps(S, nS, z, nz) || overlaps(ws, ws_bytes, K, nkv) ||
-        overlaps(ws, ws_bytes, V, nkv) || overlaps(ws, ws_bytes, S, nS) || overlaps(ws, ws_bytes, z, nz))
+    if (overlaps(ws, ws_bytes, K, nkv) || overlaps(ws, ws_bytes, V, nkv) || overlaps(ws, ws_bytes, S, nS) ||
+        overlaps(ws, ws_bytes, z, nz))
         return LA_E_ALIAS;
     return run_state(K, V, S, z, nullptr, nullptr, nullptr, nullptr, ws, B, H, N, 0, d, gt, gh, gw, dtype,
                      (hipStream_t)stream);

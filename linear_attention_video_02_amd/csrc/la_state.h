@@ -11,7 +11,8 @@
 // for a given shape.  Stage 2 runs in one of two ways, with identical sums:
 //  - bf16 kernel, fused: the partials are written with device-scope stores
 //    and the last workgroup of a head to finish (a per-head counter in the
-//    workspace, tagged with the call's epoch) does the sum.  No release
+//    workspace, tagged with the call's epoch and put back to zero by the
+//    workgroup that completes the head) does the sum.  No release
 //    fence: a device-scope fence per workgroup would write back a whole XCD
 //    L2 each time.  Used while a head's partials are at most 256 KB (the
 //    tuning knob state_fused = 1 forces it).
@@ -44,8 +45,10 @@ struct StateArgs {
     LaGeom g;
     // Stage 2 inside the bf16 kernel (ticket != null): the last workgroup of
     // a head to finish sums that head's partials (see the kernel's end).
-    // Counters hold (epoch << 32) | count: each call counts from zero in its
-    // own epoch, so no call has to reset them.
+    // Counters hold (epoch << 32) | count: a call counts from zero in its own
+    // epoch, so a count left by a call that never completed is raised past.
+    // The workgroup that completes a head puts its counter back to zero, so
+    // a captured launch replayed with its one epoch starts from zero too.
     unsigned long long* ticket;  // [BH]
     unsigned epoch;              // this call's epoch (never 0)
     CombineArgs cmb;
@@ -452,6 +455,8 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     }
     lds_barrier();
     if (*flag) {
+        // every workgroup of the head has counted: no other update can follow
+        if (tid == 0) __hip_atomic_store(&a.ticket[bh], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const CombineArgs& c = a.cmb;
         constexpr int E4 = E / 4;  // S and z regions both hold whole float4s
         const BufRsrc hp = make_rsrc(c.partial + (size_t)bh * c.P * E, (uint32_t)c.P * E * 4u);

@@ -310,3 +310,65 @@ def test_stale_counters_heal(la):
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
     assert torch.equal(S, S0) and torch.equal(z, z0)
+
+
+def test_graph_replays_match_eager(la):
+    """A captured state + apply step replayed with new input contents, with
+    eager calls on the same workspace between the replays, gives the eager
+    outputs of those inputs on every replay.  The captured state launch keeps
+    one counter epoch, so this holds only because the workgroup that completes
+    a head puts its counter back to zero."""
+    import torch
+    B, H, N, d = 2, 32, 3000, 64  # four partials of 16 KB a head: fused stage 2
+    grid = (4, 23, 40)
+    sets = [_inputs(B, H, N, d, "bf16", 40 + i)[1] for i in range(3)]
+    ws = la.workspace(B, H, N, d, sets[0][0].device, grid=grid)
+    eager = [la.bidirectional(q, k, v, grid, ws=ws).clone() for q, k, v in sets]
+    sq, sk, sv = (t.clone() for t in sets[0])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up call on the capture stream
+        la.bidirectional(sq, sk, sv, grid, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = la.bidirectional(sq, sk, sv, grid, ws=ws)
+    for rep in range(6):
+        i = rep % 3
+        for dst, src in zip((sq, sk, sv), sets[i]):
+            dst.copy_(src)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[i]), rep
+        # eager work on the same workspace between replays
+        o2 = la.bidirectional(*sets[(i + 1) % 3], grid, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, eager[(i + 1) % 3]), rep
+
+
+def test_one_workspace_many_shapes(la):
+    """One workspace, zero-filled once, shared by calls of different sizes in
+    turn: a call whose partial states cover the bytes another shape's counters
+    would sit at must not disturb that shape's next call (the counters have a
+    fixed place)."""
+    import torch
+    shapes = [(1, 16, 4000, 128, (4, 25, 40)), (2, 32, 3000, 64, (3, 25, 40)), (1, 4, 2500, 32, (3, 25, 40))]
+    data = [_inputs(B, H, N, d, "bf16", 70 + i)[1] for i, (B, H, N, d, _) in enumerate(shapes)]
+    ref = []
+    for (B, H, N, d, grid), (q, k, v) in zip(shapes, data):
+        ws = torch.zeros(la.workspace_bytes(B, H, N, d, grid), dtype=torch.uint8, device=q.device)
+        S, z = la.state_reduce(k, v, grid, ws=ws)
+        ref.append((S.clone(), z.clone(), la.bidirectional(q, k, v, grid, ws=ws).clone()))
+    nbytes = max(la.workspace_bytes(B, H, N, d, grid) for B, H, N, d, grid in shapes)
+    shared = torch.zeros(nbytes, dtype=torch.uint8, device=data[0][0].device)
+    for rep in range(3):
+        for i in (0, 1, 2, 1, 0):
+            q, k, v = data[i]
+            grid = shapes[i][4]
+            S, z = la.state_reduce(k, v, grid, ws=shared)
+            o = la.bidirectional(q, k, v, grid, ws=shared)
+            torch.cuda.synchronize()
+            assert torch.equal(S, ref[i][0]) and torch.equal(z, ref[i][1]), (rep, i)
+            assert torch.equal(o, ref[i][2]), (rep, i)
