@@ -103,6 +103,25 @@ LA_API int la_state_reduce(const void* Q, const void* K, const void* V, void* O,
                     int B, int H, int N, int d, int gt, int gh, int gw,
                     int block_tokens, float eps, int dtype, void* stream);
 
+/* The state pass as la_state_reduce, for callers that cannot allocate device
+ * memory -- code under stream capture, tight serving loops, harnesses that
+ * forbid allocation -- and so have no workspace to pass: its counters and
+ * partial states live in a static array of the library (one per GPU, held
+ * until the process ends) of LA_NOALLOC_SCRATCH_BYTES bytes.  Same arguments,
+ * kernels and results (bitwise) as la_state_reduce without ws / ws_bytes.
+ * Sizes whose plan needs more scratch than that return LA_E_WORKSPACE before
+ * anything is launched (la_last_hip_error() then says how much they need).
+ * The call allocates nothing and calls no allocating routine.  The first call
+ * on a device looks up the array's address there and clears its counters on
+ * `stream`.  Every call on one GPU shares that GPU's array: two calls that
+ * may overlap in time (two streams, two threads) race on it and must not be
+ * made; calls in order on one stream are safe. */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+LA_API int la_state_reduce_noalloc(const void* Q, const void* K, const void* V, void* O,
+                            float* S, float* z,
+                            int B, int H, int N, int d, int gt, int gh, int gw,
+                            int block_tokens, float eps, int dtype, void* stream);
+
 /* Apply pass (numerator / denominator of Eq. 2):
  *   O[b,h,n] = RoPE(relu(Q[b,h,n])) S[b,h] / (relu(Q[b,h,n]) . z[b,h] + eps).
  * Reads Q, S, z; writes O (bf16 outputs are rounded to nearest even).

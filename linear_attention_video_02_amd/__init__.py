@@ -35,7 +35,7 @@ class LinAttnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         msg = f"{where}: {STATUS.get(status, status)} ({strerror(status)})"
-        if status == -6:
+        if status == -6 or (status == -5 and where == "la_state_reduce_noalloc"):
             msg += ": " + lib().la_last_hip_error().decode()
         super().__init__(msg)
 
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.la_workspace_bytes_grid.restype = cs
         L.la_state_reduce.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [vp]
         L.la_state_reduce.restype = ci
+        L.la_state_reduce_noalloc.argtypes = [vp, vp, vp, vp, vp, vp] + common + [vp]
+        L.la_state_reduce_noalloc.restype = ci
         L.la_apply.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [vp]
         L.la_apply.restype = ci
         L.la_block_causal_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [ci, ci, vp]
@@ -245,6 +247,21 @@ def state_reduce(k, v, grid=None, S=None, z=None, ws=None):
                                _dtype_code(k), _stream(k))
     if rc:
         raise LinAttnError(rc, "la_state_reduce")
+    return S, z
+
+
+def state_reduce_noalloc(k, v, S, z, grid=None):
+    """state_reduce into the caller's S and z through la_state_reduce_noalloc:
+    no workspace, the library's static scratch instead (nothing is allocated)."""
+    _check_same_shape("state_reduce_noalloc k/v", k, v)
+    B, H, N, d = k.shape
+    _check_state(S, z, B, H, d, k.device, "state_reduce_noalloc")
+    _check_qkv(k, v)
+    gt, gh, gw = _grid(grid)
+    rc = lib().la_state_reduce_noalloc(None, _ptr(k), _ptr(v), None, _ptr(S), _ptr(z), B, H, N, d,
+                                       gt, gh, gw, 0, 0.0, _dtype_code(k), _stream(k))
+    if rc:
+        raise LinAttnError(rc, "la_state_reduce_noalloc")
     return S, z
 
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -25,6 +26,18 @@
 __global__ __launch_bounds__(256) void la_copy_kernel(const u32x4* src, u32x4* dst, size_t n16) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n16) dst[i] = src[i];
+}
+
+// Scratch of la_state_reduce_noalloc, for callers that cannot allocate: the
+// same layout as a caller's workspace (counters, then partial states), in a
+// fixed array of the code object.  Each GPU the library runs on holds its own
+// copy until the process ends.  Host code uses the array only through the
+// device address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void la_zero_kernel(u32x4* p, size_t n16) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n16) p[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
 namespace {
@@ -614,8 +627,8 @@ int max_partials(int B, int H, int N, int d, int gt, int gh, int gw) {
     return P;
 }
 
-// Argument checks of the state pass (everything but the workspace);
-// *need = workspace bytes of the call's plan.
+// Argument checks of the state pass shared by la_state_reduce and its
+// no-allocation variant; *need = workspace bytes of the call's plan.
 int state_reduce_checks(const void* K, const void* V, const float* S, const float* z, int B, int H, int N, int d,
                         int gt, int gh, int gw, float eps, int dtype, size_t* need) {
     int rc = check_common(B, H, N, d, gt, gh, gw, eps, dtype);
@@ -631,6 +644,36 @@ int state_reduce_checks(const void* K, const void* V, const float* S, const floa
     if (overlaps(S, nS, K, nkv) || overlaps(S, nS, V, nkv) || overlaps(z, nz, K, nkv) ||
         overlaps(z, nz, V, nkv) || overlaps(S, nS, z, nz))
         return LA_E_ALIAS;
+    return LA_OK;
+}
+
+// Device address of the static scratch on the current device, looked up once
+// per device (each device holds its own copy of the array at its own
+// address).  The first call on a device also clears the counter region, on
+// the caller's stream ahead of the caller's own work.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(hipStream_t st, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return LA_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        const size_t n16 = (size_t)kTicketHeads * 8 / 16;
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(la_zero_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st, (u32x4*)ptr,
+                           n16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "la_zero_kernel launch");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return LA_OK;
 }
 
@@ -667,6 +710,28 @@ int la_state_reduce(const void* Q, const void* K, const void* V, void* O, float*
     if (overlaps(ws, ws_bytes, K, nkv) || overlaps(ws, ws_bytes, V, nkv) || overlaps(ws, ws_bytes, S, nS) ||
         overlaps(ws, ws_bytes, z, nz))
         return LA_E_ALIAS;
+    return run_state(K, V, S, z, nullptr, nullptr, nullptr, nullptr, ws, B, H, N, 0, d, gt, gh, gw, dtype,
+                     (hipStream_t)stream);
+}
+
+int la_state_reduce_noalloc(const void* Q, const void* K, const void* V, void* O, float* S, float* z, int B,
+                            int H, int N, int d, int gt, int gh, int gw, int block_tokens, float eps, int dtype,
+                            void* stream) {
+    (void)Q;
+    (void)O;
+    (void)block_tokens;
+    size_t need = 0;
+    int rc = state_reduce_checks(K, V, S, z, B, H, N, d, gt, gh, gw, eps, dtype, &need);
+    if (rc != LA_OK) return rc;
+    if (need > LA_NOALLOC_SCRATCH_BYTES) {
+        snprintf(g_hip_msg, sizeof(g_hip_msg),
+                 "la_state_reduce_noalloc: these sizes need %zu bytes of scratch, the static scratch holds %zu",
+                 need, (size_t)LA_NOALLOC_SCRATCH_BYTES);
+        return LA_E_WORKSPACE;
+    }
+    void* ws = nullptr;
+    rc = scratch_of_current_device((hipStream_t)stream, &ws);
+    if (rc != LA_OK) return rc;
     return run_state(K, V, S, z, nullptr, nullptr, nullptr, nullptr, ws, B, H, N, 0, d, gt, gh, gw, dtype,
                      (hipStream_t)stream);
 }

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
                           "la_block_causal_step", "la_token_causal", "la_temporal_conv_step",
                           "la_stream_copy", "la_strerror", "la_last_hip_error", "la_set_tuning",
-                          "la_workspace_bytes_grid"}
+                          "la_workspace_bytes_grid", "la_state_reduce_noalloc"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -265,3 +265,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(la, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         la.lib()
+
+
+def test_noalloc_rejects_before_any_device_call(L):
+    """la_state_reduce_noalloc checks arguments and the scratch size its plan
+    needs before it touches a device (there is none here)."""
+    code = header_enum
+    G = 1 << 38  # buffers far apart: no overlap for the sizes below
+
+    def call(B=1, H=2, N=256, d=64, dtype=la.LA_BF16, K=p(0), S=p(2 * G), z=p(3 * G), grid=(0, 0, 0)):
+        return L.la_state_reduce_noalloc(None, K, p(G), None, S, z, B, H, N, d, *grid, 0, 1e-6, dtype, None)
+
+    assert call(d=48) == code("LA_E_UNSUPPORTED")
+    assert call(B=0) == code("LA_E_SHAPE")
+    assert call(S=None) == code("LA_E_NULLPTR")
+    assert call(z=p(3 * G + 4)) == code("LA_E_ALIGN")
+    assert call(z=p(2 * G + 64)) == code("LA_E_ALIAS")  # z inside S
+    # 4096 (batch, head) pairs at d = 128: one partial per head is 264 MB
+    assert call(B=64, H=64, N=4096, d=128) == code("LA_E_WORKSPACE")
+    assert b"scratch" in L.la_last_hip_error()
+    assert call(B=64, H=64, N=4096, d=128, dtype=la.LA_FP32) == code("LA_E_WORKSPACE")

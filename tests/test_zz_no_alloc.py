@@ -1,0 +1,43 @@
+"""la_state_reduce_noalloc (static scratch, no workspace argument) against
+la_state_reduce with a caller's workspace: bitwise equal S and z on two calls
+in a row, the second on a smaller input, in the fused (bf16, small partials)
+and separate-combine (bf16 d = 112, fp32) stage-2 forms."""
+import pytest
+
+from _gpu import say, upload
+from linear_attention_video_02_amd.inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def la():
+    import linear_attention_video_02_amd as m
+    m.lib()
+    return m
+
+
+CASES = [  # (B, H, N, d, dtype, grid) first call, then a smaller second call
+    ((2, 32, 6000, 64, "bf16", (6, 25, 40)), (1, 8, 2077, 64, "bf16", (3, 25, 40))),
+    ((1, 6, 5000, 112, "bf16", (5, 25, 40)), (1, 2, 999, 112, "bf16", (1, 25, 40))),
+    ((1, 4, 3000, 128, "fp32", (3, 25, 40)), (1, 1, 700, 32, "fp32", (1, 25, 40))),
+]
+
+
+@pytest.mark.parametrize("first,second", CASES)
+def test_noalloc_matches_workspace_entry(la, first, second):
+    import torch
+    for i, (B, H, N, d, dt, grid) in enumerate((first, second)):
+        say(f"  noalloc call {i}: B={B} H={H} N={N} d={d} {dt} grid={grid}")
+        _, k, v = (upload(a, dt) for a in make_qkv(B, H, N, d, dt, seed=60 + i))
+        S_ref, z_ref = la.state_reduce(k, v, grid)
+        S = torch.full((B, H, d, d), float("nan"), dtype=torch.float32, device=k.device)
+        z = torch.full((B, H, d), float("nan"), dtype=torch.float32, device=k.device)
+        la.state_reduce_noalloc(k, v, S, z, grid)
+        torch.cuda.synchronize()
+        assert torch.equal(S, S_ref) and torch.equal(z, z_ref), i
+        # and again without RoPE, on the scratch the call before left behind
+        S_ref2, z_ref2 = la.state_reduce(k, v, None)
+        la.state_reduce_noalloc(k, v, S, z, None)
+        torch.cuda.synchronize()
+        assert torch.equal(S, S_ref2) and torch.equal(z, z_ref2), i
