@@ -50,13 +50,14 @@ def kernel_source_hash(workload=None):
 
 
 # The bf16 state pass is one launch when a head's partials are small (its last
-# workgroup per head sums them); otherwise, or with LA_STATE_FUSED=0, a
-# separate combine launch follows it.
+# workgroup per head sums them); otherwise, or with the tuning knob
+# state_fused = 0, a separate combine launch follows it.
 STATE_KERNELS = ("la_state_bf16_kernel",)
 COMBINE_KERNEL = "la_state_combine_kernel"
 APPLY_KERNELS = ("la_apply_bf16_kernel",)
+CAUSAL_KERNELS = ("la_prefix_kernel", "la_causal_bf16_kernel")  # token-causal pass after the partials
 TCONV_KERNELS = ("la_tconv_bf16_kernel",)
-OUR_KERNELS = STATE_KERNELS + (COMBINE_KERNEL,) + APPLY_KERNELS + TCONV_KERNELS
+OUR_KERNELS = STATE_KERNELS + (COMBINE_KERNEL,) + APPLY_KERNELS + CAUSAL_KERNELS + TCONV_KERNELS
 CALIB_KERNEL = "MulFunctor"   # torch's elementwise o = q * 1: a plain copy of known size
 LIBGEMM_KERNEL = "Cijk_"      # hipBLASLt's GEMM kernels (context for the temporal convolution)
 
@@ -281,6 +282,11 @@ def _short(name):
 
 WORKLOAD_TITLES = {
     WORKLOAD: "720p5s workload (bf16, B=2 H=32 N=19320 d=64, RoPE)",
+    "sana2b": "sana2b workload (SANA-Video-2B heads: bf16, B=1 H=20 N=19320 d=112, RoPE)",
+    "cross720p": "cross720p workload (cross-attention: bf16, B=2 H=32, 19320 video queries over 300 text "
+                 "keys/values, d=64, no RoPE)",
+    "tc720p5s": "tc720p5s workload (token-causal: bf16, B=2 H=32 N=19320 d=64, RoPE)",
+    "720p60s": "720p60s workload (block-causal: bf16, B=1 H=32 N=220800 in 10 blocks of 22080, d=64, RoPE)",
     "tconv720p": "tconv720p workload (temporal convolution, bf16, one block of 24 frames x 920 "
                  "positions, D=2240, bias)",
 }
@@ -307,26 +313,39 @@ def summarize_trace(trace_dir, command, out_path, workload=WORKLOAD):
         if k in OUR_KERNELS or (k or "").startswith("hipBLASLt"):
             lines.append(f"| {k} | {st['Calls']} | {float(st['AverageNs']) / 1e3:.1f} | "
                          f"{float(st['MinNs']) / 1e3:.1f} | {float(st['MaxNs']) / 1e3:.1f} |")
-    # per step, from the trace: state kernel start .. (combine end) .. apply end
+    # per pass, from the trace: state kernel start .. (combine end) .. last kernel's end,
+    # the last kernel being the apply (or the causal scan in token-causal mode)
     t = lambda r, k: int(r[k]) / 1e3
+    last = CAUSAL_KERNELS[1:] if workload == "tc720p5s" else APPLY_KERNELS
     steps_ = []
     for i, r in enumerate(la):
         if _short(r["Kernel_Name"]) not in STATE_KERNELS:
             continue
         j = i + 1
-        while j < len(la) and _short(la[j]["Kernel_Name"]) == COMBINE_KERNEL:
+        while j < len(la) and _short(la[j]["Kernel_Name"]) in (COMBINE_KERNEL, CAUSAL_KERNELS[0]):
             j += 1
-        if j < len(la) and _short(la[j]["Kernel_Name"]) in APPLY_KERNELS:
+        if j < len(la) and _short(la[j]["Kernel_Name"]) in last:
             pass_end = t(la[j - 1], "End_Timestamp")
             steps_.append((pass_end - t(r, "Start_Timestamp"), t(la[j], "Start_Timestamp") - pass_end,
-                           t(la[j], "End_Timestamp") - t(r, "Start_Timestamp")))
+                           t(la[j], "End_Timestamp") - t(r, "Start_Timestamp"), t(r, "Start_Timestamp"),
+                           t(la[j], "End_Timestamp")))
     if steps_:
         n = len(steps_)
-        lines += ["", f"From the trace, over {n} steps (state kernel start to apply kernel end):", "",
-                  f"- state pass (state kernel start to its last launch's end): "
+        what = {"tc720p5s": ("state kernel start to the causal scan's end", "partials and prefix",
+                             "prefix -> scan"),
+                "720p60s": ("one block step: state kernel start to apply kernel end", "state pass",
+                            "state pass -> apply")}.get(
+            workload, ("state kernel start to apply kernel end", "state pass", "state pass -> apply"))
+        lines += ["", f"From the trace, over {n} passes ({what[0]}):", "",
+                  f"- {what[1]} (state kernel start to the end of the launch before the last kernel): "
                   f"{sum(g[0] for g in steps_) / n:.1f} us",
-                  f"- gap state pass -> apply: {sum(g[1] for g in steps_) / n:.2f} us",
-                  f"- whole step: {sum(g[2] for g in steps_) / n:.1f} us"]
+                  f"- gap {what[2]}: {sum(g[1] for g in steps_) / n:.2f} us",
+                  f"- whole pass: {sum(g[2] for g in steps_) / n:.1f} us"]
+        if workload == "720p60s" and n >= 10:
+            # ten block steps make one step of the sequence (every step runs all blocks)
+            seq = [steps_[i + 9][4] - steps_[i][3] for i in range(0, n - 9, 10)]
+            lines.append(f"- whole 10-block sequence (block 0's state start to block 9's apply end), "
+                         f"over {len(seq)} sequences: {sum(seq) / len(seq):.1f} us")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -467,10 +486,21 @@ def main():
             tensor_bytes = w["B"] * w["T"] * w["P"] * w["D"] * 2  # the calibration copy moves X
             # minimum HBM bytes of one launch: X and W read once, Y written once
             algo = {"la_tconv_bf16_kernel": 2 * tensor_bytes + 3 * w["D"] * w["D"] * 2}
+        elif wlname == "cross720p":
+            from linear_attention_video_02_amd.inputs import CROSS
+            w = CROSS[wlname]
+            tensor_bytes = w["B"] * w["H"] * w["Nq"] * w["d"] * 2  # the calibration copy moves Q
+            tkv = w["B"] * w["H"] * w["Nkv"] * w["d"] * 2
+            algo = {"la_state_bf16_kernel": 2 * tkv, "la_apply_bf16_kernel": 2 * tensor_bytes}
         else:
             from linear_attention_video_02_amd.inputs import WORKLOADS
-            w = WORKLOADS[wlname]
-            tensor_bytes = w["B"] * w["H"] * w["N"] * w["d"] * 2
+            w = WORKLOADS["720p5s" if wlname == "tc720p5s" else wlname]
+            n_tok = w["block"] if wlname == "720p60s" else w["N"]  # per launch: one block
+            tensor_bytes = w["B"] * w["H"] * n_tok * w["d"] * 2
+            if wlname == "tc720p5s":
+                # each kernel's own stream: the partials pass reads K, V; the scan
+                # reads Q, K, V and writes O (the path's minimum is 4 tensors)
+                algo = {"la_state_bf16_kernel": 2 * tensor_bytes, "la_causal_bf16_kernel": 4 * tensor_bytes}
         cmds_ = profile_commands(wlname)
         os.makedirs(args.out, exist_ok=True)
         if args.summarize_trace:
