@@ -49,5 +49,39 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+# Host-side sanitizers: the host code (argument checks, planning and alias
+# logic) compiled with AddressSanitizer and UndefinedBehaviorSanitizer, any UB
+# report fatal; the device code is built as usual, without sanitizers.
+SANITIZE = ["-O1", "-g", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime to preload into a non-sanitized host process."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """Compile the library's host code with ASan + UBSan into `out` (CPU tests only)."""
+    import tempfile
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    host_flags = [f for f in FLAGS if f != "-O3"]  # -O1 from SANITIZE
+    with tempfile.TemporaryDirectory(prefix="la_san_") as tmp:
+        objs = []
+        for src, flags in SOURCES.items():
+            obj = os.path.join(tmp, src + ".o")
+            _run([hipcc, *host_flags, *flags, *SANITIZE, "-I", INCLUDE, "-I", CSRC, "-c",
+                  os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+              "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *objs, "-o", out], verbose)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

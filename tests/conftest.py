@@ -8,3 +8,9 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # the host-sanitizer test reruns the CPU boundary tests against a sanitized
+    # host-only build of the library, named here
+    lib = os.environ.get("LA_TEST_LIBRARY")
+    if lib:
+        import linear_attention_video_02_amd as la
+        la.LIB_PATH = lib
