@@ -158,8 +158,9 @@ LA_API int la_block_causal_step(const void* Q, const void* K, const void* V, voi
  * (gt*gh*gw must hold n_offset + N tokens), so a long sequence can be fed in
  * segments.  S_carry/z_carry are both NULL (start from the empty state; the
  * final state is not returned) or both non-NULL: the state before token 0 on
- * entry, the state after token N-1 on return.  bf16 and d = 64 only
- * (otherwise LA_E_UNSUPPORTED).  N = 0 returns LA_OK and leaves the carry as
+ * entry, the state after token N-1 on return.  Every d and dtype of the
+ * other calls (bf16 on matrix cores, fp32 in plain fp32 arithmetic).
+ * N = 0 returns LA_OK and leaves the carry as
  * it is.  ws: at least la_workspace_bytes(B, H, N, d) bytes (this call
  * neither needs nor disturbs the zero counters); it must not overlap O or
  * the carry.  Every piece of

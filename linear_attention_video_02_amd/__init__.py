@@ -345,7 +345,7 @@ def block_causal_step(q, k, v, S_carry, z_carry, N, grid, block_tokens, block_id
 def token_causal(q, k, v, grid=None, eps=1e-6, S_carry=None, z_carry=None, n_offset=0, out=None, ws=None):
     """Token-causal linear attention (Eq. 3): token i sees tokens j <= i.
 
-    q, k, v: [B, H, N, d] bf16, d = 64; token i sits at global position
+    q, k, v: [B, H, N, d] bf16 or fp32, d in {32, 64, 112, 128}; token i sits at global position
     n_offset + i.  With S_carry/z_carry ([B, H, d, d] / [B, H, d] fp32) the
     scan starts from that state and leaves the final state in them.
     """

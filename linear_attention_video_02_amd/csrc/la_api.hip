@@ -505,23 +505,44 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
     return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope, pl.nph), dim3(pl.grid), pl.lds, st, a, threads);
 }
 
+// LDS of the token-causal scan kernel without its RoPE table
+size_t causal_fixed_lds(int d, int dtype) {
+#define LA_CFG(D)                                                                                  \
+    if (d == D) return dtype == LA_BF16 ? (size_t)CausalBf16Cfg<D>::SMEM_FIXED : (size_t)CausalF32Cfg<D>::SMEM_FIXED;
+    LA_CFG(32)
+    LA_CFG(64)
+    LA_CFG(112)
+#undef LA_CFG
+    return dtype == LA_BF16 ? (size_t)CausalBf16Cfg<128>::SMEM_FIXED : (size_t)CausalF32Cfg<128>::SMEM_FIXED;
+}
+
+// The partial-state pass of token-causal mode: at bf16 d = 64 the 512-thread
+// state kernel, two per CU (see run_token_causal), unless the tuning knob
+// tc_state_threads = 1024 asks for the larger workgroups.
+bool tc_half_state(int d, int dtype) {
+    return dtype == LA_BF16 && d == 64 && knob(K_TC_STATE_THREADS, 512) == 512;
+}
+
 // Token-causal pass: about causal_wgs workgroups (default two 256-thread
-// workgroups per CU), chunks a multiple of 128 tokens (the state kernel's tile
-// at d = 64 and two causal steps), at most kMaxPartials per head.
-int plan_causal(const LaGeom& g, Plan* out) {
+// workgroups per CU where two fit -- bf16, d <= 64 -- else one), chunks a
+// multiple of 128 tokens (the state kernel's tile at d = 64 and two causal
+// steps), at most kMaxPartials per head.
+int plan_causal(const LaGeom& g, int d, int dtype, Plan* out) {
     constexpr int unit = 128;
-    const int target = knob(K_CAUSAL_WGS, 512);
+    const bool two_per_cu = dtype == LA_BF16 && d <= 64;
+    const int target = knob(K_CAUSAL_WGS, two_per_cu ? 512 : 256);
     const int ntok = g.ntok;
     int P = target / g.BH;  // at most `target` workgroups (see plan_state)
     P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
     const int max_p = (ntok + unit - 1) / unit;
     if (P > max_p) P = max_p;
+    const int state_lds = tc_half_state(d, dtype) ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0;
     for (;;) {
         const int chunk = (int)align_up((size_t)((ntok + P - 1) / P), unit);
         const int Peff = (ntok + chunk - 1) / chunk;
-        const size_t lds = (size_t)CausalBf16Cfg<64>::SMEM_FIXED + table_entries(g, chunk) * 8;
+        const size_t lds = causal_fixed_lds(d, dtype) + table_entries(g, chunk) * 8;
         Plan st;
-        if (Peff <= kMaxPartials && lds <= kLdsLimit && plan_state(g, 64, LA_BF16, &st, chunk) == LA_OK) {
+        if (Peff <= kMaxPartials && lds <= kLdsLimit && plan_state(g, d, dtype, &st, chunk, state_lds) == LA_OK) {
             out->P = Peff;
             out->chunk = chunk;
             out->lds = lds;
@@ -532,19 +553,50 @@ int plan_causal(const LaGeom& g, Plan* out) {
     }
 }
 
+KernelFn<CausalArgs> causal_kernel(int d, int dtype, bool rope) {
+#define LA_PICK(D)                                                                                  \
+    if (d == D) {                                                                                   \
+        if (dtype == LA_BF16) return rope ? la_causal_bf16_kernel<D, true> : la_causal_bf16_kernel<D, false>; \
+        return rope ? la_causal_f32_kernel<D, true> : la_causal_f32_kernel<D, false>;             \
+    }
+    LA_PICK(32)
+    LA_PICK(64)
+    LA_PICK(112)
+    LA_PICK(128)
+#undef LA_PICK
+    return nullptr;
+}
+
+KernelFn<PrefixArgs> prefix_kernel(int d) {
+    if (d == 32) return la_prefix_kernel<32>;
+    if (d == 64) return la_prefix_kernel<64>;
+    if (d == 112) return la_prefix_kernel<112>;
+    return la_prefix_kernel<128>;
+}
+
+int state_threads(int d, int dtype) {
+    return dtype != LA_BF16 ? 256
+           : d == 32        ? StateBf16Cfg<32>::THREADS
+           : d == 64        ? StateBf16Cfg<64>::THREADS
+           : d == 112       ? StateBf16Cfg<112>::THREADS
+                            : StateBf16Cfg<128>::THREADS;
+}
+
+// Token-causal mode (Eq. 3 token by token): partial states of the chunks,
+// their exclusive prefixes in place, then the causal scan of every chunk.
 int run_token_causal(const void* Q, const void* K, const void* V, void* O, float* S_carry, float* z_carry,
                      void* ws, int B, int H, int ntok, int n_offset, int d, int gt, int gh, int gw, float eps,
-                     hipStream_t st) {
+                     int dtype, hipStream_t st) {
     const LaGeom g = make_geom(B, H, ntok, n_offset, d, gt, gh, gw);
     Plan pc, ps;
-    int rc = plan_causal(g, &pc);
+    int rc = plan_causal(g, d, dtype, &pc);
     if (rc != LA_OK) return rc;
-    // Partial states in 512-thread workgroups, two per CU: the P chunks per
-    // head (512 workgroups at 720p-5s) then run in one round instead of two
-    // rounds of 1024-thread workgroups (235 -> 229 us per call at 720p-5s).
-    // The tuning knob tc_state_threads = 1024 selects the larger workgroups.
-    const bool half = knob(K_TC_STATE_THREADS, 512) == 512;
-    rc = plan_state(g, d, LA_BF16, &ps, pc.chunk, half ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
+    // bf16 d = 64: partial states in 512-thread workgroups, two per CU: the P
+    // chunks per head (512 workgroups at 720p-5s) then run in one round
+    // instead of two rounds of 1024-thread workgroups (235 -> 229 us per call
+    // at 720p-5s).
+    const bool half = tc_half_state(d, dtype);
+    rc = plan_state(g, d, dtype, &ps, pc.chunk, half ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
     if (rc != LA_OK) return rc;
     const WsLayout L = ws_layout(g.BH, d, ps.P);
     float* partial = (float*)((char*)ws + L.partial);
@@ -557,10 +609,10 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     sa.P = ps.P;
     sa.g = g;
     sa.ticket = nullptr;  // partials only: the prefix kernel reads them
-    KernelFn<StateArgs> sk = state_kernel(d, LA_BF16, g.rope);
+    sa.epoch = 0;
+    KernelFn<StateArgs> sk = state_kernel(d, dtype, g.rope);
     if (half) sk = g.rope ? la_state_bf16_kernel<64, true, 512> : la_state_bf16_kernel<64, false, 512>;
-    rc = launch_kernel<StateArgs>(sk, dim3(ps.P * g.BH), ps.lds, st, sa,
-                                  half ? 512 : StateBf16Cfg<64>::THREADS);
+    rc = launch_kernel<StateArgs>(sk, dim3(ps.P * g.BH), ps.lds, st, sa, half ? 512 : state_threads(d, dtype));
     if (rc != LA_OK) return rc;
     // 2. exclusive prefixes in place (+ carry), total -> carry
     PrefixArgs pa;
@@ -570,7 +622,7 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     pa.S_out = S_carry;
     pa.z_out = z_carry;
     pa.P = ps.P;
-    rc = launch_kernel<PrefixArgs>(la_prefix_kernel<64>, dim3((d * d + d + 255) / 256, g.BH), 0, st, pa);
+    rc = launch_kernel<PrefixArgs>(prefix_kernel(d), dim3((d * d + d + 255) / 256, g.BH), 0, st, pa);
     if (rc != LA_OK) return rc;
     // 3. causal scan of every chunk from its prefix
     CausalArgs ca;
@@ -583,8 +635,7 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     ca.chunk = pc.chunk;
     ca.P = pc.P;
     ca.g = g;
-    auto fn = g.rope ? la_causal_bf16_kernel<64, true> : la_causal_bf16_kernel<64, false>;
-    return launch_kernel<CausalArgs>(fn, dim3(pc.P * g.BH), pc.lds, st, ca, CausalBf16Cfg<64>::THREADS);
+    return launch_kernel<CausalArgs>(causal_kernel(d, dtype, g.rope), dim3(pc.P * g.BH), pc.lds, st, ca, 256);
 }
 
 size_t elem_bytes(int dtype) { return dtype == LA_BF16 ? 2 : 4; }
@@ -622,7 +673,8 @@ int max_partials(int B, int H, int N, int d, int gt, int gh, int gw) {
     {
         const LaGeom g = make_geom(B, H, N > 0 ? N : 1, 0, d, gt, gh, gw);
         Plan pc;
-        if (d == 64 && plan_causal(g, &pc) == LA_OK && pc.P > P) P = pc.P;
+        for (int dtype : {LA_BF16, LA_FP32})
+            if (plan_causal(g, d, dtype, &pc) == LA_OK && pc.P > P) P = pc.P;
     }
     return P;
 }
@@ -800,7 +852,6 @@ int la_token_causal(const void* Q, const void* K, const void* V, void* O, float*
     if (n_offset < 0 || N < 0 || (long long)n_offset + N >= (1ll << 30)) return LA_E_SHAPE;
     int rc = check_common(B, H, n_offset + N, d, gt, gh, gw, eps, dtype);
     if (rc != LA_OK) return rc;
-    if (dtype != LA_BF16 || d != 64) return LA_E_UNSUPPORTED;
     if ((S_carry == nullptr) != (z_carry == nullptr)) return LA_E_NULLPTR;
     if (!ws || (N > 0 && (!Q || !K || !V || !O))) return LA_E_NULLPTR;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(ws) ||
@@ -810,10 +861,9 @@ int la_token_causal(const void* Q, const void* K, const void* V, void* O, float*
     Plan pc, ps;
     {
         const LaGeom g = make_geom(B, H, N, n_offset, d, gt, gh, gw);
-        rc = plan_causal(g, &pc);
+        rc = plan_causal(g, d, dtype, &pc);
         if (rc != LA_OK) return rc;
-        rc = plan_state(g, d, LA_BF16, &ps, pc.chunk,
-                        knob(K_TC_STATE_THREADS, 512) == 512 ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
+        rc = plan_state(g, d, dtype, &ps, pc.chunk, tc_half_state(d, dtype) ? StateBf16Cfg<64, 512>::SMEM_FIXED : 0);
         if (rc != LA_OK) return rc;
     }
     if (ws_bytes < ws_layout(B * H, d, ps.P).total) return LA_E_WORKSPACE;
@@ -827,7 +877,7 @@ int la_token_causal(const void* Q, const void* K, const void* V, void* O, float*
         overlaps(ws, ws_bytes, O, nb) || overlaps(ws, ws_bytes, Q, nb) || overlaps(ws, ws_bytes, K, nb) ||
         overlaps(ws, ws_bytes, V, nb))
         return LA_E_ALIAS;
-    return run_token_causal(Q, K, V, O, S_carry, z_carry, ws, B, H, N, n_offset, d, gt, gh, gw, eps,
+    return run_token_causal(Q, K, V, O, S_carry, z_carry, ws, B, H, N, n_offset, d, gt, gh, gw, eps, dtype,
                             (hipStream_t)stream);
 }
 

@@ -180,9 +180,9 @@ def causal_call(L, **kw):
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(dtype=la.LA_FP32), "LA_E_UNSUPPORTED"),
-    (dict(d=32), "LA_E_UNSUPPORTED"),
-    (dict(d=128), "LA_E_UNSUPPORTED"),
+    (dict(dtype=7), "LA_E_UNSUPPORTED"),
+    (dict(d=48), "LA_E_UNSUPPORTED"),
+    (dict(d=96), "LA_E_UNSUPPORTED"),
     (dict(n0=-1), "LA_E_SHAPE"),
     (dict(n0=1), "LA_E_SHAPE"),                    # grid holds 1000 tokens, needs 1001
     (dict(N=-3), "LA_E_SHAPE"),
@@ -194,6 +194,9 @@ def causal_call(L, **kw):
     (dict(O=p(0)), "LA_E_ALIAS"),                  # O == Q
     (dict(ws=p(3 << 30)), "LA_E_ALIAS"),           # workspace over O
     (dict(gt=1, gh=1000, gw=3000), "LA_E_UNSUPPORTED"),  # RoPE table cannot fit LDS
+    (dict(gt=1, gh=1000, gw=3000, d=128, dtype=la.LA_FP32), "LA_E_UNSUPPORTED"),
+    (dict(d=112, ws_bytes=100), "LA_E_WORKSPACE"),
+    (dict(d=32, dtype=la.LA_FP32, O=p(1 << 30)), "LA_E_ALIAS"),  # O == K
 ])
 def test_token_causal_rejects(L, kw, want):
     assert causal_call(L, **kw) == E[want]

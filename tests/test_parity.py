@@ -263,26 +263,55 @@ def test_cross720p(la):
 
 
 TC_CASES = [
-    # B, H, N, d, grid, eps   (token-causal, Eq. 3 literally)
-    (1, 1, 1, 64, (1, 1, 1), 1e-6),
-    (1, 2, 1000, 64, (10, 10, 10), 1e-6),
-    (2, 3, 300, 64, None, 1e-6),
-    (1, 2, 129, 64, (2, 9, 10), 0.0),
-    (1, 1, 5000, 64, (3, 41, 41), 1e-6),
-    (1, 4, 4097, 64, (5, 23, 40), 1e-6),
+    # B, H, N, d, grid, eps, dtype   (token-causal, Eq. 3 literally)
+    (1, 1, 1, 64, (1, 1, 1), 1e-6, "bf16"),
+    (1, 2, 1000, 64, (10, 10, 10), 1e-6, "bf16"),
+    (2, 3, 300, 64, None, 1e-6, "bf16"),
+    (1, 2, 129, 64, (2, 9, 10), 0.0, "bf16"),
+    (1, 1, 5000, 64, (3, 41, 41), 1e-6, "bf16"),
+    (1, 4, 4097, 64, (5, 23, 40), 1e-6, "bf16"),
+    # other head sizes: 32 on the 64-channel kernel, 112 and 128 on the 128-channel one
+    (1, 2, 1000, 32, (10, 10, 10), 1e-6, "bf16"),
+    (2, 3, 300, 32, None, 1e-6, "bf16"),
+    (1, 2, 1000, 112, (10, 10, 10), 1e-6, "bf16"),
+    (1, 3, 129, 112, (2, 9, 10), 0.0, "bf16"),
+    (1, 1, 4097, 112, (5, 23, 40), 1e-6, "bf16"),
+    (1, 2, 1000, 128, (10, 10, 10), 1e-6, "bf16"),
+    (2, 2, 2077, 128, None, 1e-6, "bf16"),
+    (1, 1, 1, 128, (1, 1, 1), 1e-6, "bf16"),
+    # fp32 inputs
+    (1, 2, 1000, 64, (10, 10, 10), 1e-6, "fp32"),
+    (1, 1, 129, 64, (2, 9, 10), 0.0, "fp32"),
+    (2, 2, 300, 32, None, 1e-6, "fp32"),
+    (1, 1, 3001, 112, (4, 23, 40), 1e-6, "fp32"),
+    (1, 2, 777, 128, (3, 23, 40), 1e-6, "fp32"),
+    (1, 1, 1, 32, (1, 1, 1), 1e-6, "fp32"),
 ]
 
 
-@pytest.mark.parametrize("case", TC_CASES, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}" for c in TC_CASES])
+@pytest.mark.parametrize("case", TC_CASES, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}{c[6]}" for c in TC_CASES])
 def test_token_causal(la, case):
     import torch
-    B, H, N, d, grid, eps = case
+    B, H, N, d, grid, eps, dt = case
     say(f"[token-causal] {case}")
-    q, k, v = make_qkv(B, H, N, d, "bf16", seed=5000 + N)
-    out = la.token_causal(upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16"), grid, eps)
+    q, k, v = make_qkv(B, H, N, d, dt, seed=5000 + N + d)
+    out = la.token_causal(upload(q, dt), upload(k, dt), upload(v, dt), grid, eps)
     torch.cuda.synchronize()
     ref, _, _ = oracle.token_causal(q, k, v, grid, eps)
-    assert_close(host(out), ref, "bf16", f"token-causal {case}")
+    assert_close(host(out), ref, dt, f"token-causal {case}")
+
+
+def test_token_causal_sana2b(la):
+    """SANA-Video-2B heads (H = 20, d = 112) on the 720p-5s latent in
+    token-causal mode; sampled heads, every row."""
+    import torch
+    tq, tk, tv, w = make_workload_device("sana2b")
+    grid, eps = w["grid"], w["eps"]
+    out = la.token_causal(tq, tk, tv, grid, eps)
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 0), (0, 19), (0, 7)):
+        ref, _, _ = oracle.token_causal_head(host(tq[b, h]), host(tk[b, h]), host(tv[b, h]), grid, eps)
+        assert_close(host(out[b, h]), ref, "bf16", f"sana2b token-causal head ({b},{h})")
 
 
 def test_token_causal_720p5s(la):
@@ -297,12 +326,13 @@ def test_token_causal_720p5s(la):
         assert_close(host(out[b, h]), ref, "bf16", f"720p5s token-causal head ({b},{h})")
 
 
-def test_token_causal_carry_resume_and_determinism(la):
+@pytest.mark.parametrize("d,dt", [(64, "bf16"), (112, "bf16"), (32, "bf16"), (64, "fp32"), (128, "fp32")])
+def test_token_causal_carry_resume_and_determinism(la, d, dt):
     """Two segments with a carry and a position offset == one call; final carry == total state."""
     import torch
-    B, H, N, d, grid, eps = 1, 2, 2000, 64, (5, 20, 20), 1e-6
-    q, k, v = make_qkv(B, H, N, d, "bf16", seed=5100)
-    tq, tk, tv = upload(q, "bf16"), upload(k, "bf16"), upload(v, "bf16")
+    B, H, N, grid, eps = 1, 2, 2000, (5, 20, 20), 1e-6
+    q, k, v = make_qkv(B, H, N, d, dt, seed=5100)
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
     S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda:0")
     z = torch.zeros((B, H, d), dtype=torch.float32, device="cuda:0")
     m = 777
@@ -315,7 +345,7 @@ def test_token_causal_carry_resume_and_determinism(la):
     torch.cuda.synchronize()
     assert torch.equal(whole, again), "repeated calls differ"
     ref, Sr, zr = oracle.token_causal(q, k, v, grid, eps)
-    assert_close(host(torch.cat([o1, o2], dim=2)), ref, "bf16", "two segments with carry")
+    assert_close(host(torch.cat([o1, o2], dim=2)), ref, dt, "two segments with carry")
     assert state_err(host(S).reshape(-1, d), Sr.reshape(-1, d)) <= 1e-4
     np.testing.assert_allclose(host(z), zr, rtol=1e-5)
     # empty segment: carry unchanged
