@@ -231,10 +231,18 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     // Q and O of a head's chunk through descriptors bounded to [c0, c1): rows
     // past c1 read as zeros and their stores are dropped.
     const uint32_t chunk_bytes = (uint32_t)len * D * 2;
+    // (the head index goes through readfirstlane: the compiler cannot prove
+    // it wave-uniform once it comes out of the phase queues, and a
+    // descriptor it takes for divergent gets every load and store wrapped in
+    // a loop over lanes)
     auto q_rsrc = [&](int head) {
+        head = __builtin_amdgcn_readfirstlane(head);
         return make_rsrc((const uint16_t*)a.Q + ((size_t)head * ntok + c0) * D, chunk_bytes);
     };
-    auto o_rsrc = [&](int head) { return make_rsrc((uint16_t*)a.O + ((size_t)head * ntok + c0) * D, chunk_bytes); };
+    auto o_rsrc = [&](int head) {
+        head = __builtin_amdgcn_readfirstlane(head);
+        return make_rsrc((uint16_t*)a.O + ((size_t)head * ntok + c0) * D, chunk_bytes);
+    };
 
     if (threadIdx.x < NPH) q_next[threadIdx.x] = threadIdx.x == 0 ? C::NW * C::DEPTH * C::UNIT : 0;
 
