@@ -135,71 +135,6 @@ __device__ __forceinline__ void apply_item_of_block(int P, int NS, int spread, i
     p = k % P;
 }
 
-// One wave converts a head's S (fp32 [d][d], row = key channel) and z into an
-// LDS operand buffer: fp16 S^T scaled by 2^-eS (largest |S| to [2^13, 2^14)),
-// zero above d, and z; returns eS.  Two passes over S (from L2): the largest
-// magnitude, then the conversion, in coalesced 16-byte loads.
-template <int D, int DP>
-__device__ int convert_head_wave(const float* Sh, const float* zg, uint16_t* sth, float* zsh, int lane) {
-    constexpr int F4 = D * D / 4;  // float4 pieces of S
-    float amax = 0.0f;
-#pragma unroll 1
-    for (int f0 = 0; f0 < F4; f0 += 256) {
-        f32x4 v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 64 * i + lane;
-            v[i] = f < F4 ? *(const f32x4*)(Sh + 4 * f) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
-    }
-    amax = wave_max(amax);
-    int eS = 0;
-    if (amax > 0.0f) {
-        (void)frexpf(amax, &eS);
-        eS -= 14;
-    }
-#pragma unroll 1
-    for (int f0 = 0; f0 < F4; f0 += 256) {
-        f32x4 v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 64 * i + lane;
-            v[i] = f < F4 ? *(const f32x4*)(Sh + 4 * f) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 64 * i + lane;
-            if (f < F4) {
-                const int k = f / (D / 4), co = 4 * (f % (D / 4));
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    sth[st_off<DP>(st_row(co + j), k >> 3) + (k & 7)] =
-                        __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v[i][j], -eS));
-            }
-        }
-    }
-    if constexpr (DP > D) {  // the padding rows and columns (key or value channel >= d)
-#pragma unroll 1
-        for (int e = lane; e < DP * DP - D * D; e += 64) {
-            int k, co;
-            if (e < D * (DP - D)) {
-                k = e / (DP - D);
-                co = D + e % (DP - D);
-            } else {
-                k = D + (e - D * (DP - D)) / DP;
-                co = (e - D * (DP - D)) % DP;
-            }
-            sth[st_off<DP>(st_row(co), k >> 3) + (k & 7)] = 0;
-        }
-    }
-    for (int c = lane; c < DP; c += 64) zsh[c] = c < D ? zg[c] : 0.0f;
-    return eS;
-}
-
 // NPH: register slots for S, at least the heads per workgroup (a.nph)
 template <int D, bool ROPE, int NPH>
 __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel(ApplyArgs a) {
@@ -365,9 +300,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             if (threadIdx.x == 0) eSs[ph] = eS;
             uint16_t* sth = st16 + ph * C::DP * C::DP;
             auto put_st = [&](int k, int co, float sv) {
-                const int T = 2 * (co >> 5) + ((co >> 2) & 1);
-                const int m = (((co >> 3) & 3) << 2) | (co & 3);
-                sth[st_off<C::DP>(16 * T + m, k >> 3) + (k & 7)] =
+                sth[st_off<C::DP>(st_row(co), k >> 3) + (k & 7)] =
                     __builtin_bit_cast(uint16_t, (_Float16)ldexpf(sv, -eS));
             };
 #pragma unroll
