@@ -43,7 +43,8 @@
  *    after allocating it).  The counters carry the epoch of the call that
  *    last used them (an increasing per-process number), so no call needs to
  *    reset them and a call that never completed leaves nothing a later call
- *    misreads.  One workspace must not be used by two calls that may overlap
+ *    misreads (the epoch is a 32-bit count of calls in this process: such a
+ *    leftover could be misread only by a call 2^32 calls later).  One workspace must not be used by two calls that may overlap
  *    in time (two streams): they would race on it.  Calls check ws_bytes
  *    against their own plan and return LA_E_WORKSPACE if it is too small.
  *  - All pointers must be 16-byte aligned.  O must not overlap Q, K, V, S or
@@ -113,9 +114,11 @@ LA_API int la_state_reduce(const void* Q, const void* K, const void* V, void* O,
  * anything is launched (la_last_hip_error() then says how much they need).
  * The call allocates nothing and calls no allocating routine.  The first call
  * on a device looks up the array's address there and clears its counters on
- * `stream`.  Every call on one GPU shares that GPU's array: two calls that
- * may overlap in time (two streams, two threads) race on it and must not be
- * made; calls in order on one stream are safe. */
+ * `stream` (inside a stream capture that clear becomes part of the graph,
+ * which is harmless: the counters are zero between completed calls).  Every
+ * call on one GPU shares that GPU's array: two calls that may overlap in
+ * time (two streams, two threads) race on it and must not be made; calls in
+ * order on one stream are safe. */
 #define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 LA_API int la_state_reduce_noalloc(const void* Q, const void* K, const void* V, void* O,
                             float* S, float* z,
