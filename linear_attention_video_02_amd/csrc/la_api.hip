@@ -45,6 +45,7 @@ namespace {
 constexpr int kMaxPartials = 64;         // state workgroups per (batch, head), upper bound
 constexpr size_t kLdsLimit = 160 * 1024; // gfx950 LDS per workgroup
 constexpr size_t kFusedCombineBytes = 256 * 1024;  // per-head partials summed in the state launch
+constexpr int kOnePartTiles = 4;  // state pass: up to this many tiles a head, one workgroup per head
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -245,6 +246,10 @@ int plan_state(const LaGeom& g, int d, int dtype, Plan* out, int force_chunk = 0
     P = P < 1 ? 1 : (P > kMaxPartials ? kMaxPartials : P);
     const int max_p = ntok > 0 ? (ntok + tile - 1) / tile : 1;
     if (P > max_p) P = max_p;
+    // A sequence of at most kOnePartTiles tiles goes to one bf16 workgroup per
+    // head, which writes S and z itself: no partials, no second stage (text
+    // keys of cross-attention, short blocks).  Set state_wgs to override.
+    if (dtype == LA_BF16 && knob(K_STATE_WGS, -1) < 0 && max_p <= kOnePartTiles) P = 1;
     for (;;) {
         int chunk = ntok > 0 ? (ntok + P - 1) / P : tile;
         chunk = (int)align_up((size_t)chunk, tile);
@@ -331,6 +336,10 @@ int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
     if (P < 1) P = 1;
     const int max_p = ntok > 0 ? (ntok + tile - 1) / tile : 1;
     if (P > max_p) P = max_p;
+    // A sequence of at most kOnePartTiles tiles goes to one bf16 workgroup per
+    // head, which writes S and z itself: no partials, no second stage (text
+    // keys of cross-attention, short blocks).  Set state_wgs to override.
+    if (dtype == LA_BF16 && knob(K_STATE_WGS, -1) < 0 && max_p <= kOnePartTiles) P = 1;
     for (;;) {
         int chunk = ntok > 0 ? (ntok + P - 1) / P : tile;
         chunk = (int)align_up((size_t)chunk, tile);

@@ -375,7 +375,12 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     // ---- write this workgroup's partial (token group 0 holds the sums) ----
     // In the fused mode the partials are device-coherent stores (sc1: written
     // through to the agent-wide coherence point, not left in this XCD's L2).
+    // With one partial per head (fused, P = 1) it is the head's sum: S and z
+    // are written directly, formed as stage 2 forms them (0 + the partial,
+    // then the carry), and the counters are not touched.
     const bool fused = a.ticket != nullptr;
+    const bool direct = fused && a.P == 1;
+    const CombineArgs& cd = a.cmb;
     auto put = [&](float* dst, float v) {
         if (fused)
             __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -404,7 +409,16 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
         const BufRsrc pr16 = make_rsrc(part, (uint32_t)D * D * 4u);
         for (int f = tid; f < D * D / 4; f += C::THREADS) {
             const int row = f / (D / 4), c4 = f % (D / 4);
-            const u32x4 v = __builtin_bit_cast(u32x4, *(const f32x4*)(srow + row * SR + 4 * c4));
+            const f32x4 v4 = *(const f32x4*)(srow + row * SR + 4 * c4);
+            if (direct) {
+                const size_t o = (size_t)bh * D * D + 4 * f;  // row-major S: element 4f
+                f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f} + v4;
+                if (cd.S_carry) sum = *(const f32x4*)(cd.S_carry + o) + sum;
+                *(f32x4*)(cd.S_out + o) = sum;
+                if (cd.S_out2) *(f32x4*)(cd.S_out2 + o) = sum;
+                continue;
+            }
+            const u32x4 v = __builtin_bit_cast(u32x4, v4);
             if (fused)
                 buf_store16_dev(v, pr16, (uint32_t)f * 16u);
             else
@@ -428,9 +442,17 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
         float sum = 0.0f;
 #pragma unroll
         for (int w = 0; w < C::NW; ++w) sum += zr[w * C::DP + tid];
-        put(&part[D * D + tid], sum);
+        if (direct) {
+            const size_t o = (size_t)bh * D + tid;
+            float zs = 0.0f + sum;
+            if (cd.z_carry) zs = cd.z_carry[o] + zs;
+            cd.z_out[o] = zs;
+            if (cd.z_out2) cd.z_out2[o] = zs;
+        } else {
+            put(&part[D * D + tid], sum);
+        }
     }
-    if (!fused) return;
+    if (!fused || direct) return;
 
     // ---- fused stage 2.  Every thread waits until its partial stores have
     // completed (sc1 stores complete at the device coherence point), then one

@@ -48,14 +48,16 @@ def test_determinism_bidirectional(la):
 
 
 @pytest.mark.parametrize("d", [32, 64, 112, 128])
-def test_fused_combine_matches_separate_launch(la, d):
+@pytest.mark.parametrize("N,L", [(5000, 1000), (400, 200)])
+def test_fused_combine_matches_separate_launch(la, d, N, L):
     """The bf16 state kernel's in-kernel stage 2 (last workgroup of a head sums
-    the partials) and the separate combine launch give bitwise equal S and z,
-    also with a carry (block-causal), over repeated calls on one workspace."""
+    the partials; with a short sequence, one workgroup per head writing the
+    sums directly) and the separate combine launch give bitwise equal S and
+    z, also with a carry (block-causal), over repeated calls on one workspace."""
     import torch
-    _, (tq, tk, tv) = _inputs(2, 6, 5000, d, "bf16", 17)
+    _, (tq, tk, tv) = _inputs(2, 6, N, d, "bf16", 17)
     grid = (6, 23, 40)
-    qb, kb, vb = (t[:, :, 1000:2000].contiguous() for t in (tq, tk, tv))
+    qb, kb, vb = (t[:, :, L:2 * L].contiguous() for t in (tq, tk, tv))
     res = {}
     for fused in (0, 1):
         runs = []
@@ -64,13 +66,13 @@ def test_fused_combine_matches_separate_launch(la, d):
                 S, z = la.state_reduce(tk, tv, grid)
                 Sc = S.clone() * 0.5
                 zc = z.clone() * 0.5
-                la.block_causal_step(qb, kb, vb, Sc, zc, 5000, grid, 1000, 1, commit=True)
+                la.block_causal_step(qb, kb, vb, Sc, zc, N, grid, L, 1, commit=True)
                 runs.append((S, z, Sc, zc))
             torch.cuda.synchronize()
         for r in runs[1:]:
             assert all(torch.equal(x, y) for x, y in zip(r, runs[0])), fused
         res[fused] = runs[0]
-    say(f"  d={d}: fused and separate stage 2 bitwise equal")
+    say(f"  d={d} N={N}: fused and separate stage 2 bitwise equal")
     assert all(torch.equal(x, y) for x, y in zip(res[0], res[1]))
 
 
