@@ -1,7 +1,8 @@
 """la_state_reduce_noalloc (static scratch, no workspace argument) against
 la_state_reduce with a caller's workspace: bitwise equal S and z on two calls
-in a row, the second on a smaller input, in the fused (bf16, small partials)
-and separate-combine (bf16 d = 112, fp32) stage-2 forms."""
+in a row, the second on a smaller input, in the fused (bf16, small partials),
+separate-combine (bf16 d = 112, fp32) and one-workgroup-per-head (short
+sequences) stage-2 forms."""
 import pytest
 
 from _gpu import say, upload
@@ -21,6 +22,8 @@ CASES = [  # (B, H, N, d, dtype, grid) first call, then a smaller second call
     ((2, 32, 6000, 64, "bf16", (6, 25, 40)), (1, 8, 2077, 64, "bf16", (3, 25, 40))),
     ((1, 6, 5000, 112, "bf16", (5, 25, 40)), (1, 2, 999, 112, "bf16", (1, 25, 40))),
     ((1, 4, 3000, 128, "fp32", (3, 25, 40)), (1, 1, 700, 32, "fp32", (1, 25, 40))),
+    # short sequences: one workgroup per head, no partials in the scratch
+    ((2, 8, 300, 64, "bf16", (1, 25, 40)), (1, 3, 77, 32, "bf16", (1, 25, 40))),
 ]
 
 
