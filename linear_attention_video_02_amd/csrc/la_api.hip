@@ -471,6 +471,7 @@ int run_state(const void* K, const void* V, float* S_out, float* z_out, float* S
     a.partial = (float*)((char*)ws + L.partial);
     a.chunk = pl.chunk;
     a.P = pl.P;
+    a.pslots = pl.P;
     a.g = g;
     a.ticket = fused ? (unsigned long long*)((char*)ws + L.ticket) : nullptr;
     a.epoch = next_epoch();
@@ -609,20 +610,27 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     if (rc != LA_OK) return rc;
     const WsLayout L = ws_layout(g.BH, d, ps.P);
     float* partial = (float*)((char*)ws + L.partial);
-    // 1. one partial state per chunk
+    // 1. one partial state per chunk.  Without a carry to return, no prefix
+    // needs the last chunk's sum (the scan of that chunk starts from the sum
+    // of the ones before it), so its partial is not computed: the prefix
+    // kernel then writes the exclusive prefixes as before, and only the
+    // total, which is not stored, would have used that slot.
     StateArgs sa;
     sa.K = K;
     sa.V = V;
     sa.partial = partial;
     sa.chunk = ps.chunk;
-    sa.P = ps.P;
+    sa.P = S_carry ? ps.P : ps.P - 1;
+    sa.pslots = ps.P;
     sa.g = g;
     sa.ticket = nullptr;  // partials only: the prefix kernel reads them
     sa.epoch = 0;
     KernelFn<StateArgs> sk = state_kernel(d, dtype, g.rope);
     if (half) sk = g.rope ? la_state_bf16_kernel<64, true, 512> : la_state_bf16_kernel<64, false, 512>;
-    rc = launch_kernel<StateArgs>(sk, dim3(ps.P * g.BH), ps.lds, st, sa, half ? 512 : state_threads(d, dtype));
-    if (rc != LA_OK) return rc;
+    if (sa.P > 0) {
+        rc = launch_kernel<StateArgs>(sk, dim3(sa.P * g.BH), ps.lds, st, sa, half ? 512 : state_threads(d, dtype));
+        if (rc != LA_OK) return rc;
+    }
     // 2. exclusive prefixes in place (+ carry), total -> carry
     PrefixArgs pa;
     pa.partial = partial;

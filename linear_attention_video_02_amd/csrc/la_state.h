@@ -39,9 +39,10 @@ struct CombineArgs {
 struct StateArgs {
     const void* K;
     const void* V;
-    float* partial;        // [BH][P][D*D + D]
+    float* partial;        // [BH][pslots][D*D + D]
     int chunk;             // tokens per workgroup
-    int P;                 // workgroups per (batch, head)
+    int P;                 // workgroups per (batch, head): chunks 0 .. P-1
+    int pslots;            // partial slots per (batch, head), >= P
     LaGeom g;
     // Stage 2 inside the bf16 kernel (ticket != null): the last workgroup of
     // a head to finish sums that head's partials (see the kernel's end).
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
             *dst = v;
     };
     constexpr int E = D * D + D;
-    float* part = a.partial + ((size_t)bh * a.P + p) * E;
+    float* part = a.partial + ((size_t)bh * a.pslots + p) * E;
     // The sums go to LDS as rows (stride SR floats), and every thread then
     // writes 16 contiguous bytes of the partial at a time (from the MFMA
     // layout directly, a lane would store single words, up to 64 a lane).
@@ -582,7 +583,7 @@ __global__ __launch_bounds__(256) void la_state_f32_kernel(StateArgs a) {
         }
     }
     constexpr int E = D * D + D;
-    float* part = a.partial + ((size_t)bh * a.P + p) * E;
+    float* part = a.partial + ((size_t)bh * a.pslots + p) * E;
 #pragma unroll
     for (int j = 0; j < C::NE; ++j) part[tid + 256 * j] = acc[j];
     if (tid < D) part[D * D + tid] = zacc;
