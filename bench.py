@@ -498,9 +498,16 @@ def main():
             n_tok = w["block"] if wlname == "720p60s" else w["N"]  # per launch: one block
             tensor_bytes = w["B"] * w["H"] * n_tok * w["d"] * 2
             if wlname == "tc720p5s":
-                # each kernel's own stream: the partials pass reads K, V; the scan
-                # reads Q, K, V and writes O (the path's minimum is 4 tensors)
-                algo = {"la_state_bf16_kernel": 2 * tensor_bytes, "la_causal_bf16_kernel": 4 * tensor_bytes}
+                # each kernel's own stream: the partial-state pass reads K and V of every
+                # chunk but each head's last (no carry is returned), the scan reads Q, K, V
+                # and writes O (the path's minimum is 4 tensors).  Chunks as the library
+                # plans them by default: P = 512 / (B H) per head, 128-token aligned.
+                P = max(1, min(64, 512 // (w["B"] * w["H"])))
+                chunk = -(-w["N"] // P)
+                chunk = -(-chunk // 128) * 128
+                last = w["N"] - (-(-w["N"] // chunk) - 1) * chunk
+                algo = {"la_state_bf16_kernel": 2 * tensor_bytes * (w["N"] - last) // w["N"],
+                        "la_causal_bf16_kernel": 4 * tensor_bytes}
         cmds_ = profile_commands(wlname)
         os.makedirs(args.out, exist_ok=True)
         if args.summarize_trace:
@@ -516,7 +523,7 @@ def main():
                           algo, wlname)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (got --gpus {args.gpus}); "
               "across GPUs the bidirectional path would shard by (batch, head), with no "
               "communication", file=sys.stderr)
         sys.exit(2)
