@@ -70,9 +70,10 @@ def profile_commands(workload):
     """The profiler runs whose summaries are committed (run from /tmp, with the
     repository at $REPO); the summaries are then written by --summarize-*."""
     wl = "" if workload == WORKLOAD else f" --workload {workload}"
+    noextra = " --no-extra" if workload == "overlap720p" else ""
     return {
         "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/la_prof/trace -o trace "
-                 f"-- python3 $REPO/bench.py{wl} --steps 50 --warmup 5 --no-cpu-baseline",
+                 f"-- python3 $REPO/bench.py{wl} --steps 50 --warmup 5 --no-cpu-baseline{noextra}",
         "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d /tmp/la_prof/fetch -o fetch "
                  f"-- python3 $REPO/bench.py{wl} --steps 10 --warmup 2 --prewarm-ms 0 --no-cpu-baseline",
         "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d /tmp/la_prof/write -o write "
@@ -232,6 +233,7 @@ class FenceFreeEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         self.stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.events = []
 
@@ -247,6 +249,12 @@ class FenceFreeEvents:
         rc = self.hip.hipEventRecord(ev, self.stream())
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def wait(self, stream, ev):
+        """Make `stream` (a torch stream) wait for `ev` (no host synchronisation)."""
+        rc = self.hip.hipStreamWaitEvent(self.ct.c_void_p(stream.cuda_stream), ev, 0)
+        if rc != 0:
+            raise RuntimeError(f"hipStreamWaitEvent failed ({rc})")
 
     def ms(self, a, b):
         out = self.ct.c_float()
@@ -287,6 +295,8 @@ WORKLOAD_TITLES = {
                  "keys/values, d=64, no RoPE)",
     "tc720p5s": "tc720p5s workload (token-causal: bf16, B=2 H=32 N=19320 d=64, RoPE)",
     "720p60s": "720p60s workload (block-causal: bf16, B=1 H=32 N=220800 in 10 blocks of 22080, d=64, RoPE)",
+    "overlap720p": "overlap720p diagnostic (the 720p5s step as its two batch elements on two streams, "
+                   "each one's state pass then its apply)",
     "tconv720p": "tconv720p workload (temporal convolution, bf16, one block of 24 frames x 920 "
                  "positions, D=2240, bias)",
 }
@@ -313,6 +323,44 @@ def summarize_trace(trace_dir, command, out_path, workload=WORKLOAD):
         if k in OUR_KERNELS or (k or "").startswith("hipBLASLt"):
             lines.append(f"| {k} | {st['Calls']} | {float(st['AverageNs']) / 1e3:.1f} | "
                          f"{float(st['MinNs']) / 1e3:.1f} | {float(st['MaxNs']) / 1e3:.1f} |")
+    if workload == "overlap720p":
+        # every step is 4 launches (state and apply of each batch element, two
+        # streams) between a fork and a join: consecutive groups of 4 by start
+        t = lambda r, k: int(r[k]) / 1e3
+        n = len(la) // 4
+        spans, busy, st_us, ap_us, conc = [], [], [], [], []
+        for i in range(n):
+            g = la[4 * i:4 * i + 4]
+            t0, t1 = min(t(r, "Start_Timestamp") for r in g), max(t(r, "End_Timestamp") for r in g)
+            spans.append(t1 - t0)
+            busy.append(sum(t(r, "End_Timestamp") - t(r, "Start_Timestamp") for r in g))
+            for r in g:
+                (st_us if _short(r["Kernel_Name"]) in STATE_KERNELS else ap_us).append(
+                    t(r, "End_Timestamp") - t(r, "Start_Timestamp"))
+            # time two launches of the step run at once: the two state passes, the two
+            # applies, and a state pass with the other group's apply
+            sts = [r for r in g if _short(r["Kernel_Name"]) in STATE_KERNELS]
+            aps = [r for r in g if _short(r["Kernel_Name"]) in APPLY_KERNELS]
+
+            def both(a_, b_):
+                return max(0.0, min(t(a_, "End_Timestamp"), t(b_, "End_Timestamp")) -
+                           max(t(a_, "Start_Timestamp"), t(b_, "Start_Timestamp")))
+            conc.append((both(*sts) if len(sts) == 2 else 0.0, both(*aps) if len(aps) == 2 else 0.0,
+                         sum(both(a_, b_) for a_ in sts for b_ in aps)))
+        if n:
+            lines += ["", f"From the trace, over {n} steps (4 launches each, two streams):", "",
+                      f"- step span (first launch start to last launch end): {sum(spans) / n:.1f} us",
+                      f"- sum of the 4 launch durations: {sum(busy) / n:.1f} us",
+                      f"- state kernel (half batch) average: {sum(st_us) / len(st_us):.1f} us; "
+                      f"apply (half batch) average: {sum(ap_us) / len(ap_us):.1f} us",
+                      f"- time two launches run at once, per step: the two state passes "
+                      f"{sum(c[0] for c in conc) / n:.1f} us, the two applies {sum(c[1] for c in conc) / n:.1f} us, "
+                      f"a state pass with an apply {sum(c[2] for c in conc) / n:.1f} us"]
+        with open(out_path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return steps
+
     # per pass, from the trace: state kernel start .. (combine end) .. last kernel's end,
     # the last kernel being the apply (or the causal scan in token-causal mode)
     t = lambda r, k: int(r[k]) / 1e3
@@ -456,8 +504,11 @@ def main():
                     help="before the warm-up steps, run untimed steps for this long so that the GPU "
                          "reaches its steady clock (from idle it needs tens of ms)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip a workload's extra measurements (library GEMM, stream comparisons)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b", "tconv720p", "sweep"],
+    ap.add_argument("--workload", default=WORKLOAD, choices=[WORKLOAD, "cross720p", "720p60s", "tc720p5s", "sana2b", "tconv720p", "sweep",
+                             "overlap720p"],
                     help="default: the headline 720p-5s bidirectional step")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record per-kernel events on every n-th timed step (each event costs ~2 us)")
@@ -494,7 +545,7 @@ def main():
             algo = {"la_state_bf16_kernel": 2 * tkv, "la_apply_bf16_kernel": 2 * tensor_bytes}
         else:
             from linear_attention_video_02_amd.inputs import WORKLOADS
-            w = WORKLOADS["720p5s" if wlname == "tc720p5s" else wlname]
+            w = WORKLOADS["720p5s" if wlname in ("tc720p5s", "overlap720p") else wlname]
             n_tok = w["block"] if wlname == "720p60s" else w["N"]  # per launch: one block
             tensor_bytes = w["B"] * w["H"] * n_tok * w["d"] * 2
             if wlname == "tc720p5s":
@@ -653,7 +704,7 @@ def main():
         "wall_s": wall,
         "src_hash": src_hash,
     }
-    if "extra" in wl:
+    if "extra" in wl and not args.no_extra:
         out.update(wl["extra"](tev_factory=FenceFreeEvents))
     if not args.no_cpu_baseline and "cpu_baseline" in wl:
         out["cpu_baseline"] = wl["cpu_baseline"](args.cpu_budget)
@@ -847,6 +898,88 @@ def setup_workload(name, la, dev):
                        "input_sets": len(sets)},
             "groups": [("state", STATE_KERNELS, 2 * tkv), ("apply", APPLY_KERNELS, 2 * tq)],
             "copy_pairs": [(s[0], s[3]) for s in sets],
+        }
+
+    if name == "overlap720p":
+        # Diagnostic, not the headline: the 720p-5s step split into two head
+        # groups (its two batch elements), each group's state pass then its
+        # apply on a stream of its own, so that one group's pass can drain
+        # while the other's ramps up.  The comparison figures in the JSON line
+        # time the whole batch on one stream and the two groups on one stream.
+        spec = WORKLOADS["720p5s"]
+        B, H, N, d, grid, eps = spec["B"], spec["H"], spec["N"], spec["d"], spec["grid"], spec["eps"]
+        q, k, v = make_qkv_device(B, H, N, d, "bf16", spec["seed"], dev)
+        tb = q.numel() * q.element_size()
+        base = rotating((q, k, v), n_sets_for(4 * tb))
+        sets = [(qi, ki, vi, torch.empty_like(q), torch.empty((B, H, d, d), dtype=torch.float32, device=dev),
+                 torch.empty((B, H, d), dtype=torch.float32, device=dev)) for (qi, ki, vi) in base]
+        main = torch.cuda.current_stream()
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+        ws_half = [torch.zeros(la.workspace_bytes(1, H, N, d, grid), dtype=torch.uint8, device=dev)
+                   for _ in streams]
+        ws_all = la.workspace(B, H, N, d, dev, grid=grid)
+        pool = []
+
+        def group(h, i, ws):
+            qi, ki, vi, oi, S, z = sets[i % len(sets)]
+            sl = slice(h, h + 1)
+            la.state_reduce(ki[sl], vi[sl], grid, S=S[sl], z=z[sl], ws=ws)
+            la.apply(qi[sl], S[sl], z[sl], grid, eps, out=oi[sl])
+
+        def step(i, ev, tev):
+            if not pool:
+                pool.extend(tev.new() for _ in range(3))
+            if ev is not None:
+                tev.record(ev[0])
+            tev.record(pool[0])
+            for h, st in enumerate(streams):
+                tev.wait(st, pool[0])
+                with torch.cuda.stream(st):
+                    group(h, i, ws_half[h])
+                    tev.record(pool[1 + h])
+            tev.wait(main, pool[1])
+            tev.wait(main, pool[2])
+            if ev is not None:
+                tev.record(ev[1])
+
+        def compare(tev_factory):
+            te = tev_factory()
+
+            def per_step_us(fn, n=100):
+                for i in range(10):
+                    fn(i)
+                torch.cuda.synchronize()
+                e0, e1 = te.new(), te.new()
+                te.record(e0)
+                for i in range(n):
+                    fn(i)
+                te.record(e1)
+                torch.cuda.synchronize()
+                return te.ms(e0, e1) / n * 1e3
+
+            def whole(i):
+                qi, ki, vi, oi, S, z = sets[i % len(sets)]
+                la.state_reduce(ki, vi, grid, S=S, z=z, ws=ws_all)
+                la.apply(qi, S, z, grid, eps, out=oi)
+
+            def two_on_one(i):
+                group(0, i, ws_half[0])
+                group(1, i, ws_half[0])
+
+            out = {"compare_us": {"whole_batch_one_stream": per_step_us(whole),
+                                  "two_groups_one_stream": per_step_us(two_on_one)}}
+            te.close()
+            return out
+
+        return {
+            "metric": METRIC + " (diagnostic: two streams)",
+            "step": step, "tokens_per_step": B * N, "step_bytes": 4 * tb,
+            "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "eps": eps,
+                       "streams": 2, "input_sets": len(sets)},
+            # one group: the whole step across both streams (fork to join)
+            "groups": [("step_two_streams", STATE_KERNELS + APPLY_KERNELS, 4 * tb)],
+            "copy_pairs": [(s_[0], s_[3]) for s_ in sets],
+            "extra": compare,
         }
 
     if name == "tc720p5s":
