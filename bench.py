@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -518,8 +519,15 @@ def main():
                     help="write the HBM-traffic summary of rocprofv3 FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--summarize-counters", nargs="+", metavar="WORKLOAD=DIR",
                     help="write the MFMA-utilisation summary of rocprofv3 --pmc runs of " + MFMA_COUNTERS)
+    ap.add_argument("--summarize-sweep", nargs="+", metavar=("JSON", "TRACE_DIR"),
+                    help="write profiles/sweep_scaling.md from a --workload sweep JSON line (and its trace)")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"), help="where summaries go")
     args = ap.parse_args()
+    if args.summarize_sweep:
+        os.makedirs(args.out, exist_ok=True)
+        summarize_sweep(args.summarize_sweep[0], args.summarize_sweep[1] if len(args.summarize_sweep) > 1 else None,
+                        os.path.join(args.out, "sweep_scaling.md"))
+        return
     if args.summarize_counters:
         os.makedirs(args.out, exist_ok=True)
         summarize_counters(dict(x.split("=", 1) for x in args.summarize_counters),
@@ -786,6 +794,69 @@ def run_sweep(args):
         "sweep": points, "linearity": linear,
     }
     print(json.dumps(out), flush=True)
+
+
+SWEEP_TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/la_prof/sweep "
+                   "-o tr -- python3 $REPO/bench.py --workload sweep")
+
+
+def summarize_sweep(json_path, trace_dir, out_path):
+    """profiles/sweep_scaling.md from a `bench.py --workload sweep` JSON line and,
+    if given, a rocprofv3 kernel trace of the same command (per-kernel rates at
+    the largest N: the sweep runs its points in order, so the last launches of
+    each kernel instance belong to the largest N of that head size)."""
+    import csv
+    d_ = json.loads(open(json_path).read().strip().splitlines()[-1])
+    pts, lin = d_["sweep"], d_["linearity"]
+    lines = ["# d x N sweep: linear scaling of the bidirectional step", "",
+             "Commands (repository root, one MI355X):", "", "```",
+             "python3 bench.py --workload sweep > /tmp/la_prof/sweep.json"]
+    if trace_dir:
+        lines.append(SWEEP_TRACE_CMD)
+    lines += ["python3 bench.py --summarize-sweep /tmp/la_prof/sweep.json" +
+              (" /tmp/la_prof/sweep" if trace_dir else ""), "```", "",
+              "B = 1, H = 32, bf16, grid ceil(N/920) x 23 x 40 with RoPE; one step = la_state_reduce + "
+              "la_apply, inputs rotating over >= 2 GiB of independent sets, each point warmed for >= 50 ms; "
+              "HIP events on the launch stream.", "",
+              "| d | N | us per step | tokens/s | GB/s (Q, K, V, O) |", "|---|---|---|---|---|"]
+    for p_ in pts:
+        lines.append(f"| {p_['d']} | {p_['N']} | {p_['us']:.1f} | {p_['tokens_per_s'] / 1e6:.1f}M | "
+                     f"{p_['GBps']:.0f} |")
+    lines += ["", "Least-squares fit per head size, t = a + b * (N / 1e6) (Table 1's O(N) claim):", "",
+              "| d | a (us) | b (us per M tokens) | R^2 | us per M tokens at the two largest N |",
+              "|---|---|---|---|---|"]
+    for d, v in lin.items():
+        a_, b_ = v["fit_us"]
+        t1, t2 = v["us_per_Mtoken_largest_two"]
+        lines.append(f"| {d} | {a_:.1f} | {b_:.0f} | {v['r2']:.5f} | {t1:.0f} / {t2:.0f} |")
+    lines += ["", "The intercept is the fixed cost of the two launches and their set-up; the slope doubles "
+              "with d (bytes per token are proportional to d), and the time per token keeps falling toward "
+              "the slope as N grows."]
+    if trace_dir:
+        rows = list(csv.DictReader(open(_find(trace_dir, "kernel_trace.csv"))))
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        by = {}
+        for r in rows:
+            k = _short(r["Kernel_Name"])
+            if k in STATE_KERNELS + APPLY_KERNELS:
+                m = re.search(r"<(\d+)", r["Kernel_Name"])
+                dd = int(m.group(1)) if m else 0
+                by.setdefault((k, dd), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        nmax = max(p_["N"] for p_ in pts)
+        lines += ["", f"Per kernel at N = {nmax} (mean of the last 20 launches of each kernel of that head size):",
+                  "", "| d | state kernel | apply kernel | bytes per pass | state | apply |", "|---|---|---|---|---|---|"]
+        for d in sorted({p_["d"] for p_ in pts}):
+            st = by.get((STATE_KERNELS[0], d), [])[-20:]
+            ap = by.get((APPLY_KERNELS[0], d), [])[-20:]
+            if not st or not ap:
+                continue
+            nb = 2 * 32 * nmax * d * 2
+            ts, ta = sum(st) / len(st), sum(ap) / len(ap)
+            lines.append(f"| {d} | {ts:.1f} us | {ta:.1f} us | {nb / 1e6:.0f} MB | {nb / ts / 1e6:.1f} TB/s | "
+                         f"{nb / ta / 1e6:.1f} TB/s |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def setup_workload(name, la, dev):
