@@ -281,10 +281,15 @@ struct ApplyPlan {
     size_t lds;
 };
 
-// Heads per bf16 apply workgroup unless the apply_heads knob says otherwise:
-// at d <= 64 two halve the per-workgroup setup against one, more cost S
-// registers and setup latency than they save; past 64 channels one.
-int default_apply_heads(int d) { return d <= 64 ? 2 : 1; }
+// Heads per bf16 apply workgroup unless the apply_heads knob says otherwise.
+// Measured (d = 64): the apply runs best with about 8 workgroups per slot of
+// heads; one head per workgroup gets there when the target gives each head 8
+// or more, else (64 heads at 720p-5s: 4 a head) two heads per workgroup do.
+// Past 64 channels one (S^T of two heads fills the LDS).
+int default_apply_heads(int d, int BH, int target) {
+    if (d > 64) return 1;
+    return target / BH >= 8 ? 1 : 2;
+}
 
 int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
     const int target = knob(K_APPLY_WGS, dtype == LA_BF16 ? 256 : 1024);
@@ -298,7 +303,7 @@ int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
         const long long want = (long long)BH * pmax < target ? (long long)BH * pmax : target;
         const size_t table = table_entries(g, ntok) * 8;
         const int forced = knob(K_APPLY_HEADS, 0);
-        const int first = forced > 0 ? forced : (maxph < default_apply_heads(d) ? maxph : default_apply_heads(d));
+        const int first = forced > 0 ? forced : (maxph < default_apply_heads(d, BH, target) ? maxph : default_apply_heads(d, BH, target));
         for (int nph = first; nph >= 1; --nph) {
             if (nph > maxph || BH % nph != 0) {
                 if (forced > 0) break;
