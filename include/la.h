@@ -218,7 +218,7 @@ LA_API int la_stream_copy(const void* src, void* dst, size_t bytes, void* stream
  *   "apply_heads"      1..8: heads per apply slot (if they divide B*H and fit)
  *   "tc_state_threads" 512 / 1024: token-causal partial-state workgroups
  *   "tconv_gm", "tconv_gn"  temporal-convolution tile-order group (1..64)
- *   "apply_spread"     0: a head's apply workgroups on as few XCDs as possible
+ *   "apply_spread"     0 / 1: a slot's apply workgroups on as few XCDs as possible / on all 8
  * Returns LA_OK, LA_E_NULLPTR, LA_E_UNSUPPORTED (unknown name) or
  * LA_E_SHAPE (value out of range).  Not thread-safe: set knobs while no
  * other thread calls the library.  Results are correct under every value. */

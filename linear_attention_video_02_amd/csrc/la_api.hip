@@ -328,8 +328,11 @@ int plan_apply(const LaGeom& g, int d, int dtype, ApplyPlan* out) {
             out->P = P;
             out->nph = nph;
             out->hs = hs;
-            // a slot's workgroups on all 8 XCDs (workgroup i runs on XCD i % 8)
-            out->spread = P % 8 == 0 && knob(K_APPLY_SPREAD, 1) != 0;
+            // a slot's workgroups on all 8 XCDs (workgroup i runs on XCD i % 8),
+            // or on as few as possible.  Measured: at d <= 64 few XCDs per slot are
+            // faster (N = 65,536, 32 heads: 99 against 109 us; 720p-5s 63.2
+            // against 64.3 us), at d = 128 all eight slightly (231 against 235 us).
+            out->spread = P % 8 == 0 && knob(K_APPLY_SPREAD, d > 64 ? 1 : 0) != 0;
             out->chunk = ntok;
             out->grid = hs * P;
             out->lds = lds;
