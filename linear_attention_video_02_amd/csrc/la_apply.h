@@ -77,6 +77,12 @@ struct ApplyBf16Cfg {
     // d >= 112: the MFMA A fragments are read from the LDS copy of S^T per
     // k-step (128 x 128 fp16 in registers would take 128 a lane)
     static constexpr bool SLDS = DP > 64;
+    // d = 112: the last k-step covers channels 96..111 only, on the K = 16
+    // MFMA (v_mfma_f32_16x16x16_f16): no work and no LDS reads on the key
+    // channels 112..127, so the S^T copy needs no zeroed padding columns.
+    // (Its rows 112..127 -- value channels past d -- feed only outputs that
+    // are never stored.)
+    static constexpr bool HALF = D == 112;
     // heads per workgroup at most (their S^T copies share the LDS)
     static constexpr int MAXPH = DP > 64 ? 2 : 8;
     // d = 64: Q and O pass through a per-wave LDS tile so that every global
@@ -228,8 +234,14 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         for (int r = 0; r < C::GR; ++r) {
             const int tl = u0 + 16 * r + n;
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks)
-                q[r][ks] = buf_load16(Qr, (uint32_t)(tl * D + 32 * ks + 8 * g) * 2u);
+            for (int ks = 0; ks < C::KS; ++ks) {
+                if (C::HALF && ks == C::KS - 1) {  // channels 32 ks + 4 g .. +3
+                    const u32x2v h = buf_load8(Qr, (uint32_t)(tl * D + 32 * ks + 4 * g) * 2u);
+                    q[r][ks] = u32x4{h[0], h[1], 0u, 0u};
+                } else {
+                    q[r][ks] = buf_load16(Qr, (uint32_t)(tl * D + 32 * ks + 8 * g) * 2u);
+                }
+            }
         }
     };
     // first DEPTH units of each wave: fixed positions of phase 0's queue (the
@@ -262,7 +274,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                pr[ks][i] = pair_ref((C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g + i : 0, nt, a.g);
+                pr[ks][i] = pair_ref(C::HALF && ks == C::KS - 1 ? (i < 2 ? 16 * ks + 2 * g + i : 0)
+                                     : (C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g + i : 0, nt, a.g);
     }
 
     // each head's largest |S|: per thread, per wave, then over the waves
@@ -312,8 +325,9 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     for (int j = 0; j < 4; ++j) put_st(k, co + j, sraw[ph][i][j]);
                 }
             }
-            // the padding rows and columns (key or value channel >= d)
-            for (int e = threadIdx.x; e < C::DP * C::DP - D * D; e += C::THREADS) {
+            // the padding rows and columns (key or value channel >= d); with the
+            // half last k-step no padding entry is ever read into a stored output
+            for (int e = threadIdx.x; !C::HALF && e < C::DP * C::DP - D * D; e += C::THREADS) {
                 int k, co;
                 if (e < D * (C::DP - D)) {
                     k = e / (C::DP - D);
@@ -426,7 +440,8 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 uint32_t m16 = 0;
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
-                    const bool live = C::DP == D || 32 * ks + 8 * g < D;
+                    // (the half last k-step holds 4 live channels and 4 zeros)
+                    const bool live = C::DP == D || (C::HALF && ks == C::KS - 1) || 32 * ks + 8 * g < D;
                     const uint32_t mk = live ? max_relu_bits8(qc[r][ks]) : 0u;
                     m16 = mk > m16 ? mk : m16;
                 }
@@ -442,6 +457,40 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 // one 32-channel k-step at a time: its B fragments, then its MFMAs
 #pragma unroll
                 for (int ks = 0; ks < C::KS; ++ks) {
+                    if (C::HALF && ks == C::KS - 1) {
+                        // channels 32 ks + 4 g .. +3 on the K = 16 MFMA
+                        float x[4];
+                        uint32_t w2[2];
+#pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            w2[i] = relu_bf16x2(qc[r][ks][i]);
+                            x[2 * i] = bf_lo(w2[i]);
+                            x[2 * i + 1] = bf_hi(w2[i]);
+                        }
+                        const float4 za = *(const float4*)(zh + 32 * ks + 4 * g);
+                        den = fmaf(x[0], za.x, den); den = fmaf(x[1], za.y, den);
+                        den = fmaf(x[2], za.z, den); den = fmaf(x[3], za.w, den);
+                        if (scaled) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) x[e] = ldexpf(x[e], sc);
+                        }
+                        if (ROPE) {
+#pragma unroll
+                            for (int i = 0; i < 2; ++i)
+                                rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[ks][i], ps)]);
+                        }
+                        typedef __attribute__((ext_vector_type(4))) _Float16 f16x4v;
+                        const f16x4v Bq4 = __builtin_bit_cast(
+                            f16x4v, u32x2v{pack_f16(x[0], x[1]), pack_f16(x[2], x[3])});
+#pragma unroll
+                        for (int T = 0; T < C::NT; ++T) {
+                            const f16x4v A4 = *(const f16x4v*)(sth + st_off<C::DP>(16 * T + n, 4 * ks + (g >> 1)) +
+                                                               4 * (g & 1));
+                            acc[T] = __builtin_amdgcn_mfma_f32_16x16x16f16(A4, Bq4, acc[T], 0, 0, 0);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        continue;
+                    }
                     const bool live = C::DP == D || 32 * ks + 8 * g < D;
                     u32x4 w4;
                     float x[8];

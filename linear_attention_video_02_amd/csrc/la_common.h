@@ -80,6 +80,11 @@ __device__ __forceinline__ u32x4 buf_load16(BufRsrc r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2v;
+__device__ __forceinline__ u32x2v buf_load8(BufRsrc r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
 __device__ __forceinline__ void buf_store16(u32x4 v, BufRsrc r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
