@@ -91,13 +91,25 @@ struct ApplyBf16Cfg {
     static constexpr bool STG = D == 64;
     static constexpr int RPI = 8;                          // rows per staged load / store
     static constexpr int NI = UNIT / RPI;                  // staged loads per unit (= GR * KS)
-    static constexpr int STGBYTES = STG ? NW * 2 * UNIT * D * 2 : 0;
+    // d >= 112: a 16-token unit of Q (or O) is one contiguous block of UB
+    // bytes, moved by NIW instructions of 16 bytes a lane (1 KB each) through
+    // a per-wave LDS tile of UNIT rows x DP channels (the MFMA operand layout
+    // would touch 16 rows per instruction, 64 bytes of each, and at d = 112
+    // those pieces straddle 128-byte lines).  Lanes past the unit's end (the
+    // last 512 bytes of the fourth instruction at d = 112) load and store out
+    // of range and park in the tile's padding chunks.
+    static constexpr bool STW = D >= 112;
+    static constexpr int UB = UNIT * D * 2;
+    static constexpr int NIW = (UB + 1023) / 1024;
+    static constexpr int STGBYTES = STG ? NW * 2 * UNIT * D * 2 : STW ? NW * UNIT * DP * 2 : 0;
     static constexpr int SHEAD = DP * DP * 2;              // fp16 S^T of one head
     static constexpr int ZHEAD = DP * 4;                   // z of one head (zero above d)
     // LDS: staging tiles, then nph x (S^T, z), then the RoPE table
     static constexpr int FIXED = STGBYTES;
     static constexpr int PERHEAD = SHEAD + ZHEAD;
     static_assert(!STG || NI == GR * KS, "staged unit = register ring slot");
+    static_assert(!STW || (GR == 1 && NIW == KS), "whole-unit staging = register ring slot");
+    static_assert(!STW || (NIW * 1024 - UB) / 16 <= UNIT * (DP - D) / 8, "parking slots");
 };
 
 // Element offset of row r, 16-byte chunk c of a wave's staging tile
@@ -106,6 +118,14 @@ struct ApplyBf16Cfg {
 // (16 consecutive rows at one chunk) free of bank conflicts.
 __device__ __forceinline__ int stg_off(int r, int c) {
     return r * 64 + ((c ^ ((r ^ (r >> 3)) & 7)) << 3);
+}
+
+// Element offset of row r (< 16), 16-byte chunk c of a wave's whole-unit tile
+// ([16][DP] bf16, d >= 112): chunk c of row r sits at c ^ r, so the 16 rows
+// read at one chunk (MFMA operand layout) cover all banks once.
+template <int DP>
+__device__ __forceinline__ int stw_off(int r, int c) {
+    return r * DP + ((c ^ r) << 3);
 }
 
 // Element offset of S^T row pr (= 16 T + m, see below), 16-byte chunk c, in
@@ -219,10 +239,32 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             ++wph;
         }
     };
+    // whole-unit staging: each lane's tile slot for staged instruction i
+    int woff[C::STW ? C::NIW : 1];
+    bool wok[C::STW ? C::NIW : 1];
+    if (C::STW) {
+#pragma unroll
+        for (int i = 0; i < C::NIW; ++i) {
+            const int b = 1024 * i + 16 * lane;
+            wok[i] = b < C::UB;
+            if (wok[i]) {
+                woff[i] = stw_off<C::DP>(b / (2 * D), (b % (2 * D)) / 16);
+            } else {  // a padding chunk (channel >= d) of some row
+                const int k = (b - C::UB) / 16, pads = (C::DP - D) / 8;
+                woff[i] = stw_off<C::DP>(k / pads, D / 8 + k % pads);
+            }
+        }
+    }
     u32x4 qr[C::DEPTH][C::GR][C::KS];
     auto load_unit = [&](u32x4 (&q)[C::GR][C::KS], int2 u) {
         const BufRsrc Qr = q_rsrc(u.x < nph ? head_of(u.x) : slot);
         const int u0 = u.x < nph ? u.y : len;  // none: a read past the end (zeros)
+        if (C::STW) {  // byte 1024 i + 16 lane of the unit (past the unit: out of range, zeros)
+#pragma unroll
+            for (int i = 0; i < C::NIW; ++i)
+                q[0][i] = buf_load16(Qr, wok[i] ? (uint32_t)u0 * (2u * D) + (uint32_t)(1024 * i + 16 * lane) : chunk_bytes);
+            return;
+        }
         if (C::STG) {  // whole rows: lane -> row RPI*i + lane/8, 16-byte chunk lane%8
 #pragma unroll
             for (int i = 0; i < C::NI; ++i)
@@ -398,9 +440,28 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             if (uc.x != cur) use_head(uc.x);
             const BufRsrc Or = o_rsrc(head_of(uc.x));
             u32x4 qc[C::GR][C::KS];
-            uint16_t* wq = stg + wave * (2 * C::UNIT * D);  // this wave's Q tile, then its O tile
-            uint16_t* wo = wq + C::UNIT * D;
-            if (C::STG) {
+            // this wave's Q tile, then its O tile (d >= 112: one tile, O over Q)
+            uint16_t* wq = stg + wave * (C::STG ? 2 * C::UNIT * D : C::UNIT * C::DP);
+            uint16_t* wo = C::STG ? wq + C::UNIT * D : wq;
+            if (C::STW) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int i = 0; i < C::NIW; ++i) *(u32x4*)(wq + woff[i]) = qr[s][0][i];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int ks = 0; ks < C::KS; ++ks) {
+                    if (C::HALF && ks == C::KS - 1) {  // channels 32 ks + 4 g .. +3
+                        const u32x2v h = *(const u32x2v*)(wq + stw_off<C::DP>(n, 4 * ks + (g >> 1)) + 4 * (g & 1));
+                        qc[0][ks] = u32x4{h[0], h[1], 0u, 0u};
+                    } else {
+                        qc[0][ks] = *(const u32x4*)(wq + stw_off<C::DP>(n, 4 * ks + g));
+                    }
+                }
+            } else if (C::STG) {
                 // rows into LDS, then each lane reads its MFMA operand (token n, 8 channels)
 #pragma unroll
                 for (int i = 0; i < C::NI; ++i)
@@ -552,11 +613,22 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     o[1] = pack_bf16(acc[2 * sp][2] * inv, acc[2 * sp][3] * inv);
                     o[2] = pack_bf16(acc[2 * sp + 1][0] * inv, acc[2 * sp + 1][1] * inv);
                     o[3] = pack_bf16(acc[2 * sp + 1][2] * inv, acc[2 * sp + 1][3] * inv);
-                    if (C::STG)
+                    if (C::STW)  // (channels past d land in the row's padding chunks)
+                        *(u32x4*)(wo + stw_off<C::DP>(n, 4 * sp + g)) = o;
+                    else if (C::STG)
                         *(u32x4*)(wo + stg_off(16 * r + n, 4 * sp + g)) = o;
                     else if (C::DP == D || 32 * sp + 8 * g < D)  // part-lines: let L2 merge them
                         buf_store16(o, Or, (uint32_t)(tl * D + 32 * sp + 8 * g) * 2u);
                 }
+            }
+            if (C::STW) {  // the unit out of LDS, 1 KB per streaming store instruction
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int i = 0; i < C::NIW; ++i)
+                    buf_store16_stream(*(const u32x4*)(wo + woff[i]), Or,
+                                       wok[i] ? (uint32_t)u0 * (2u * D) + (uint32_t)(1024 * i + 16 * lane) : chunk_bytes);
             }
             if (C::STG) {  // whole rows out of LDS, one streaming store per 8 rows
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
