@@ -319,6 +319,63 @@ __device__ __forceinline__ int pair_entry(PairRef r, Pos3 p) {
     return (r >> 2) + p.t + dh + dw;
 }
 
+// Byte offsets of global token n's table rows: 8 (t - t_lo) pt, 8 h ph, 8 w pw
+// (token_pos with the float2 entry size folded into the multipliers).
+__device__ __forceinline__ Pos3 token_pos8(uint32_t n, int t_lo, const LaGeom& g) {
+    uint32_t t = fdiv(n, g.div_hw);
+    uint32_t r = n - __umul24(t, (uint32_t)(g.gh * g.gw));
+    uint32_t h = fdiv(r, g.div_w);
+    Pos3 p;
+    p.t = __mul24((int)t - t_lo, 8 * g.pt);
+    p.h = __mul24((int)h, 8 * g.ph);
+    p.w = __mul24((int)(r - __umul24(h, (uint32_t)g.gw)), 8 * g.pw);
+    return p;
+}
+
+// The table entries of four consecutive pairs p0 .. p0 + 3 (8 channels of
+// one row, one lane).  Every axis has at least 3 pairs (P / 3 >= 3 from
+// d = 18 on), so the four lie on at most two axes: A, pair 0's, and B, pair
+// 3's.  For a token the lane forms the two row bases once,
+//   ra = 8 (base of pair 0) + row offset of A,
+//   rb = 8 (base of B's first pair k - k) + row offset of B,
+// and pair i's entry is at byte (pair i on B ? rb : ra) + 8 i of the table:
+// one select a pair, the + 8 i an immediate offset of the LDS read.
+struct Rope4 {
+    int xa, xb;            // 8 (base of pair 0), 8 (base of pair k - k)
+    bool ah, aw, bh, bw;   // A / B is the h / the w axis
+    bool onb1, onb2, onb3; // pair i (1..3) lies on B, B != A
+};
+
+__device__ __forceinline__ Rope4 rope4_make(int p0, int nt, const LaGeom& g) {
+    auto axis = [&](int p) { return p < g.pt ? 0 : (p < g.pt + g.ph ? 1 : 2); };
+    auto base = [&](int p) {
+        const int a = axis(p);
+        return a == 0 ? p : (a == 1 ? nt * g.pt + (p - g.pt) : nt * g.pt + g.gh * g.ph + (p - g.pt - g.ph));
+    };
+    const int A = axis(p0), B = axis(p0 + 3);
+    int k = 3;
+    while (k > 1 && axis(p0 + k - 1) == B) --k;  // first pair on B (k = 3 if only pair 3)
+    Rope4 r;
+    r.xa = 8 * base(p0);
+    r.xb = A == B ? r.xa : 8 * (base(p0 + k) - k);
+    r.ah = A == 1;
+    r.aw = A == 2;
+    r.bh = B == 1;
+    r.bw = B == 2;
+    r.onb1 = axis(p0 + 1) != A;
+    r.onb2 = axis(p0 + 2) != A;
+    r.onb3 = axis(p0 + 3) != A;
+    return r;
+}
+
+// the two row bases of a token (p8 from token_pos8; passed by value: see
+// pair_entry)
+__device__ __forceinline__ int2 rope4_rows(Rope4 r, Pos3 p8) {
+    const int oa = r.aw ? p8.w : (r.ah ? p8.h : p8.t);
+    const int ob = r.bw ? p8.w : (r.bh ? p8.h : p8.t);
+    return make_int2(oa + r.xa, ob + r.xb);
+}
+
 // rotate (x0, x1) by the angle whose (cos, sin) is cs
 __device__ __forceinline__ void rotate(float& x0, float& x1, float2 cs) {
     float a = x0 * cs.x - x1 * cs.y;

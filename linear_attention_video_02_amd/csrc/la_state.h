@@ -196,8 +196,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     const BufRsrc Kr = make_rsrc((const uint16_t*)a.K + chunk_off, chunk_bytes);
     const BufRsrc Vr = make_rsrc((const uint16_t*)a.V + chunk_off, chunk_bytes);
     const int cc = tid % C::CH, trow = tid / C::CH;
-    // lanes past the real channels (d = 112 only) load a neighbour's bytes
-    // unconditionally (keeps the load count uniform) and stage zeros
+    // lanes past the real channels (d = 112 only) load out of range: zeros
     const bool live = C::DP == D || 8 * cc < D;
 
     // ring of DEPTH tiles in registers: tile i lives in slot i % DEPTH
@@ -205,7 +204,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     auto load_tile = [&](u32x4 (&kk)[C::LP], u32x4 (&vv)[C::LP], int tile) {
 #pragma unroll
         for (int j = 0; j < C::LP; ++j) {
-            const uint32_t off = (uint32_t)((tile * C::TT + trow + j * C::ROWS) * D + 8 * cc) * 2u;
+            const uint32_t off = live ? (uint32_t)((tile * C::TT + trow + j * C::ROWS) * D + 8 * cc) * 2u : chunk_bytes;
             kk[j] = buf_load16(Kr, off);
             vv[j] = buf_load16(Vr, off);
         }
@@ -214,14 +213,13 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     for (int s = 0; s < C::DEPTH; ++s) load_tile(kr[s], vr[s], s);
 
     int t_lo = 0;
-    PairRef pr[4];
+    Rope4 r4{};
     if (ROPE) {
         const int cl = c1 > c0 ? c1 - 1 : c0;
         t_lo = (int)fdiv((uint32_t)(a.g.n_offset + c0), a.g.div_hw);
         int nt = (int)fdiv((uint32_t)(a.g.n_offset + cl), a.g.div_hw) - t_lo + 1;
         build_rope_table(tab, t_lo, nt, a.g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = pair_ref(live ? 4 * cc + i : 0, nt, a.g);
+        r4 = rope4_make(live ? 4 * cc : 0, nt, a.g);
     }
 
     float zp[8];
@@ -239,7 +237,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
             float x[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t w = live ? relu_bf16x2(kr[s][j][i]) : 0u;
+                const uint32_t w = relu_bf16x2(kr[s][j][i]);
                 x[2 * i] = bf_lo(w);
                 x[2 * i + 1] = bf_hi(w);
             }
@@ -247,9 +245,13 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
             for (int e = 0; e < 8; ++e) zp[e] += x[e];
             if (ROPE) {
                 const int tok = min(c0 + tile * C::TT + tl, c1 - 1);
-                const Pos3 ps = token_pos((uint32_t)(a.g.n_offset + tok), t_lo, a.g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[i], ps)]);
+                const int2 rr = rope4_rows(r4, token_pos8((uint32_t)(a.g.n_offset + tok), t_lo, a.g));
+                const char* pa = (const char*)tab + rr.x;
+                const char* pb = (const char*)tab + rr.y;
+                rotate(x[0], x[1], *(const float2*)pa);
+                rotate(x[2], x[3], *(const float2*)((r4.onb1 ? pb : pa) + 8));
+                rotate(x[4], x[5], *(const float2*)((r4.onb2 ? pb : pa) + 16));
+                rotate(x[6], x[7], *(const float2*)((r4.onb3 ? pb : pa) + 24));
             }
             u32x4 hw, lw;
 #pragma unroll
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
             const int o = swz<C::DP>(tl, 8 * cc);
             *(u32x4*)(khi + o) = hw;
             *(u32x4*)(klo + o) = lw;
-            *(u32x4*)(vt + o) = live ? vr[s][j] : u32x4{0u, 0u, 0u, 0u};
+            *(u32x4*)(vt + o) = vr[s][j];
         }
     };
 
