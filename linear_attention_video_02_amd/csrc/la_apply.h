@@ -306,18 +306,18 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     for (int ph = 1; ph < NPH; ++ph) load_s(ph);
 
     int t_lo = 0, nt = 1;
-    PairRef pr[C::KS][4];
+    Rope4 r4[C::KS];
     if (ROPE) {
         const int cl = c1 > c0 ? c1 - 1 : c0;
         t_lo = (int)fdiv((uint32_t)(a.g.n_offset + c0), a.g.div_hw);
         nt = (int)fdiv((uint32_t)(a.g.n_offset + cl), a.g.div_hw) - t_lo + 1;
         build_rope_table(tab, t_lo, nt, a.g);
+        // pairs past d / 2 hold zeros: any table entry rotates them to zeros
+        // (the half last k-step: pairs 16 ks + 2 g, + 1)
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pr[ks][i] = pair_ref(C::HALF && ks == C::KS - 1 ? (i < 2 ? 16 * ks + 2 * g + i : 0)
-                                     : (C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g + i : 0, nt, a.g);
+            r4[ks] = rope4_make(C::HALF && ks == C::KS - 1 ? 16 * ks + 2 * g
+                                : (C::DP == D || 32 * ks + 8 * g < D) ? 16 * ks + 4 * g : 0, nt, a.g);
     }
 
     // each head's largest |S|: per thread, per wave, then over the waves
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             for (int r = 0; r < C::GR; ++r) {
                 const int tl = u0 + 16 * r + n;  // token within the chunk
                 Pos3 ps;
-                if (ROPE) ps = token_pos((uint32_t)(a.g.n_offset + c0 + min(tl, len - 1)), t_lo, a.g);
+                if (ROPE) ps = token_pos8((uint32_t)(a.g.n_offset + c0 + min(tl, len - 1)), t_lo, a.g);
                 float den = 0.0f;
                 f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
                 f32x4 acc[C::NT];
@@ -535,11 +535,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
                             for (int e = 0; e < 4; ++e) x[e] = ldexpf(x[e], sc);
                         }
-                        if (ROPE) {
-#pragma unroll
-                            for (int i = 0; i < 2; ++i)
-                                rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[ks][i], ps)]);
-                        }
+                        if (ROPE) rope4_rotate<2>(x, tab, r4[ks], rope4_rows(r4[ks], ps));
                         typedef __attribute__((ext_vector_type(4))) _Float16 f16x4v;
                         const f16x4v Bq4 = __builtin_bit_cast(
                             f16x4v, u32x2v{pack_f16(x[0], x[1]), pack_f16(x[2], x[3])});
@@ -577,10 +573,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
 #pragma unroll
                         for (int e = 0; e < 8; ++e) x[e] = ldexpf(x[e], sc);
                     }
-                    if (ROPE) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(pr[ks][i], ps)]);
-                    }
+                    if (ROPE) rope4_rotate(x, tab, r4[ks], rope4_rows(r4[ks], ps));
                     u32x4 hw;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) hw[i] = pack_f16(x[2 * i], x[2 * i + 1]);

@@ -226,19 +226,16 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, CausalBf16Cfg<D>::MINB) 
     load_q(1, 1);
 
     int t_lo = 0, nt = 1;
-    PairRef prk[4], prq[C::KS][4];
+    Rope4 rk4{}, rq4[C::KS];
     if (ROPE) {
         const int cl = c1 > c0 ? c1 - 1 : c0;
         t_lo = (int)fdiv((uint32_t)(a.g.n_offset + c0), a.g.div_hw);
         nt = (int)fdiv((uint32_t)(a.g.n_offset + cl), a.g.div_hw) - t_lo + 1;
         build_rope_table(tab, t_lo, nt, a.g);
         // pairs past d / 2 hold zeros: any table entry rotates them to zeros
+        rk4 = rope4_make(s_live ? 4 * sc : 0, nt, a.g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) prk[i] = pair_ref(s_live ? 4 * sc + i : 0, nt, a.g);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) prq[ks][i] = pair_ref(q_live(ks) ? 16 * ks + 4 * g + i : 0, nt, a.g);
+        for (int ks = 0; ks < C::KS; ++ks) rq4[ks] = rope4_make(q_live(ks) ? 16 * ks + 4 * g : 0, nt, a.g);
     }
 
     // bf16 hi / lo of the tiles, transposed (row = permuted value channel), into S buffer `buf`
@@ -307,9 +304,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, CausalBf16Cfg<D>::MINB) 
             for (int e = 0; e < 8; ++e) zp[e] += x[e];
             if (ROPE) {
                 const int tok = min(c0 + t0 + row, c1 - 1);
-                const Pos3 ps = token_pos((uint32_t)(a.g.n_offset + tok), t_lo, a.g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(prk[i], ps)]);
+                rope4_rotate(x, tab, rk4, rope4_rows(rk4, token_pos8((uint32_t)(a.g.n_offset + tok), t_lo, a.g)));
             }
             u32x4 hw, lw;
 #pragma unroll
@@ -343,7 +338,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, CausalBf16Cfg<D>::MINB) 
         uint32_t qbits = 0;  // non-zero iff this lane's relu(Q) values are not all zero
         bf16x8 Bq[C::KS], Bl[C::KS], Bu[C::KS];
         Pos3 qps;
-        if (ROPE) qps = token_pos((uint32_t)(a.g.n_offset + min(c0 + t0 + 16 * wave + n, c1 - 1)), t_lo, a.g);
+        if (ROPE) qps = token_pos8((uint32_t)(a.g.n_offset + min(c0 + t0 + 16 * wave + n, c1 - 1)), t_lo, a.g);
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
             const u32x4 qraw = q_live(ks) ? rq[slot][ks] : u32x4{0u, 0u, 0u, 0u};
@@ -365,8 +360,7 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, CausalBf16Cfg<D>::MINB) 
             den = fmaf(x[4], zb.x, den); den = fmaf(x[5], zb.y, den);
             den = fmaf(x[6], zb.z, den); den = fmaf(x[7], zb.w, den);
             if (ROPE) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rotate(x[2 * i], x[2 * i + 1], tab[pair_entry(prq[ks][i], qps)]);
+                rope4_rotate(x, tab, rq4[ks], rope4_rows(rq4[ks], qps));
             }
             u32x4 hw, lw;
 #pragma unroll

@@ -383,3 +383,17 @@ __device__ __forceinline__ void rotate(float& x0, float& x1, float2 cs) {
     x0 = a;
     x1 = b;
 }
+
+// rotate the four pairs of x by their entries of table tab (rows rr from
+// rope4_rows); npairs = 2 rotates pairs 0 and 1 only
+template <int NPAIRS = 4>
+__device__ __forceinline__ void rope4_rotate(float (&x)[2 * NPAIRS], const float2* tab, Rope4 r, int2 rr) {
+    const char* pa = (const char*)tab + rr.x;
+    const char* pb = (const char*)tab + rr.y;
+    rotate(x[0], x[1], *(const float2*)pa);
+    rotate(x[2], x[3], *(const float2*)((r.onb1 ? pb : pa) + 8));
+    if (NPAIRS > 2) {
+        rotate(x[4 % (2 * NPAIRS)], x[5 % (2 * NPAIRS)], *(const float2*)((r.onb2 ? pb : pa) + 16));
+        rotate(x[6 % (2 * NPAIRS)], x[7 % (2 * NPAIRS)], *(const float2*)((r.onb3 ? pb : pa) + 24));
+    }
+}

@@ -245,13 +245,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
             for (int e = 0; e < 8; ++e) zp[e] += x[e];
             if (ROPE) {
                 const int tok = min(c0 + tile * C::TT + tl, c1 - 1);
-                const int2 rr = rope4_rows(r4, token_pos8((uint32_t)(a.g.n_offset + tok), t_lo, a.g));
-                const char* pa = (const char*)tab + rr.x;
-                const char* pb = (const char*)tab + rr.y;
-                rotate(x[0], x[1], *(const float2*)pa);
-                rotate(x[2], x[3], *(const float2*)((r4.onb1 ? pb : pa) + 8));
-                rotate(x[4], x[5], *(const float2*)((r4.onb2 ? pb : pa) + 16));
-                rotate(x[6], x[7], *(const float2*)((r4.onb3 ? pb : pa) + 24));
+                rope4_rotate(x, tab, r4, rope4_rows(r4, token_pos8((uint32_t)(a.g.n_offset + tok), t_lo, a.g)));
             }
             u32x4 hw, lw;
 #pragma unroll
