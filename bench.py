@@ -635,12 +635,16 @@ def main():
 
     # dominant launch group: algorithmic bytes per launch / its mean event duration
     g = max(range(ngroups), key=lambda i: group_ms[i])
-    gname, kernels, nbytes = wl["groups"][g]
+    gname, kernels, nbytes = wl["groups"][g][:3]
+    # launches of each kernel in one pass of the group (the counter summary is per launch)
+    nlaunch = wl["groups"][g][3] if len(wl["groups"][g]) > 3 else 1
     dur_ms = group_ms[g]
     rf = wl.get("roofline", {"bound": "hbm", "peak": HBM_PEAK_GBPS, "unit": "GB/s", "scale": 1e9})
     achieved = nbytes / (dur_ms * 1e-3) / rf["scale"]
     src_hash = kernel_source_hash(args.workload)
     traffic = load_traffic(kernels, src_hash, args.workload)
+    if traffic is not None:
+        traffic *= nlaunch
 
     # Calibration copy o = q * 1 over rotating buffers: a plain elementwise
     # copy of known size (reads and writes copy_bytes), timed as the practical
@@ -1115,8 +1119,8 @@ def setup_workload(name, la, dev):
             "step": step, "tokens_per_step": B * N, "step_bytes": step_bytes,
             "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "block": L,
                        "eps": eps, "input_sets": 1},
-            # one group = all block steps (state, combine and apply launches of 10 blocks)
-            "groups": [("block_steps", STATE_KERNELS + APPLY_KERNELS, step_bytes)],
+            # one group = all block steps (state, combine and apply launches of the nb blocks)
+            "groups": [("block_steps", STATE_KERNELS + APPLY_KERNELS, step_bytes, nb)],
             "copy_pairs": [(blocks[0][b], outs[b]) for b in range(nb)],
             "block_bytes": blk_bytes,
         }
