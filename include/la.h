@@ -136,6 +136,31 @@ LA_API int la_apply(const void* Q, const void* K, const void* V, void* O,
              int B, int H, int N, int d, int gt, int gh, int gw,
              int block_tokens, float eps, int dtype, void* stream);
 
+/* Linear cross-attention in one call (the SANA-Video analysis page, "How
+ * SANA-Video Positions Itself" and the Linear DiT block of section 3.4: the
+ * cross-attention is the same ReLU linear attention as Eq. 2; text tokens
+ * carry no grid position, so no RoPE):
+ *   O[b,h,i] = relu(Q[b,h,i]) S[b,h] / (relu(Q[b,h,i]) . z[b,h] + eps),
+ *   S[b,h] = sum_j relu(K[b,h,j])^T V[b,h,j],   z[b,h] = sum_j relu(K[b,h,j]),
+ * over the N_kv keys/values.  Q, O: [B, H, N_q, d]; K, V: [B, H, N_kv, d]
+ * (K and V may be NULL when N_kv = 0: O is then all zeros).  bf16 at d = 64
+ * with N_kv <= 512 runs as one launch, each apply workgroup forming its
+ * heads' S and z from K and V; every other case runs the state pass into
+ * the workspace's S and z, then the apply pass (la_state_reduce and
+ * la_apply in one call).  ws: at least la_cross_workspace_bytes(B, H, N_kv,
+ * d) bytes, zero-filled once like any workspace, used only by the two-launch
+ * path; it must not overlap Q, K, V or O, nor O overlap Q, K or V
+ * (LA_E_ALIAS).  N_q = 0 returns LA_OK with nothing written.  Each output
+ * has one fixed order of summation, so repeated calls give bitwise equal
+ * results. */
+LA_API int la_cross_attention(const void* Q, const void* K, const void* V, void* O,
+                       void* ws, size_t ws_bytes, int B, int H, int N_q, int N_kv, int d,
+                       float eps, int dtype, void* stream);
+
+/* Workspace bytes for la_cross_attention over N_kv keys/values (0 for
+ * invalid sizes). */
+LA_API size_t la_cross_workspace_bytes(int B, int H, int N_kv, int d);
+
 /* One block of block-causal mode (Eq. 3 taken a block at a time, Algorithm 1).
  * The sequence has N tokens in blocks of L = block_tokens; block b =
  * block_idx covers global tokens [b*L, min((b+1)*L, N)) and Q, K, V, O hold
@@ -219,6 +244,7 @@ LA_API int la_stream_copy(const void* src, void* dst, size_t bytes, void* stream
  *   "tc_state_threads" 512 / 1024: token-causal partial-state workgroups
  *   "tconv_gm", "tconv_gn"  temporal-convolution tile-order group (1..64)
  *   "apply_spread"     0 / 1: a slot's apply workgroups on as few XCDs as possible / on all 8
+ *   "cross_fused"      0: la_cross_attention always takes the two-launch path
  * Returns LA_OK, LA_E_NULLPTR, LA_E_UNSUPPORTED (unknown name) or
  * LA_E_SHAPE (value out of range).  Not thread-safe: set knobs while no
  * other thread calls the library.  Results are correct under every value. */

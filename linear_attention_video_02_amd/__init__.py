@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.la_apply.restype = ci
         L.la_block_causal_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + common + [ci, ci, vp]
         L.la_block_causal_step.restype = ci
+        L.la_cross_attention.argtypes = [vp, vp, vp, vp, vp, cs] + [ci] * 5 + [cf, ci, vp]
+        L.la_cross_attention.restype = ci
+        L.la_cross_workspace_bytes.argtypes = [ci] * 4
+        L.la_cross_workspace_bytes.restype = cs
         L.la_token_causal.argtypes = [vp, vp, vp, vp, vp, vp, vp, cs] + [ci] * 8 + [cf, ci, vp]
         L.la_token_causal.restype = ci
         L.la_temporal_conv_step.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
@@ -298,17 +302,47 @@ def bidirectional(q, k, v, grid=None, eps=1e-6, out=None, ws=None):
 def cross_attention(q, k, v, eps=1e-6, out=None, ws=None):
     """Linear cross-attention: q [B, H, N_q, d] over k, v [B, H, N_kv, d], no RoPE.
 
-    The same two library calls as self-attention (la_state_reduce over the
-    N_kv keys/values, la_apply over the N_q queries); N_kv = 0 gives zeros.
+    One library call (la_cross_attention): one launch for bf16 at d = 64 with
+    N_kv <= 512, otherwise the state pass over the N_kv keys/values and the
+    apply pass over the N_q queries.  N_kv = 0 gives zeros.
     """
+    torch = _torch()
     _check_dims(q, k, v)
     if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
         raise ValueError("k and v must be [B, H, N_kv, d] with q's B, H and d")
     if out is not None:
         _check_same_shape("cross_attention q/out", q, out)
     _check_qkv(q, k, v)
-    S, z = state_reduce(k, v, None, ws=ws)
-    return apply(q, S, z, None, eps, out)
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if ws is None:
+        ws = cross_workspace(B, H, Nkv, d, q.device)
+    rc = lib().la_cross_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ws.numel(), B, H, Nq, Nkv, d,
+                                  float(eps), _dtype_code(q), _stream(q))
+    if rc:
+        raise LinAttnError(rc, "la_cross_attention")
+    return out
+
+
+def cross_workspace(B, H, Nkv, d, device):
+    """A zero-filled workspace for cross_attention over Nkv keys/values, cached like workspace()."""
+    torch = _torch()
+    nbytes = int(lib().la_cross_workspace_bytes(B, H, Nkv, d))
+    if nbytes == 0:
+        raise ValueError("invalid sizes for a workspace")
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    stream = torch.cuda.current_stream(dev)
+    key = ("cross", dev.type, dev.index, int(stream.cuda_stream), nbytes)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
 
 
 def block_causal_step(q, k, v, S_carry, z_carry, N, grid, block_tokens, block_idx,

@@ -54,7 +54,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // la_set_tuning().  Nothing here reads the process environment.
 enum Knob {
     K_STATE_WGS, K_APPLY_WGS, K_CAUSAL_WGS, K_STATE_FUSED, K_APPLY_ILV, K_APPLY_HEADS,
-    K_TC_STATE_THREADS, K_TCONV_GM, K_TCONV_GN, K_APPLY_SPREAD, K_COUNT
+    K_TC_STATE_THREADS, K_TCONV_GM, K_TCONV_GN, K_APPLY_SPREAD, K_CROSS_FUSED, K_COUNT
 };
 struct KnobInfo {
     const char* name;
@@ -64,9 +64,9 @@ const KnobInfo kKnobs[K_COUNT] = {
     {"state_wgs", 1, 1 << 20},  {"apply_wgs", 1, 1 << 20},  {"causal_wgs", 1, 1 << 20},
     {"state_fused", 0, 1},      {"apply_ilv", 0, 1},        {"apply_heads", 1, 8},
     {"tc_state_threads", 512, 1024}, {"tconv_gm", 1, 64},   {"tconv_gn", 1, 64},
-    {"apply_spread", 0, 1},
+    {"apply_spread", 0, 1},     {"cross_fused", 0, 1},
 };
-int g_knob[K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+int g_knob[K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
 
 int knob(Knob k, int dflt) { return g_knob[k] >= 0 ? g_knob[k] : dflt; }
 
@@ -431,6 +431,11 @@ KernelFn<ApplyArgs> apply_bf16_kernel(int nph) {
     return la_apply_bf16_kernel<D, ROPE, M>;
 }
 
+// cross-attention in one launch (d = 64, no RoPE): the KV instance with one or two heads
+KernelFn<ApplyArgs> apply_kv_kernel(int nph) {
+    return nph <= 1 ? la_apply_bf16_kernel<64, false, 1, true> : la_apply_bf16_kernel<64, false, 2, true>;
+}
+
 KernelFn<ApplyArgs> apply_kernel(int d, int dtype, bool rope, int nph) {
 #define LA_PICK(D)                                                                              \
     if (d == D) {                                                                               \
@@ -515,12 +520,53 @@ int run_apply(const void* Q, void* O, const float* S, const float* z, int B, int
     a.hs = pl.hs;
     a.spread = pl.spread;
     a.g = g;
+    a.K = nullptr;
+    a.V = nullptr;
+    a.nkv = 0;
     const int threads = dtype != LA_BF16 ? 256
                         : d == 32        ? ApplyBf16Cfg<32>::THREADS
                         : d == 64        ? ApplyBf16Cfg<64>::THREADS
                         : d == 112       ? ApplyBf16Cfg<112>::THREADS
                                          : ApplyBf16Cfg<128>::THREADS;
     return launch_kernel<ApplyArgs>(apply_kernel(d, dtype, g.rope, pl.nph), dim3(pl.grid), pl.lds, st, a, threads);
+}
+
+// Linear cross-attention in one launch: the apply kernel's KV instance forms
+// each head's S and z from its n_kv keys/values (bf16, d = 64, n_kv <=
+// KV_MAXKV).  Returns LA_E_UNSUPPORTED, launching nothing, where the
+// plan puts more than two heads on a workgroup.
+int run_cross_fused(const void* Q, const void* K, const void* V, void* O, int B, int H, int nq, int nkv, float eps,
+                    hipStream_t st) {
+    const LaGeom g = make_geom(B, H, nq, 0, 64, 0, 0, 0);
+    ApplyPlan pl;
+    int rc = plan_apply(g, 64, LA_BF16, &pl);
+    if (rc != LA_OK) return rc;
+    if (pl.nph > 2 || nkv > KV_MAXKV) return LA_E_UNSUPPORTED;
+    ApplyArgs a;
+    a.Q = Q;
+    a.O = O;
+    a.S = nullptr;
+    a.z = nullptr;
+    a.K = K;
+    a.V = V;
+    a.nkv = nkv;
+    a.eps = eps;
+    a.chunk = pl.chunk;
+    a.P = pl.P;
+    a.ilv = pl.ilv;
+    a.nph = pl.nph;
+    a.hs = pl.hs;
+    a.spread = pl.spread;
+    a.g = g;
+    return launch_kernel<ApplyArgs>(apply_kv_kernel(pl.nph), dim3(pl.grid), pl.lds, st, a,
+                                    ApplyBf16Cfg<64>::THREADS);
+}
+
+// Cross-attention workspace: the state pass's over n_kv tokens, then S and z
+// (used where the two-launch path runs)
+size_t cross_ws_bytes(int BH, int d, int partials) {
+    return align_up(ws_layout(BH, d, partials).total, 256) + align_up((size_t)BH * d * d * 4, 256) +
+           align_up((size_t)BH * d * 4, 256);
 }
 
 // LDS of the token-causal scan kernel without its RoPE table
@@ -833,6 +879,45 @@ int la_apply(const void* Q, const void* K, const void* V, void* O, const float* 
     rc = precheck_plans(B, H, N, 0, d, gt, gh, gw, dtype, false, true);
     if (rc != LA_OK) return rc;
     return run_apply(Q, O, S, z, B, H, N, 0, d, gt, gh, gw, eps, dtype, (hipStream_t)stream);
+}
+
+size_t la_cross_workspace_bytes(int B, int H, int N_kv, int d) {
+    if (check_common(B, H, N_kv, d, 0, 0, 0, 0.0f, LA_BF16) != LA_OK) return 0;
+    return cross_ws_bytes(B * H, d, max_partials(B, H, N_kv, d, 0, 0, 0));
+}
+
+int la_cross_attention(const void* Q, const void* K, const void* V, void* O, void* ws, size_t ws_bytes, int B,
+                       int H, int N_q, int N_kv, int d, float eps, int dtype, void* stream) {
+    int rc = check_common(B, H, N_q, d, 0, 0, 0, eps, dtype);
+    if (rc != LA_OK) return rc;
+    rc = check_common(B, H, N_kv, d, 0, 0, 0, eps, dtype);
+    if (rc != LA_OK) return rc;
+    if (N_q == 0) return LA_OK;  // nothing to write
+    if (!Q || !O || !ws || (N_kv > 0 && (!K || !V))) return LA_E_NULLPTR;
+    if (!aligned16(Q) || !aligned16(O) || !aligned16(K) || !aligned16(V) || !aligned16(ws)) return LA_E_ALIGN;
+    int partials = 0;
+    rc = precheck_plans(B, H, N_kv, 0, d, 0, 0, 0, dtype, true, false, &partials);
+    if (rc != LA_OK) return rc;
+    rc = precheck_plans(B, H, N_q, 0, d, 0, 0, 0, dtype, false, true);
+    if (rc != LA_OK) return rc;
+    if (ws_bytes < cross_ws_bytes(B * H, d, partials)) return LA_E_WORKSPACE;
+    const size_t nq = (size_t)B * H * N_q * d * elem_bytes(dtype);
+    const size_t nkv = (size_t)B * H * N_kv * d * elem_bytes(dtype);
+    if (overlaps(O, nq, Q, nq) || overlaps(O, nq, K, nkv) || overlaps(O, nq, V, nkv) || overlaps(ws, ws_bytes, Q, nq) ||
+        overlaps(ws, ws_bytes, O, nq) || overlaps(ws, ws_bytes, K, nkv) || overlaps(ws, ws_bytes, V, nkv))
+        return LA_E_ALIAS;
+    const hipStream_t st = (hipStream_t)stream;
+    if (dtype == LA_BF16 && d == 64 && N_kv <= KV_MAXKV && knob(K_CROSS_FUSED, 1) != 0) {
+        rc = run_cross_fused(Q, K, V, O, B, H, N_q, N_kv, eps, st);
+        if (rc != LA_E_UNSUPPORTED) return rc;
+    }
+    // two launches: the state pass into the workspace's S and z, then the apply
+    const size_t off_S = align_up(ws_layout(B * H, d, partials).total, 256);
+    float* S = (float*)((char*)ws + off_S);
+    float* z = (float*)((char*)ws + off_S + align_up((size_t)B * H * d * d * 4, 256));
+    rc = run_state(K, V, S, z, nullptr, nullptr, nullptr, nullptr, ws, B, H, N_kv, 0, d, 0, 0, 0, dtype, st);
+    if (rc != LA_OK) return rc;
+    return run_apply(Q, O, S, z, B, H, N_q, 0, d, 0, 0, 0, eps, dtype, st);
 }
 
 int la_block_causal_step(const void* Q, const void* K, const void* V, void* O, float* S_carry, float* z_carry,

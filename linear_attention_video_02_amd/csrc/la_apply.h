@@ -8,12 +8,18 @@
 #pragma once
 
 #include "la_common.h"
+#include "la_state.h"
 
 struct ApplyArgs {
     const void* Q;
     void* O;
     const float* S;  // [BH][D*D]
     const float* z;  // [BH][D]
+    // cross-attention in one launch (the KV instance): S and z of each head
+    // formed in the prologue from its nkv keys/values instead of read
+    const void* K;   // [BH][nkv][D]
+    const void* V;
+    int nkv;
     float eps;
     int chunk;       // ilv = 0: tokens per workgroup
     int P;           // workgroups per head
@@ -162,9 +168,14 @@ __device__ __forceinline__ void apply_item_of_block(int P, int NS, int spread, i
 }
 
 // NPH: register slots for S, at least the heads per workgroup (a.nph)
-template <int D, bool ROPE, int NPH>
+// KV: cross-attention in one launch, S and z formed from K and V (d = 64, no
+// RoPE, at most KV_MAXKV keys/values a head; the instance with NPH slots runs
+// with exactly NPH heads a workgroup)
+constexpr int KV_MAXKV = 512;
+template <int D, bool ROPE, int NPH, bool KV = false>
 __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel(ApplyArgs a) {
     using C = ApplyBf16Cfg<D>;
+    static_assert(!KV || (D == 64 && !ROPE && C::STGBYTES == 64 * 1024), "one-launch cross-attention layout");
     extern __shared__ __align__(16) unsigned char smem[];
     const bool ilv = a.ilv != 0;
     const int nph = ilv ? a.nph : 1;
@@ -224,7 +235,32 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             sraw[ph][i] = *(const f32x4*)(Sh + 4 * (f < D * D / 4 ? f : 0));
         }
     };
-    load_s(0);
+    // KV instance: every load of a head's keys/values at once (at most 512
+    // tokens: two fills of 256 tokens, 16-byte pieces: thread -> rows
+    // 64 j + sr of a fill, channels 8 sc .. 8 sc + 7), phase 0's ahead of the
+    // first units of Q, the next phase's as soon as this one's are staged;
+    // rows past nkv read as zeros (no traffic)
+    u32x4 kvk[KV ? 2 : 1][4], kvv[KV ? 2 : 1][4];
+    const int kv_sr = threadIdx.x >> 3, kv_sc = threadIdx.x & 7;
+    const uint32_t kv_bytes = KV ? (uint32_t)a.nkv * D * 2 : 0u;
+    auto kv_issue = [&](int ph) {
+        const int hd = __builtin_amdgcn_readfirstlane(head_of(ph < nph ? ph : 0));
+        const BufRsrc Kr = make_rsrc((const uint16_t*)a.K + (size_t)hd * a.nkv * D, kv_bytes);
+        const BufRsrc Vr = make_rsrc((const uint16_t*)a.V + (size_t)hd * a.nkv * D, kv_bytes);
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t off = (uint32_t)((256 * f + 64 * j + kv_sr) * D + 8 * kv_sc) * 2u;
+                kvk[f][j] = buf_load16(Kr, off);
+                kvv[f][j] = buf_load16(Vr, off);
+            }
+    };
+    if constexpr (KV) {
+        kv_issue(0);
+    } else {
+        load_s(0);
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of Q's
 
     // the ring: slot s holds the unit (phase, first token) whose Q is in qr[s]
@@ -302,8 +338,108 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         load_unit(qr[s], fixed ? us[s] : make_int2(nph, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!KV) {
 #pragma unroll
-    for (int ph = 1; ph < NPH; ++ph) load_s(ph);
+        for (int ph = 1; ph < NPH; ++ph) load_s(ph);
+    } else {
+        // S = relu(K)^T V on v_mfma_f32_32x32x16_bf16 (relu K and V exact in
+        // bf16, every product exact in fp32): wave w sums the 32 x 32 tile
+        // (w & 1, (w >> 1) & 1) over token half w >> 2 of each fill, the
+        // halves are added in LDS, and the rows of S go to the registers the
+        // conversion below reads (as if loaded from S).  z: per-thread sums
+        // of relu(K), then across the lanes and waves.  The Q/O staging tiles
+        // are free until the unit loop: during a fill relu K [0, 32 KB) and
+        // V [32, 64 KB); then the upper halves' tiles [0, 16 KB), S rows
+        // [16, 32 KB), per-wave z [32, 34 KB).
+        uint16_t* kt = stg;
+        uint16_t* vt = stg + 256 * 64;
+        float* red = (float*)smem;
+        float* srw = (float*)(smem + 16384);
+        float* zw = (float*)(smem + 32768);
+        const int i16 = lane & 15, q2 = (lane >> 4) & 1, gq = lane >> 5, m32 = lane & 31;
+        const int rd_row = 8 * gq + (i16 >> 2), rd_col = 16 * q2 + 4 * (i16 & 3);
+        const int tile = wave & 3, ci = tile & 1, cj = tile >> 1, th = wave >> 2;
+        const int nfill = (a.nkv + 255) / 256;
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph) {
+            float zp[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zp[e] = 0.0f;
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                if (f < nfill) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u32x4 w;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            w[i] = relu_bf16x2(kvk[f][j][i]);
+                            zp[2 * i] += bf_lo(w[i]);
+                            zp[2 * i + 1] += bf_hi(w[i]);
+                        }
+                        *(u32x4*)(kt + swz<64>(64 * j + kv_sr, 8 * kv_sc)) = w;
+                        *(u32x4*)(vt + swz<64>(64 * j + kv_sr, 8 * kv_sc)) = kvv[f][j];
+                    }
+                    lds_barrier();
+#pragma unroll
+                    for (int st = 0; st < 8; ++st) {
+                        const int r0 = 128 * th + 16 * st + rd_row, r1 = r0 + 4;
+                        const bf16x8 A = lds_read_tr8(kt + swz<64>(r0, 32 * ci + rd_col),
+                                                      kt + swz<64>(r1, 32 * ci + rd_col));
+                        const bf16x8 B = lds_read_tr8(vt + swz<64>(r0, 32 * cj + rd_col),
+                                                      vt + swz<64>(r1, 32 * cj + rd_col));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
+                    }
+                    lds_barrier();  // tiles free for the next fill
+                }
+            }
+            // the next phase's keys/values (this phase's are all staged; every
+            // phase of this instance is a head of the workgroup: nph = NPH)
+            if (ph + 1 < NPH) kv_issue(ph + 1);
+            if (th == 1) {
+#pragma unroll
+                for (int r = 0; r < 16; r += 4)
+                    *(f32x4*)(red + ((tile * 4 + r / 4) * 64 + lane) * 4) =
+                        f32x4{acc[r], acc[r + 1], acc[r + 2], acc[r + 3]};
+            }
+#pragma unroll
+            for (int msk = 8; msk < 64; msk <<= 1)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zp[e] += __shfl_xor(zp[e], msk);
+            if (lane < 8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) zw[wave * 64 + 8 * lane + e] = zp[e];
+            }
+            lds_barrier();
+            if (th == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; r += 4) {
+                    const f32x4 u = *(const f32x4*)(red + ((tile * 4 + r / 4) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[r + e] += u[e];
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    srw[(32 * ci + 8 * (r >> 2) + 4 * gq + (r & 3)) * 64 + 32 * cj + m32] = acc[r];
+            }
+            if (threadIdx.x < 64) {
+                float zsum = 0.0f;
+#pragma unroll
+                for (int w = 0; w < C::NW; ++w) zsum += zw[w * 64 + threadIdx.x];
+                zs[ph * C::DP + threadIdx.x] = zsum;
+            }
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < S4; ++i) {
+                const int f = threadIdx.x + i * C::THREADS;
+                sraw[ph][i] = *(const f32x4*)(srw + 4 * (f < D * D / 4 ? f : 0));
+            }
+            lds_barrier();  // before the next head's tiles
+        }
+    }
 
     int t_lo = 0, nt = 1;
     Rope4 r4[C::KS];
@@ -381,7 +517,7 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                 put_st(k, co, 0.0f);
             }
             for (int c = threadIdx.x; c < C::DP; c += C::THREADS)
-                zs[ph * C::DP + c] = c < D ? a.z[(size_t)hd * D + c] : 0.0f;
+                if (!KV) zs[ph * C::DP + c] = c < D ? a.z[(size_t)hd * D + c] : 0.0f;
         }
     }
     lds_barrier();  // S^T copies, z, exponents and the queue heads visible

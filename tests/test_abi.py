@@ -40,7 +40,8 @@ def test_exports_every_declared_function(L):
     assert set(names) == {"la_workspace_bytes", "la_state_reduce", "la_apply",
                           "la_block_causal_step", "la_token_causal", "la_temporal_conv_step",
                           "la_stream_copy", "la_strerror", "la_last_hip_error", "la_set_tuning",
-                          "la_workspace_bytes_grid", "la_state_reduce_noalloc"}
+                          "la_workspace_bytes_grid", "la_state_reduce_noalloc", "la_cross_attention",
+                          "la_cross_workspace_bytes"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -207,6 +208,46 @@ def test_token_causal_empty_is_noop(L):
     assert causal_call(L, N=0, Q=None, K=None, V=None, O=None) == 0
 
 
+def cross_call(L, **kw):
+    a = dict(Q=p(0), K=p(1 << 30), V=p(2 << 30), O=p(3 << 30), ws=p(4 << 30), ws_bytes=1 << 40, B=1, H=2,
+             Nq=1000, Nkv=300, d=64, eps=1e-6, dtype=la.LA_BF16)
+    a.update(kw)
+    return L.la_cross_attention(a["Q"], a["K"], a["V"], a["O"], a["ws"], a["ws_bytes"], a["B"], a["H"],
+                                a["Nq"], a["Nkv"], a["d"], a["eps"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=48), "LA_E_UNSUPPORTED"),
+    (dict(dtype=7), "LA_E_UNSUPPORTED"),
+    (dict(Nkv=-1), "LA_E_SHAPE"),
+    (dict(Nq=-1), "LA_E_SHAPE"),
+    (dict(eps=-1.0), "LA_E_SHAPE"),
+    (dict(Q=None), "LA_E_NULLPTR"),
+    (dict(K=None), "LA_E_NULLPTR"),
+    (dict(ws=None), "LA_E_NULLPTR"),
+    (dict(V=p((2 << 30) + 8)), "LA_E_ALIGN"),
+    (dict(ws_bytes=100), "LA_E_WORKSPACE"),
+    (dict(O=p(0)), "LA_E_ALIAS"),                  # O == Q
+    (dict(O=p(2 << 30)), "LA_E_ALIAS"),            # O == V
+    (dict(ws=p(1 << 30)), "LA_E_ALIAS"),           # workspace over K
+])
+def test_cross_attention_rejects(L, kw, want):
+    assert cross_call(L, **kw) == E[want]
+
+
+def test_cross_attention_workspace_and_empty(L):
+    L.la_cross_workspace_bytes.restype = ctypes.c_size_t
+    n = L.la_cross_workspace_bytes(2, 32, 300, 64)
+    # the state pass's workspace over the keys/values, then S and z (two-launch path)
+    assert n >= L.la_workspace_bytes(2, 32, 300, 64) + 2 * 32 * (64 * 64 + 64) * 4
+    assert L.la_cross_workspace_bytes(2, 32, 300, 48) == 0
+    # N_q = 0: checks on sizes pass, nothing is launched
+    assert cross_call(L, Nq=0, Q=None, K=None, V=None, O=None, ws=None) == 0
+    # N_kv = 0: K and V may be NULL (the output is all zeros); here the
+    # workspace check fails first, before anything is launched
+    assert cross_call(L, Nkv=0, K=None, V=None, ws_bytes=10) == E["LA_E_WORKSPACE"]
+
+
 def tconv_call(L, **kw):
     a = dict(X=p(0), Y=p(1 << 30), W=p(2 << 30), bias=None, cache=p(3 << 30), B=1, T=4, P=920,
              D=2240, commit=1, dtype=la.LA_BF16)
@@ -255,6 +296,7 @@ def test_set_tuning(L):
     assert L.la_set_tuning(b"apply_heads", 9) == E["LA_E_SHAPE"]
     assert L.la_set_tuning(b"state_fused", 2) == E["LA_E_SHAPE"]
     assert L.la_set_tuning(b"tc_state_threads", 700) == E["LA_E_SHAPE"]
+    assert L.la_set_tuning(b"cross_fused", 0) == 0 and L.la_set_tuning(b"cross_fused", -1) == 0
     assert L.la_set_tuning(b"no_such_knob", 1) == E["LA_E_UNSUPPORTED"]
     assert L.la_set_tuning(None, 1) == E["LA_E_NULLPTR"]
     with la.tuning(apply_wgs=12, state_fused=0):
