@@ -243,7 +243,10 @@ def test_cross_attention_one_launch_matches_two(la, B, H, Nkv):
     say(f"  one launch vs two: {e:.3e}")
     assert e <= 1e-2
     assert torch.equal(two, four) or row_err(host(four), host(two)) <= 1e-2
-    assert_close(host(one), oracle.cross_attention(q, k, v, 1e-6), "bf16", "one launch")
+    ref = oracle.cross_attention(q, k, v, 1e-6)
+    assert_close(host(one), ref, "bf16", "one launch")
+    assert_close(host(two), ref, "bf16", "two launches")
+    assert_close(host(four), ref, "bf16", "four heads a workgroup")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
