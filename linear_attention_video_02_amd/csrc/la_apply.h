@@ -285,8 +285,9 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             wok[i] = b < C::UB;
             if (wok[i]) {
                 woff[i] = stw_off<C::DP>(b / (2 * D), (b % (2 * D)) / 16);
-            } else {  // a padding chunk (channel >= d) of some row
-                const int k = (b - C::UB) / 16, pads = (C::DP - D) / 8;
+            } else {  // a padding chunk (channel >= d) of some row (d < DP only)
+                constexpr int pads = C::DP > D ? (C::DP - D) / 8 : 1;
+                const int k = (b - C::UB) / 16;
                 woff[i] = stw_off<C::DP>(k / pads, D / 8 + k % pads);
             }
         }
@@ -505,11 +506,12 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             }
             // the padding rows and columns (key or value channel >= d); with the
             // half last k-step no padding entry is ever read into a stored output
+            constexpr int padc = C::DP > D ? C::DP - D : 1;  // (the loop runs only where DP > d)
             for (int e = threadIdx.x; !C::HALF && e < C::DP * C::DP - D * D; e += C::THREADS) {
                 int k, co;
                 if (e < D * (C::DP - D)) {
-                    k = e / (C::DP - D);
-                    co = D + e % (C::DP - D);
+                    k = e / padc;
+                    co = D + e % padc;
                 } else {
                     k = D + (e - D * (C::DP - D)) / C::DP;
                     co = (e - D * (C::DP - D)) % C::DP;
