@@ -236,6 +236,11 @@ def test_cross_attention_one_launch_matches_two(la, B, H, Nkv):
     # more heads a workgroup than the one-launch instance holds: two launches too
     with la.tuning(apply_heads=4):
         four = la.cross_attention(tq, tk, tv, 1e-6)
+    # one launch with one contiguous chunk per workgroup, and with few workgroups
+    with la.tuning(apply_ilv=0):
+        chunks = la.cross_attention(tq, tk, tv, 1e-6)
+    with la.tuning(apply_wgs=7):
+        few = la.cross_attention(tq, tk, tv, 1e-6)
     torch.cuda.synchronize()
     assert torch.equal(one, again)
     from _gpu import row_err
@@ -247,6 +252,8 @@ def test_cross_attention_one_launch_matches_two(la, B, H, Nkv):
     assert_close(host(one), ref, "bf16", "one launch")
     assert_close(host(two), ref, "bf16", "two launches")
     assert_close(host(four), ref, "bf16", "four heads a workgroup")
+    assert_close(host(chunks), ref, "bf16", "contiguous chunks")
+    assert_close(host(few), ref, "bf16", "seven workgroups")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
