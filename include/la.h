@@ -228,8 +228,9 @@ LA_API int la_temporal_conv_step(const void* X, void* Y, const void* W, const fl
 /* Measurement utility, not part of the method: a plain copy of `bytes`
  * bytes from src to dst (device memory, 16-byte aligned, bytes a multiple of
  * 16, no overlap; otherwise LA_E_ALIGN / LA_E_ALIAS), one 16-byte piece per
- * lane.  Its rate is the practical ceiling of a read + write HBM stream that
- * the kernels above are compared with.  bytes = 0 returns LA_OK; more than
+ * lane, with the same cache policies as the kernels' own streams
+ * (non-temporal loads, streaming stores).  Its rate is the practical ceiling
+ * of a read + write HBM stream that the kernels above are compared with.  bytes = 0 returns LA_OK; more than
  * 2^42 bytes returns LA_E_UNSUPPORTED. */
 LA_API int la_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 

@@ -76,13 +76,18 @@ __device__ __forceinline__ BufRsrc make_rsrc(const void* base, uint32_t nbytes) 
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
 
+// Streaming loads of the inputs (Q, K, V: read once per pass) carry the
+// non-temporal hint (cache policy nt).  Same-process A/B on gfx950, outputs
+// bitwise equal: 720p-5s state pass 61.4 -> 55.7 us, apply 62.5 -> 61.0 us;
+// token-causal call 222 -> 220 us; N = 65,536 d = 128 step 420 -> 412 us.
+// The scope bits (sc0, sc1) made no difference either way.
 __device__ __forceinline__ u32x4 buf_load16(BufRsrc r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
 }
 
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2v;
 __device__ __forceinline__ u32x2v buf_load8(BufRsrc r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
 }
 
 __device__ __forceinline__ void buf_store16(u32x4 v, BufRsrc r, uint32_t off) {

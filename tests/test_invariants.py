@@ -283,13 +283,15 @@ def test_token_causal_canaries_untouched(la):
 
 def test_stream_copy_is_exact(la):
     """The measurement copy (la_stream_copy) moves every byte, at a size that
-    is not a multiple of one sweep of the grid."""
+    is not a multiple of one workgroup's 4 KB, and writes nothing past the end."""
     import torch
-    src = torch.randint(0, 2**31 - 1, (5 * 1048576 + 20,), dtype=torch.int32, device="cuda:0")  # > one sweep (16 MB)
-    dst = torch.zeros_like(src)
-    la.stream_copy(src, dst)
+    n = 5 * 1048576 + 20  # 1,310,725 pieces of 16 bytes: the last workgroup holds 5
+    src = torch.randint(0, 2**31 - 1, (n + 1024,), dtype=torch.int32, device="cuda:0")
+    dst = torch.full((n + 1024,), -7, dtype=torch.int32, device="cuda:0")
+    la.stream_copy(src[:n], dst[:n])
     torch.cuda.synchronize()
-    assert torch.equal(src, dst)
+    assert torch.equal(src[:n], dst[:n])
+    assert bool((dst[n:] == -7).all())
 
 
 def test_stale_counters_heal(la):
