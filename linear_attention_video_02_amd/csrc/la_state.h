@@ -131,8 +131,9 @@ __device__ __forceinline__ void item_of_block(int P, int BH, int& bh, int& p) {
 // touches fall in distinct banks.  MFMA operands -- 8 consecutive tokens of
 // one channel -- come back with two ds_read_b64_tr_b16.
 // MFMA: C[c_in][c_out] += A[c_in][tok] B[tok][c_out], A = (hi, lo)^T, B = V.
-// Wave w owns key-channel tile w % NCI (32 rows of S, all value channels)
-// and token group w / NCI of every tile; at the end the NTG token groups of
+// Wave w owns key-channel tile w % NCI (32 rows of S), value-channel split
+// (w / NCI) % NVS (all value channels, or at d = 64 one 32-channel half) and
+// token group w / (NCI NVS) of every tile; at the end the NTG token groups of
 // each key-channel tile are summed in LDS in a fixed order (a tree of fan-in four).
 // Two LDS buffers: tile t's MFMAs read one while tile t+1 is staged into the
 // other, with one barrier per tile.  DEPTH tiles of K/V are in flight per
@@ -150,15 +151,22 @@ struct StateBf16Cfg {
     static constexpr int DEPTH = 2;           // tiles of K/V in flight per workgroup
     static constexpr int TILE = TT * DP;      // elements per LDS tile
     static constexpr int BUF = 3 * TILE;      // K hi, K lo, V
-    static constexpr int NCI = DP / 32;       // key-channel tiles = wave groups
-    static constexpr int NTG = NW / NCI;      // token groups
-    static constexpr int NJ = DP / 32;        // value-channel tiles per wave
+    static constexpr int NCI = DP / 32;       // key-channel tiles
+    // Value channels split over the waves at d = 64: each wave then owns one
+    // 32 x 32 tile of S, and the fold at the end moves half the bytes through
+    // LDS in one level instead of two (it took 1.44 us of the 720p-5s pass).
+    // The extra K fragment reads per tile cost nothing visible.  At d >= 112
+    // the staging VALU bounds the loop and the split is not used.
+    static constexpr int NVS = D == 64 ? 2 : 1;
+    static constexpr int NCO = NCI * NVS;     // (key tile, value split) pairs
+    static constexpr int NTG = NW / NCO;      // token groups
+    static constexpr int NJ = DP / 32 / NVS;  // value-channel tiles per wave
     static constexpr int KSTEPS = TT / (16 * NTG);  // 16-token steps per wave per tile
     static constexpr int NACC = NJ * 16;      // accumulators per lane
     static constexpr int STAGE_BYTES = 2 * BUF * 2;
     // fold of the token groups in groups of four: the first level has the
-    // most senders, NTG - ceil(NTG / 4) per key-channel tile
-    static constexpr int RED_BYTES = (NTG - (NTG + 3) / 4) * NCI * 64 * NACC * 4;
+    // most senders, NTG - ceil(NTG / 4) per (key tile, value split) pair
+    static constexpr int RED_BYTES = (NTG - (NTG + 3) / 4) * NCO * 64 * NACC * 4;
     static constexpr int ZRED_BYTES = NW * DP * 4;  // z: one row of DP sums per wave
     static constexpr int m1 = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
     static constexpr int SMEM_FIXED = m1 > ZRED_BYTES ? m1 : ZRED_BYTES;
@@ -173,6 +181,33 @@ template <int D>
 __device__ __forceinline__ int swz(int row, int ch) {
     const int s = D == 32 ? 0 : (D == 64 ? ((row >> 1) & 1) : (row & 3));  // D = on-chip width
     return row * D + (((ch >> 5) ^ s) << 5) + (ch & 31);
+}
+
+// One level of the z reduce-scatter (partner lane ^ MSK) and the levels
+// after it: a lane holding NV channel sums keeps half (the upper half if its
+// MSK bit is set) and adds the partner's copy of that half; once one value
+// is left, the remaining levels add plainly.  coff tracks the first channel
+// held.  Every channel's sum is formed pair for pair as the full butterfly
+// forms it.
+template <int NV, int MSK>
+__device__ __forceinline__ void z_scatter(float (&zp)[8], int lane, int& coff) {
+    if constexpr (MSK < 64) {
+        if constexpr (NV > 1) {
+            constexpr int H = NV / 2;
+            const bool hi = (lane & MSK) != 0;
+#pragma unroll
+            for (int e = 0; e < H; ++e) {
+                const float keep = hi ? zp[H + e] : zp[e];
+                const float send = hi ? zp[e] : zp[H + e];
+                zp[e] = keep + __shfl_xor(send, MSK);
+            }
+            coff += hi ? H : 0;
+            z_scatter<H, MSK * 2>(zp, lane, coff);
+        } else {
+            zp[0] += __shfl_xor(zp[0], MSK);
+            z_scatter<1, MSK * 2>(zp, lane, coff);
+        }
+    }
 }
 
 template <int D, bool ROPE, int THR = StateBf16Cfg<D>::THREADS>
@@ -274,7 +309,9 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     const int rd_row = 8 * gq + (i16 >> 2);
     const int rd_col = 16 * q + 4 * (i16 & 3);
     const int ctile = wave % C::NCI;   // key-channel tile of this wave
-    const int tgrp = wave / C::NCI;    // token group of this wave
+    const int vsp = (wave / C::NCI) % C::NVS;  // value-channel split of this wave
+    const int co = ctile * C::NVS + vsp;       // its (key tile, value split) pair
+    const int tgrp = wave / C::NCO;    // token group of this wave
 
     const int ntiles = c1 > c0 ? (c1 - c0 + C::TT - 1) / C::TT : 0;
     // The loop sits inside this branch so that it is entered only after tile
@@ -307,7 +344,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
                 Al[st] = lds_read_tr8(klo + swz<C::DP>(r0, col), klo + swz<C::DP>(r1, col));
 #pragma unroll
                 for (int j = 0; j < C::NJ; ++j) {
-                    const int vcol = 32 * j + rd_col;
+                    const int vcol = 32 * (vsp * C::NJ + j) + rd_col;
                     Bv[st][j] = lds_read_tr8(vt + swz<C::DP>(r0, vcol), vt + swz<C::DP>(r1, vcol));
                 }
             }
@@ -340,7 +377,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
         const bool member = tgrp % lvl == 0;
         const int base = (tgrp / (4 * lvl)) * 3;  // first slot of this group
         if (member && k > 0) {
-            const int slot = (base + k - 1) * C::NCI + ctile;
+            const int slot = (base + k - 1) * C::NCO + co;
 #pragma unroll
             for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
@@ -353,7 +390,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
 #pragma unroll
             for (int m = 1; m < 4; ++m) {
                 if (tgrp + m * lvl >= C::NTG) break;
-                const int slot = (base + m - 1) * C::NCI + ctile;
+                const int slot = (base + m - 1) * C::NCO + co;
 #pragma unroll
                 for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
@@ -398,7 +435,7 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 32 * ctile + 8 * (r >> 2) + 4 * gq + (r & 3);
-                srow[row * SR + 32 * j + m] = acc[j][r];
+                srow[row * SR + 32 * (vsp * C::NJ + j) + m] = acc[j][r];
             }
     }
     lds_barrier();
@@ -424,15 +461,34 @@ __global__ __launch_bounds__(THR) void la_state_bf16_kernel(StateArgs a) {
     }
     lds_barrier();  // the rows are read before the z sums reuse the LDS
     // ---- z partial: the lanes of a wave that share a channel block (lane
-    //      % CH) summed across lanes, then the waves' sums in wave order ----
-#pragma unroll
-    for (int msk = C::CH; msk < 64; msk <<= 1)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zp[e] += __shfl_xor(zp[e], msk);
+    //      % CH) summed across lanes, then the waves' sums in wave order.
+    //      Across lanes as a reduce-scatter: at each level of the butterfly
+    //      (partner lane ^ msk) a lane keeps half of its channels and adds the
+    //      partner's copy of that half, so each level moves half as many
+    //      values as the one before: 7 cross-lane moves a lane at d = 64
+    //      instead of 24, whose LDS-crossbar permutes took 1.2 us at the end of
+    //      the 720p-5s pass.  The additions are those of the full butterfly,
+    //      pair for pair, so z is unchanged bitwise. ----
     float* zr = (float*)smem;  // [NW][DP]
-    if (lane < C::CH) {
+    if constexpr (C::CH <= 8) {
+        int coff = 0;  // first channel (within the lane's block of 8) still held
+        z_scatter<8, C::CH>(zp, lane, coff);
+        // lanes past the last halving hold copies: the first 64 / 2^(levels
+        // after it) lanes write, one channel each
+        constexpr int WR = C::CH == 4 ? 32 : 64;
+        if (lane < WR) zr[wave * C::DP + 8 * (lane % C::CH) + coff] = zp[0];
+    } else {
+        // 128 channels on chip: two levels only, as a full butterfly (the
+        // reduce-scatter's selects do not fit the 512-thread kernel's
+        // registers there)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zr[wave * C::DP + 8 * lane + e] = zp[e];
+        for (int msk = C::CH; msk < 64; msk <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zp[e] += __shfl_xor(zp[e], msk);
+        if (lane < C::CH) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zr[wave * C::DP + 8 * lane + e] = zp[e];
+        }
     }
     lds_barrier();
     if (tid < D) {
