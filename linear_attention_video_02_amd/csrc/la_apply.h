@@ -223,16 +223,26 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
     // then waits for its own S only, and the first units of Q do not queue
     // behind every head's S.  Every register slot loads (a phase past nph
     // reloads phase 0's head) so that the compiler counts the loads exactly.
-    // S comes in with coalesced 16-byte loads and goes to LDS transposed and
-    // rounded to fp16, where each lane reads its fragments.
-    constexpr int S4 = (D * D / 4 + C::THREADS - 1) / C::THREADS;  // float4s a thread per head
-    f32x4 sraw[NPH][S4];
+    // A thread takes column segments of S: segment g is value channel
+    // co = g % D, key channels 8 kb .. 8 kb + 7 (kb = g / D), read as 8 words
+    // that consecutive lanes take from consecutive channels of a row (256
+    // bytes a wave instruction).  Rounded to fp16, a segment is one 16-byte
+    // piece of a row of S^T in LDS, where each lane reads its fragments (as
+    // 2-byte pieces, the transposed writes took 1.7 us of the SANA-2B apply).
+    constexpr int NSEG = D * (D / 8);
+    constexpr int SC = (NSEG + C::THREADS - 1) / C::THREADS;  // segments a thread per head
+    float scol[NPH][SC][8];
+    auto seg_at = [&](int i) { return (int)threadIdx.x + i * C::THREADS; };
+    auto seg_off = [&](int sg) {  // float offset of the segment's first entry (0 past the end)
+        return sg < NSEG ? 8 * (sg / D) * D + sg % D : 0;
+    };
     auto load_s = [&](int ph) {
         const float* Sh = a.S + (size_t)head_of(ph < nph ? ph : 0) * D * D;
 #pragma unroll
-        for (int i = 0; i < S4; ++i) {
-            const int f = threadIdx.x + i * C::THREADS;
-            sraw[ph][i] = *(const f32x4*)(Sh + 4 * (f < D * D / 4 ? f : 0));
+        for (int i = 0; i < SC; ++i) {
+            const int o = seg_off(seg_at(i));
+#pragma unroll
+            for (int r = 0; r < 8; ++r) scol[ph][i][r] = Sh[o + r * D];
         }
     };
     // KV instance: every load of a head's keys/values at once (at most 512
@@ -434,9 +444,10 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
             }
             lds_barrier();
 #pragma unroll
-            for (int i = 0; i < S4; ++i) {
-                const int f = threadIdx.x + i * C::THREADS;
-                sraw[ph][i] = *(const f32x4*)(srw + 4 * (f < D * D / 4 ? f : 0));
+            for (int i = 0; i < SC; ++i) {
+                const int o = seg_off(seg_at(i));  // (srw rows have D = 64 entries)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) scol[ph][i][r] = srw[o + r * D];
             }
             lds_barrier();  // before the next head's tiles
         }
@@ -463,11 +474,10 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
         if (ph < nph && head_of(ph) < BH) {
             float amax = 0.0f;
 #pragma unroll
-            for (int i = 0; i < S4; ++i) {
-                const int f = threadIdx.x + i * C::THREADS;
-                if (f < D * D / 4)
+            for (int i = 0; i < SC; ++i) {
+                if (seg_at(i) < NSEG)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(sraw[ph][i][j]));
+                    for (int r = 0; r < 8; ++r) amax = fmaxf(amax, fabsf(scol[ph][i][r]));
             }
             amax = wave_max(amax);
             if (lane == 0) smax[ph][wave] = amax;
@@ -496,12 +506,17 @@ __global__ __launch_bounds__(ApplyBf16Cfg<D>::THREADS) void la_apply_bf16_kernel
                     __builtin_bit_cast(uint16_t, (_Float16)ldexpf(sv, -eS));
             };
 #pragma unroll
-            for (int i = 0; i < S4; ++i) {
-                const int f = threadIdx.x + i * C::THREADS;
-                if (f < D * D / 4) {
-                    const int k = f / (D / 4), co = 4 * (f % (D / 4));
+            for (int i = 0; i < SC; ++i) {
+                const int sg = seg_at(i);
+                if (sg < NSEG) {
+                    u32x4 w;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) put_st(k, co + j, sraw[ph][i][j]);
+                    for (int r = 0; r < 4; ++r) {
+                        const _Float16 lo = (_Float16)ldexpf(scol[ph][i][2 * r], -eS);
+                        const _Float16 hi = (_Float16)ldexpf(scol[ph][i][2 * r + 1], -eS);
+                        w[r] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                    }
+                    *(u32x4*)(sth + st_off<C::DP>(st_row(sg % D), sg / D)) = w;
                 }
             }
             // the padding rows and columns (key or value channel >= d); with the
