@@ -73,7 +73,15 @@ const KnobInfo kKnobs[K_COUNT] = {
     {"tc_state_threads", 512, 1024}, {"tconv_gm", 1, 64},   {"tconv_gn", 1, 64},
     {"apply_spread", 0, 1},     {"cross_fused", 0, 1},
 };
-int g_knob[K_COUNT] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+// every knob starts unset (-1), however many there are
+struct KnobValues {
+    int v[K_COUNT];
+    KnobValues() {
+        for (int& x : v) x = -1;
+    }
+};
+KnobValues g_knob_values;
+int* const g_knob = g_knob_values.v;
 
 int knob(Knob k, int dflt) { return g_knob[k] >= 0 ? g_knob[k] : dflt; }
 
