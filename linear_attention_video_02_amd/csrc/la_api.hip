@@ -67,12 +67,13 @@ struct KnobInfo {
     const char* name;
     int lo, hi;  // accepted values (a negative value resets the knob)
 };
-const KnobInfo kKnobs[K_COUNT] = {
+const KnobInfo kKnobs[] = {
     {"state_wgs", 1, 1 << 20},  {"apply_wgs", 1, 1 << 20},  {"causal_wgs", 1, 1 << 20},
     {"state_fused", 0, 1},      {"apply_ilv", 0, 1},        {"apply_heads", 1, 8},
     {"tc_state_threads", 512, 1024}, {"tconv_gm", 1, 64},   {"tconv_gn", 1, 64},
     {"apply_spread", 0, 1},     {"cross_fused", 0, 1},
 };
+static_assert(sizeof(kKnobs) / sizeof(kKnobs[0]) == K_COUNT, "one table entry per knob");
 // every knob starts unset (-1), however many there are
 struct KnobValues {
     int v[K_COUNT];

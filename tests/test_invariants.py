@@ -376,3 +376,35 @@ def test_one_workspace_many_shapes(la):
             torch.cuda.synchronize()
             assert torch.equal(S, ref[i][0]) and torch.equal(z, ref[i][1]), (rep, i)
             assert torch.equal(o, ref[i][2]), (rep, i)
+
+
+def test_two_streams_each_get_their_own_workspace(la):
+    """Calls on two streams at once: the binding hands each stream its own
+    workspace (the in-kernel second stage keeps per-head counters and partial
+    states there), so both give bitwise the results of one-stream calls."""
+    import torch
+    B, H, N, d, grid = 2, 16, 6000, 64, (7, 25, 40)
+    (_, _, _), (q1, k1, v1) = _inputs(B, H, N, d, "bf16", 81)
+    (_, _, _), (q2, k2, v2) = _inputs(B, H, N, d, "bf16", 82)
+    S1, z1 = la.state_reduce(k1, v1, grid)
+    S2, z2 = la.state_reduce(k2, v2, grid)
+    o1 = la.bidirectional(q1, k1, v1, grid)
+    o2 = la.bidirectional(q2, k2, v2, grid)
+    torch.cuda.synchronize()
+    ref = [(S1.clone(), z1.clone(), o1.clone()), (S2.clone(), z2.clone(), o2.clone())]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(5):
+        got = []
+        for s, (q, k, v) in zip(streams, ((q1, k1, v1), (q2, k2, v2))):
+            with torch.cuda.stream(s):
+                S, z = la.state_reduce(k, v, grid)
+                o = la.bidirectional(q, k, v, grid)
+                got.append((S, z, o))
+        torch.cuda.synchronize()
+        for i in range(2):
+            for a, b in zip(got[i], ref[i]):
+                assert torch.equal(a, b), (rep, i)
+    ws = {id(la.workspace(B, H, N, d, q1.device, stream=s, grid=grid)) for s in streams}
+    assert len(ws) == 2
