@@ -701,16 +701,22 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
         rc = launch_kernel<StateArgs>(sk, dim3(sa.P * g.BH), ps.lds, st, sa, half ? 512 : state_threads(d, dtype));
         if (rc != LA_OK) return rc;
     }
-    // 2. exclusive prefixes in place (+ carry), total -> carry
-    PrefixArgs pa;
-    pa.partial = partial;
-    pa.S_carry = S_carry;
-    pa.z_carry = z_carry;
-    pa.S_out = S_carry;
-    pa.z_out = z_carry;
-    pa.P = ps.P;
-    rc = launch_kernel<PrefixArgs>(prefix_kernel(d), dim3((d * d + d + 255) / 256, g.BH), 0, st, pa);
-    if (rc != LA_OK) return rc;
+    // 2. exclusive prefixes in place (+ carry), total -> carry.  Without a
+    // carry, the bf16 scan at 64 channels on chip (d = 32, 64) forms each
+    // chunk's prefix from the partials itself, in the same order, and this
+    // launch is not needed (720p-5s: 6 us of the call).
+    const bool raw = !S_carry && dtype == LA_BF16 && d <= 64;
+    if (!raw) {
+        PrefixArgs pa;
+        pa.partial = partial;
+        pa.S_carry = S_carry;
+        pa.z_carry = z_carry;
+        pa.S_out = S_carry;
+        pa.z_out = z_carry;
+        pa.P = ps.P;
+        rc = launch_kernel<PrefixArgs>(prefix_kernel(d), dim3((d * d + d + 255) / 256, g.BH), 0, st, pa);
+        if (rc != LA_OK) return rc;
+    }
     // 3. causal scan of every chunk from its prefix
     CausalArgs ca;
     ca.Q = Q;
@@ -718,6 +724,7 @@ int run_token_causal(const void* Q, const void* K, const void* V, void* O, float
     ca.V = V;
     ca.O = O;
     ca.pre = partial;
+    ca.raw_prefix = raw ? 1 : 0;
     ca.eps = eps;
     ca.chunk = pc.chunk;
     ca.P = pc.P;

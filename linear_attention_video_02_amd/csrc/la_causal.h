@@ -9,7 +9,9 @@
 // the sequence; la_prefix_kernel turns them, in place, into exclusive
 // prefixes (state before the chunk, carry included); la_causal_bf16_kernel
 // (la_causal_f32_kernel for fp32 inputs) then scans each chunk with the
-// running state on chip.
+// running state on chip.  Without a carry, the bf16 scan at 64 channels on
+// chip sums its chunk's prefix from the partials itself (raw_prefix), in the
+// prefix kernel's order, and the prefix launch is skipped.
 #pragma once
 
 #include "la_common.h"
@@ -66,6 +68,10 @@ struct CausalArgs {
     const void* V;
     void* O;
     const float* pre;  // [BH][P][D*D + D]: state before each chunk
+    // raw_prefix (bf16, 64 channels on chip): `pre` holds the chunks' own
+    // partial states, and the scan of chunk p forms its prefix itself as the
+    // prefix kernel would without a carry: 0 + partial 0 + ... + partial p-1
+    int raw_prefix = 0;
     float eps;
     int chunk;         // tokens per workgroup (a multiple of 64)
     int P;             // chunks per (batch, head)
@@ -209,16 +215,54 @@ __global__ __launch_bounds__(CausalBf16Cfg<D>::THREADS, CausalBf16Cfg<D>::MINB) 
     auto cj_of = [&](int t) { return (wave * C::TPW + t) % C::NCB; };
     const float* pre = a.pre + ((size_t)bh * a.P + p) * (D * D + D);
     f32x16 sacc[C::TPW];
+    float zpre = 0.0f;
+    if (C::WIDE || !a.raw_prefix) {
 #pragma unroll
-    for (int t = 0; t < C::TPW; ++t) {
-        const int vc = perm_inv(32 * cj_of(t) + m32);
+        for (int t = 0; t < C::TPW; ++t) {
+            const int vc = perm_inv(32 * cj_of(t) + m32);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int k = 32 * ci + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            sacc[t][r] = (DP == D || (k < D && vc < D)) ? pre[k * D + vc] : 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                const int k = 32 * ci + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                sacc[t][r] = (DP == D || (k < D && vc < D)) ? pre[k * D + vc] : 0.0f;
+            }
+        }
+        zpre = tid < D ? pre[D * D + tid] : 0.0f;
+    } else {
+        // the prefix from the partials of chunks 0 .. p-1 of this head, NB at
+        // a time with all their loads in flight, added in chunk order from 0
+        constexpr int NB = 4;
+        const float* part0 = a.pre + (size_t)bh * a.P * (D * D + D);
+#pragma unroll
+        for (int t = 0; t < C::TPW; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[t][r] = 0.0f;
+        for (int q0 = 0; q0 < p; q0 += NB) {
+            float tv[NB][C::TPW][16], tz[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const float* src = part0 + (size_t)(q0 + u < p ? q0 + u : q0) * (D * D + D);
+#pragma unroll
+                for (int t = 0; t < C::TPW; ++t) {
+                    const int vc = perm_inv(32 * cj_of(t) + m32);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int k = 32 * ci + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                        tv[u][t][r] = (DP == D || (k < D && vc < D)) ? src[k * D + vc] : 0.0f;
+                    }
+                }
+                tz[u] = tid < D ? src[D * D + tid] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u)
+                if (q0 + u < p) {
+#pragma unroll
+                    for (int t = 0; t < C::TPW; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) sacc[t][r] = sacc[t][r] + tv[u][t][r];
+                    zpre = zpre + tz[u];
+                }
         }
     }
-    const float zpre = tid < D ? pre[D * D + tid] : 0.0f;
     __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the ring's
     load_kv(0, 0);
     load_q(0, 0);
