@@ -380,8 +380,8 @@ def summarize_trace(trace_dir, command, out_path, workload=WORKLOAD):
                            t(la[j], "End_Timestamp")))
     if steps_:
         n = len(steps_)
-        what = {"tc720p5s": ("state kernel start to the causal scan's end", "partials and prefix",
-                             "prefix -> scan"),
+        what = {"tc720p5s": ("state kernel start to the causal scan's end", "partial states",
+                             "partial states -> scan"),
                 "720p60s": ("one block step: state kernel start to apply kernel end", "state pass",
                             "state pass -> apply")}.get(
             workload, ("state kernel start to apply kernel end", "state pass", "state pass -> apply"))
@@ -1078,9 +1078,9 @@ def setup_workload(name, la, dev):
             "step": step, "tokens_per_step": B * N, "step_bytes": 4 * tb,
             "config": {"workload": name, "B": B, "H": H, "N": N, "d": d, "grid": list(grid), "eps": eps,
                        "input_sets": len(sets)},
-            # one call: partial states, in-place prefix, causal scan (K and V are read twice)
-            "groups": [("token_causal", ("la_state_bf16_kernel", "la_prefix_kernel", "la_causal_bf16_kernel"),
-                        4 * tb)],
+            # one call: partial states, then the causal scan, each of whose workgroups
+            # forms its chunk's prefix from them (K and V are read twice)
+            "groups": [("token_causal", ("la_state_bf16_kernel", "la_causal_bf16_kernel"), 4 * tb)],
             "copy_pairs": [(s_[0], s_[3]) for s_ in sets],
         }
 
