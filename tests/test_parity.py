@@ -399,3 +399,24 @@ def test_token_causal_carry_resume_and_determinism(la, d, dt):
                     grid, eps, S, z, N)
     torch.cuda.synchronize()
     assert torch.equal(S, S0)
+
+
+@pytest.mark.parametrize("d,dt", [(64, "bf16"), (32, "bf16"), (112, "bf16"), (64, "fp32")])
+def test_token_causal_zero_carry_equals_no_carry_bitwise(la, d, dt):
+    """Starting from a zero carry is starting from the empty state: the output is
+    bitwise the one without a carry.  (Without a carry, bf16 at d <= 64 forms
+    each chunk's prefix inside the scan; with one, a separate prefix launch
+    does, from the carry's zeros -- the same sums in the same order.)"""
+    import torch
+    B, H, N, grid, eps = 2, 3, 9000, (10, 30, 30), 1e-6
+    q, k, v = make_qkv(B, H, N, d, dt, seed=5300 + d)
+    tq, tk, tv = upload(q, dt), upload(k, dt), upload(v, dt)
+    S = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda:0")
+    z = torch.zeros((B, H, d), dtype=torch.float32, device="cuda:0")
+    with_carry = la.token_causal(tq, tk, tv, grid, eps, S, z, 0)
+    without = la.token_causal(tq, tk, tv, grid, eps)
+    torch.cuda.synchronize()
+    say(f"[token-causal zero carry] d={d} {dt}")
+    assert torch.equal(with_carry, without)
+    ref, _, _ = oracle.token_causal(q[:, :1], k[:, :1], v[:, :1], grid, eps)
+    assert_close(host(without[:, :1]), ref, dt, f"d={d} {dt} batch 0")
